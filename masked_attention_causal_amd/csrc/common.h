@@ -1,0 +1,87 @@
+// Device-side building blocks shared by the tfl kernels (gfx950 / CDNA4).
+//
+// Storage types: fp32, fp16 and bf16 (bf16 is carried as raw uint16 bits and
+// only ever widened to fp32 or narrowed from it).  All narrowing conversions
+// round to nearest even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tfl {
+
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 {
+    uint16_t u;
+};
+
+static constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.u << 16); }
+
+template <class T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }  // v_cvt_f16_f32, RNE
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (inputs are finite)
+    bf16 r;
+    r.u = (uint16_t)(u >> 16);
+    return r;
+}
+
+// Eight consecutive stored values -> eight fp16 MFMA operands.
+__device__ __forceinline__ f16x8 load8_as_f16(const f16* p) { return *(const f16x8*)p; }
+__device__ __forceinline__ f16x8 load8_as_f16(const bf16* p) {
+    uint4 r = *(const uint4*)p;
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        o[2 * i] = (f16)__uint_as_float(w[i] << 16);
+        o[2 * i + 1] = (f16)__uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    return o;
+}
+__device__ __forceinline__ f16x8 load8_as_f16(const float* p) {
+    float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    f16x8 o = {(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w, (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
+    return o;
+}
+
+// ---------------------------------------------------------------- MFMA
+// Lane layouts (lane l, g = l / 16), as used throughout:
+//   16x16x32 f16:  A[i][k] in lane i + 16*(k/8), element k%8;  B[k][j] in lane j + 16*(k/8)
+//   16x16x16 f16:  A[i][k] in lane i + 16*(k/4), element k%4;  B likewise
+//   16x16x4  f32:  A[i][k] in lane i + 16*k;                    B[k][j] in lane j + 16*k
+//   result D[i][j] (all three): lane j + 16*(i/4), element i%4
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+template <int WIDTH>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float h) { return 0.5f * h * (1.0f + erff(h * 0.7071067811865475f)); }
+
+}  // namespace tfl

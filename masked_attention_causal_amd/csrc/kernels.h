@@ -1,0 +1,59 @@
+// Host-side launchers of the tfl kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tfl {
+
+// Arithmetic mode, fixed by the I/O dtype:
+//   F32:  every GEMM/attention operand fp32, fp32 MFMA.
+//   F16:  operands fp16 (activations rounded once to fp16), weights fp16.
+//   BF16: operands fp16; bf16 weights are widened to fp16 as they are loaded.
+// The residual stream, LayerNorm, Q and K are fp32 in every mode.
+enum Mode { MODE_F32 = 0, MODE_F16 = 1, MODE_BF16 = 2 };
+
+enum Epi { EPI_QKV = 0, EPI_GELU = 1, EPI_RES = 2 };
+
+struct GemmArgs {
+    const void* A;     // [M, K] operand dtype, row-major
+    const void* W;     // [N, K] weight dtype (nn.Linear layout)
+    const void* bias;  // [N] weight dtype
+    int M, N, K;
+    // EPI_QKV: N = 3d; writes Q, K [B, H, L, dh] fp32 and V^T [B, H, dh, Lp] operand dtype
+    float* Q;
+    float* Kd;
+    void* Vt;
+    int L, Lp, H, dh, d;
+    // EPI_GELU: out [M, N] operand dtype
+    void* out;
+    // EPI_RES: Z = acc + bias + R, [M, N] fp32
+    const float* R;
+    float* Z;
+};
+
+struct AttnArgs {
+    const float* Q;    // [B, H, L, dh]
+    const float* K;    // [B, H, L, dh]
+    const void* Vt;    // [B, H, dh, Lp] operand dtype
+    void* O;           // [B*L, d] operand dtype, head h at columns h*dh
+    const int32_t* lens;
+    int B, H, L, Lp, d;
+    float scale_log2;  // log2(e) / sqrt(dh)
+};
+
+// Fixed tile shapes shared with the planner.
+constexpr int ATT_KT = 64;   // keys per attention tile
+constexpr int ATT_BQ = 64;   // queries per attention workgroup
+
+hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s);
+hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
+hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
+hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta, float eps,
+                     int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);
+
+// Row layout of the LayerNorm kernel: lanes per row and float4 chunks per lane.
+// Returns false when d is not supported.
+bool ln_shape(int d, int* lanes_per_row, int* chunks);
+
+}  // namespace tfl

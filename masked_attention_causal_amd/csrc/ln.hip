@@ -1,0 +1,155 @@
+// Residual LayerNorm and input staging.
+//
+// LayerNorm is the textbook two-pass one: mean first, then the biased
+// variance of the centred values, both in fp32, eps added in fp32, then the
+// affine map (the post-LN layer of the PyTorch reference the pages were
+// gated against: "Hyper-optimized megakernel-hybrid transformer inference",
+// "Challenges").  A row is spread over a group of lanes of one wave
+// (up to 64) that read it as coalesced float4 chunks; the reductions are
+// butterfly shuffles inside the group.  The row then leaves as fp32 (the
+// residual stream), as an operand-dtype copy for the next GEMM, and/or, in
+// the last layer, as the I/O dtype output.
+#include "common.h"
+#include "kernels.h"
+
+namespace tfl {
+
+bool ln_shape(int d, int* lanes_per_row, int* chunks) {
+    if (d <= 0 || d % 4 != 0) return false;
+    const int q = d / 4;
+    int lpr = 1;
+    while (lpr < 64 && q % (lpr * 2) == 0) lpr *= 2;
+    const int nc = q / lpr;
+    if (nc > 8) return false;
+    *lanes_per_row = lpr;
+    *chunks = nc;
+    return true;
+}
+
+template <class OpT, class PT, int LPR, int NC>
+__global__ __launch_bounds__(256) void ln_kernel(const float* __restrict__ Z, const PT* __restrict__ gamma,
+                                                 const PT* __restrict__ beta, float eps, int T, int d,
+                                                 float* __restrict__ Xo, OpT* __restrict__ Ao,
+                                                 PT* __restrict__ Y) {
+    constexpr int RPB = 256 / LPR;  // rows per block
+    const int tid = threadIdx.x;
+    const int sub = tid % LPR;
+    const long row = (long)blockIdx.x * RPB + tid / LPR;
+    if (row >= T) return;  // whole lane groups leave together
+    const float* z = Z + row * d;
+    float4 v[NC];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        v[c] = *(const float4*)(z + (c * LPR + sub) * 4);
+        s += (v[c].x + v[c].y) + (v[c].z + v[c].w);
+    }
+    s = wave_sum<LPR>(s);
+    const float mean = s / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        v[c].x -= mean; v[c].y -= mean; v[c].z -= mean; v[c].w -= mean;
+        q += (v[c].x * v[c].x + v[c].y * v[c].y) + (v[c].z * v[c].z + v[c].w * v[c].w);
+    }
+    q = wave_sum<LPR>(q);
+    const float rstd = 1.0f / sqrtf(q / (float)d + eps);
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        const int col = (c * LPR + sub) * 4;
+        float o[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = o[e] * rstd * to_f32(gamma[col + e]) + to_f32(beta[col + e]);
+        if (Xo) *(float4*)(Xo + row * d + col) = float4{o[0], o[1], o[2], o[3]};
+        if (Ao) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) Ao[row * d + col + e] = from_f32<OpT>(o[e]);
+        }
+        if (Y) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) Y[row * d + col + e] = from_f32<PT>(o[e]);
+        }
+    }
+}
+
+template <class OpT, class PT, int LPR>
+static hipError_t ln_nc(int nc, const float* Z, const void* g, const void* b, float eps, int T, int d,
+                        float* Xo, void* Ao, void* Y, hipStream_t s) {
+    constexpr int RPB = 256 / LPR;
+    dim3 grid((T + RPB - 1) / RPB);
+#define TFL_LN_CASE(NC)                                                                          \
+    case NC:                                                                                     \
+        hipLaunchKernelGGL((ln_kernel<OpT, PT, LPR, NC>), grid, dim3(256), 0, s, Z, (const PT*)g, \
+                           (const PT*)b, eps, T, d, Xo, (OpT*)Ao, (PT*)Y);                        \
+        break;
+    switch (nc) {
+        TFL_LN_CASE(1) TFL_LN_CASE(2) TFL_LN_CASE(3) TFL_LN_CASE(4)
+        TFL_LN_CASE(5) TFL_LN_CASE(6) TFL_LN_CASE(7) TFL_LN_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef TFL_LN_CASE
+    return hipGetLastError();
+}
+
+template <class OpT, class PT>
+static hipError_t ln_mode(const float* Z, const void* g, const void* b, float eps, int T, int d, float* Xo,
+                          void* Ao, void* Y, hipStream_t s) {
+    int lpr, nc;
+    if (!ln_shape(d, &lpr, &nc)) return hipErrorInvalidValue;
+    switch (lpr) {
+        case 1: return ln_nc<OpT, PT, 1>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 2: return ln_nc<OpT, PT, 2>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 4: return ln_nc<OpT, PT, 4>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 8: return ln_nc<OpT, PT, 8>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 16: return ln_nc<OpT, PT, 16>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 32: return ln_nc<OpT, PT, 32>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 64: return ln_nc<OpT, PT, 64>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln(Mode m, const float* Z, const void* g, const void* b, float eps, int T, int d, float* Xo,
+                     void* Ao, void* Y, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    switch (m) {
+        case MODE_F32: return ln_mode<float, float>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case MODE_F16: return ln_mode<f16, f16>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case MODE_BF16: return ln_mode<f16, bf16>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- input staging
+// x (I/O dtype) -> fp32 residual stream and operand-dtype copy.
+template <class OpT, class XT>
+__global__ __launch_bounds__(256) void prep_kernel(const XT* __restrict__ x, float* __restrict__ Xr,
+                                                   OpT* __restrict__ A, long n) {
+    const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;  // n is a multiple of 4 (d % 4 == 0)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const float v = to_f32(x[i + e]);
+        Xr[i + e] = v;
+        A[i + e] = from_f32<OpT>(v);
+    }
+}
+
+hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    dim3 grid((unsigned)((n / 4 + 255) / 256));
+    switch (m) {
+        case MODE_F32:
+            hipLaunchKernelGGL((prep_kernel<float, float>), grid, dim3(256), 0, s, (const float*)x, Xr, (float*)A, n);
+            break;
+        case MODE_F16:
+            hipLaunchKernelGGL((prep_kernel<f16, f16>), grid, dim3(256), 0, s, (const f16*)x, Xr, (f16*)A, n);
+            break;
+        case MODE_BF16:
+            hipLaunchKernelGGL((prep_kernel<f16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, Xr, (f16*)A, n);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tfl

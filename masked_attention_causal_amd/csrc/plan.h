@@ -1,0 +1,35 @@
+// Frozen per-shape plans: the dispatcher's choice of path, the workspace
+// layout and the launch sequence.  Host-only; no device call is made while
+// a plan is built.
+#pragma once
+#include <string>
+
+#include "kernels.h"
+#include "tfl.h"
+
+namespace tfl {
+
+struct Plan {
+    int path;       // tfl_path actually used
+    char name[64];
+    Mode mode;
+    int n_layers, d, H, dh, f, B, L, Lp;
+    long T;         // B * L token rows
+    float eps;
+    size_t op;      // operand element size (4 in F32 mode, 2 otherwise)
+    // workspace offsets in bytes (TILED)
+    size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G;
+    size_t ws_bytes;
+};
+
+size_t dtype_size(int dtype);
+
+// The dispatcher's rule for a valid configuration (tfl_path, never AUTO).
+int choose_path(const tfl_config& cfg);
+
+tfl_status make_plan(const tfl_config& cfg, Plan* p, std::string* why);
+
+hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
+                    char* ws, hipStream_t s);
+
+}  // namespace tfl

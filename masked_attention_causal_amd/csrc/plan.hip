@@ -1,0 +1,159 @@
+// Plans and launch sequences.
+//
+// The dispatcher is a fixed rule over (dtype, batch, seq_len, d_model,
+// heads, FFN width, layers) evaluated once at tfl_create, never a run-time
+// search: "KernelForge", "What it does" (a frozen table consulted at run
+// time, no autotuning, no nondeterminism) and "Hyper-optimized
+// megakernel-hybrid transformer inference", "Problem decomposition"
+// (families by residency and by binding resource).
+#include <climits>
+#include <cmath>
+#include <cstdio>
+
+#include "plan.h"
+
+namespace tfl {
+
+size_t dtype_size(int dtype) { return dtype == TFL_F32 ? 4 : 2; }
+
+int choose_path(const tfl_config& cfg) {
+    (void)cfg;
+    return TFL_PATH_TILED;
+}
+
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
+    if (c.n_layers < 1 || c.d_model < 1 || c.n_heads < 1 || c.d_ffn < 1 || c.batch < 1 || c.seq_len < 1) {
+        *why = "all sizes must be >= 1";
+        return TFL_E_INVALID;
+    }
+    if (c.d_model % c.n_heads != 0) {
+        *why = "d_model must be a multiple of n_heads";
+        return TFL_E_INVALID;
+    }
+    if (c.dtype != TFL_F32 && c.dtype != TFL_F16 && c.dtype != TFL_BF16) {
+        *why = "unknown dtype";
+        return TFL_E_INVALID;
+    }
+    if (c.force_path < TFL_PATH_AUTO || c.force_path > TFL_PATH_TILED) {
+        *why = "unknown force_path";
+        return TFL_E_INVALID;
+    }
+    const int dh = c.d_model / c.n_heads;
+    if (dh != 16 && dh != 32 && dh != 64) {
+        *why = "head dim must be 16, 32 or 64";
+        return TFL_E_UNSUPPORTED;
+    }
+    int lpr, nc;
+    if (c.d_model % 32 != 0 || c.d_model > 1024 || !ln_shape(c.d_model, &lpr, &nc)) {
+        *why = "d_model must be a multiple of 32 and at most 1024";
+        return TFL_E_UNSUPPORTED;
+    }
+    if (c.d_ffn % 32 != 0) {
+        *why = "d_ffn must be a multiple of 32";
+        return TFL_E_UNSUPPORTED;
+    }
+    const long T = (long)c.batch * c.seq_len;
+    if (c.batch > 65535 || T > 65535L * 64) {
+        *why = "batch must be <= 65535 and batch*seq_len <= 4194240";
+        return TFL_E_UNSUPPORTED;
+    }
+    int path = c.force_path == TFL_PATH_AUTO ? choose_path(c) : c.force_path;
+    if (path != TFL_PATH_TILED) {
+        *why = "requested path is not available for this shape";
+        return TFL_E_UNSUPPORTED;
+    }
+    Plan q{};
+    q.path = path;
+    q.mode = c.dtype == TFL_F32 ? MODE_F32 : (c.dtype == TFL_F16 ? MODE_F16 : MODE_BF16);
+    q.n_layers = c.n_layers;
+    q.d = c.d_model;
+    q.H = c.n_heads;
+    q.dh = dh;
+    q.f = c.d_ffn;
+    q.B = c.batch;
+    q.L = c.seq_len;
+    q.Lp = (c.seq_len + ATT_KT - 1) / ATT_KT * ATT_KT;
+    q.T = T;
+    q.eps = c.ln_eps > 0.f ? c.ln_eps : 1e-5f;
+    q.op = q.mode == MODE_F32 ? 4 : 2;
+    const size_t Td = (size_t)T * q.d;
+    size_t o = 0;
+    q.off_Xr = o; o += up256(Td * 4);
+    q.off_X1 = o; o += up256(Td * 4);
+    q.off_Z = o;  o += up256(Td * 4);
+    q.off_Q = o;  o += up256(Td * 4);
+    q.off_K = o;  o += up256(Td * 4);
+    q.off_A = o;  o += up256(Td * q.op);
+    q.off_O = o;  o += up256(Td * q.op);
+    q.off_Vt = o; o += up256((size_t)q.B * q.d * q.Lp * q.op);
+    q.off_G = o;  o += up256((size_t)T * q.f * q.op);
+    q.ws_bytes = o;
+    std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s", ATT_BQ, ATT_KT,
+                  q.mode == MODE_F32 ? "f32" : "f16op");
+    *p = q;
+    return TFL_OK;
+}
+
+static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
+                            char* ws, hipStream_t s) {
+    float* Xr = (float*)(ws + P.off_Xr);
+    float* X1 = (float*)(ws + P.off_X1);
+    float* Z = (float*)(ws + P.off_Z);
+    float* Q = (float*)(ws + P.off_Q);
+    float* K = (float*)(ws + P.off_K);
+    void* A = ws + P.off_A;
+    void* O = ws + P.off_O;
+    void* Vt = ws + P.off_Vt;
+    void* G = ws + P.off_G;
+    const int M = (int)P.T;
+    hipError_t e = launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s);
+    if (e != hipSuccess) return e;
+    for (int l = 0; l < P.n_layers; l++) {
+        const tfl_layer& w = layers[l];
+        const bool last = l == P.n_layers - 1;
+        GemmArgs g{};
+        g.A = A; g.W = w.w_qkv; g.bias = w.b_qkv;
+        g.M = M; g.N = 3 * P.d; g.K = P.d;
+        g.Q = Q; g.Kd = K; g.Vt = Vt;
+        g.L = P.L; g.Lp = P.Lp; g.H = P.H; g.dh = P.dh; g.d = P.d;
+        if ((e = launch_gemm(P.mode, EPI_QKV, g, s)) != hipSuccess) return e;
+
+        AttnArgs a{};
+        a.Q = Q; a.K = K; a.Vt = Vt; a.O = O; a.lens = lens;
+        a.B = P.B; a.H = P.H; a.L = P.L; a.Lp = P.Lp; a.d = P.d;
+        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+        // Scores of the first layer see the raw input (up to 1e3 in scale):
+        // fp32-accurate there; LayerNorm bounds every later layer's input.
+        if ((e = launch_attn(P.mode, P.dh, l == 0, a, s)) != hipSuccess) return e;
+
+        GemmArgs r{};
+        r.A = O; r.W = w.w_o; r.bias = w.b_o; r.M = M; r.N = P.d; r.K = P.d; r.R = Xr; r.Z = Z;
+        if ((e = launch_gemm(P.mode, EPI_RES, r, s)) != hipSuccess) return e;
+        if ((e = launch_ln(P.mode, Z, w.ln1_g, w.ln1_b, P.eps, M, P.d, X1, A, nullptr, s)) != hipSuccess) return e;
+
+        GemmArgs u{};
+        u.A = A; u.W = w.w_1; u.bias = w.b_1; u.M = M; u.N = P.f; u.K = P.d; u.out = G;
+        if ((e = launch_gemm(P.mode, EPI_GELU, u, s)) != hipSuccess) return e;
+        GemmArgs dn{};
+        dn.A = G; dn.W = w.w_2; dn.bias = w.b_2; dn.M = M; dn.N = P.d; dn.K = P.f; dn.R = X1; dn.Z = Z;
+        if ((e = launch_gemm(P.mode, EPI_RES, dn, s)) != hipSuccess) return e;
+        if (last)
+            e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, nullptr, nullptr, y, s);
+        else
+            e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, Xr, A, nullptr, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,
+                    hipStream_t s) {
+    switch (p.path) {
+        case TFL_PATH_TILED: return run_tiled(p, layers, x, lens, y, ws, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tfl

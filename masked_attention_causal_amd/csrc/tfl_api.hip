@@ -1,0 +1,124 @@
+// C ABI of tfl: argument checks, the frozen per-shape plan, the workspace
+// layout and the launch sequence.  Declarations and contracts: include/tfl.h.
+#include "tfl.h"
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+
+struct tfl_handle {
+    tfl_config cfg;
+    std::vector<tfl_layer> layers;
+    tfl::Plan plan;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+tfl_status fail(tfl_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+tfl_status hip_fail(hipError_t e, const char* what) {
+    return fail(TFL_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+tfl_status tfl_create(const tfl_config* cfg, const tfl_layer* layers, tfl_handle** out) {
+    if (!cfg || !layers || !out) return fail(TFL_E_INVALID, "tfl_create: null argument");
+    *out = nullptr;
+    std::string why;
+    tfl::Plan plan;
+    const tfl_status st = tfl::make_plan(*cfg, &plan, &why);
+    if (st != TFL_OK) return fail(st, "tfl_create: " + why);
+    const size_t es = tfl::dtype_size(cfg->dtype);
+    for (int l = 0; l < cfg->n_layers; l++) {
+        const tfl_layer& w = layers[l];
+        const void* mats[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
+        const void* vecs[8] = {w.b_qkv, w.b_o, w.ln1_g, w.ln1_b, w.b_1, w.b_2, w.ln2_g, w.ln2_b};
+        for (const void* m : mats)
+            if (!m || !aligned(m, 16))
+                return fail(TFL_E_INVALID, "tfl_create: layer " + std::to_string(l) +
+                                               ": weight matrix pointer null or not 16-byte aligned");
+        for (const void* v : vecs)
+            if (!v || !aligned(v, es))
+                return fail(TFL_E_INVALID, "tfl_create: layer " + std::to_string(l) +
+                                               ": bias/LayerNorm pointer null or misaligned");
+    }
+    tfl_handle* h = new (std::nothrow) tfl_handle;
+    if (!h) return fail(TFL_E_INTERNAL, "tfl_create: out of host memory");
+    h->cfg = *cfg;
+    h->layers.assign(layers, layers + cfg->n_layers);
+    h->plan = plan;
+    *out = h;
+    return TFL_OK;
+}
+
+tfl_status tfl_workspace_bytes(const tfl_handle* h, size_t* bytes) {
+    if (!h || !bytes) return fail(TFL_E_INVALID, "tfl_workspace_bytes: null argument");
+    *bytes = h->plan.ws_bytes;
+    return TFL_OK;
+}
+
+tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, void* y, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    if (!h) return fail(TFL_E_INVALID, "tfl_forward: null handle");
+    if (!x || !y || !valid_len) return fail(TFL_E_INVALID, "tfl_forward: null x, y or valid_len");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(valid_len, 4))
+        return fail(TFL_E_INVALID, "tfl_forward: x and y must be 16-byte aligned, valid_len 4-byte aligned");
+    const tfl::Plan& P = h->plan;
+    if (workspace_bytes < P.ws_bytes)
+        return fail(TFL_E_WORKSPACE, "tfl_forward: workspace of " + std::to_string(workspace_bytes) +
+                                         " bytes, plan needs " + std::to_string(P.ws_bytes));
+    if (P.ws_bytes > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(TFL_E_INVALID, "tfl_forward: workspace null or not 256-byte aligned");
+    const size_t io_bytes = (size_t)P.T * P.d * tfl::dtype_size(h->cfg.dtype);
+    if (overlap(x, io_bytes, y, io_bytes)) return fail(TFL_E_INVALID, "tfl_forward: y overlaps x");
+    if (P.ws_bytes > 0 && overlap(y, io_bytes, workspace, P.ws_bytes))
+        return fail(TFL_E_INVALID, "tfl_forward: y overlaps the workspace");
+    hipStream_t s = (hipStream_t)hip_stream;
+
+    const char* chk = std::getenv("TFL_CHECK");
+    if (chk && chk[0] == '1') {
+        std::vector<int32_t> lens(P.B);
+        hipError_t e = hipMemcpyAsync(lens.data(), valid_len, sizeof(int32_t) * P.B, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "tfl_forward: TFL_CHECK copy of valid_len");
+        for (int b = 0; b < P.B; b++)
+            if (lens[b] < 1 || lens[b] > P.L)
+                return fail(TFL_E_INVALID, "tfl_forward: valid_len[" + std::to_string(b) + "] = " +
+                                               std::to_string(lens[b]) + " outside [1, seq_len]");
+    }
+    const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "tfl_forward: kernel launch");
+    return TFL_OK;
+}
+
+tfl_status tfl_destroy(tfl_handle* h) {
+    delete h;
+    return TFL_OK;
+}
+
+const char* tfl_plan_name(const tfl_handle* h) { return h ? h->plan.name : "(null handle)"; }
+
+int32_t tfl_plan_path(const tfl_handle* h) { return h ? h->plan.path : -1; }
+
+const char* tfl_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

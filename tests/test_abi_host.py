@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed: tfl_create and every
+argument check run before any device call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import masked_attention_causal_amd as tfl
+from masked_attention_causal_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tfl.load_library()
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "tfl.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"\b(tfl_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert set(names) == set(tfl.SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_workload_plans():
+    for name, w in synth.WORKLOADS.items():
+        plan, path, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype)
+        assert path in ("seq", "pq", "tiled"), (name, plan)
+        assert ws > 0
+        assert plan.upper().startswith(path.upper())
+
+
+def test_workspace_covers_the_tiled_buffers():
+    w = synth.WORKLOADS["stream_d64_b1_l100000"]
+    _, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
+    T = w.B * w.L
+    Lp = (w.L + 63) // 64 * 64
+    need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2
+    assert need <= ws <= need + 9 * 256
+
+
+@pytest.mark.parametrize("cfg,status", [
+    (dict(n_layers=0), 1), (dict(d_model=0), 1), (dict(batch=0), 1), (dict(seq_len=-3), 1),
+    (dict(n_heads=3), 1), (dict(dtype=7), 1), (dict(force_path=9), 1),
+    (dict(d_model=48, n_heads=1), 2), (dict(d_model=256, n_heads=2), 2), (dict(d_ffn=100), 2),
+    (dict(d_model=2048, n_heads=32), 2), (dict(batch=70000), 2),
+])
+def test_create_rejects(cfg, status):
+    base = dict(n_layers=2, d_model=64, n_heads=4, d_ffn=128, batch=2, seq_len=16, dtype="f16")
+    base.update(cfg)
+    with pytest.raises(tfl.TflError) as e:
+        tfl.plan_for(**base)
+    assert e.value.status == status
+    assert "tfl_create" in str(e.value)
+
+
+def test_create_rejects_bad_layer_pointers(lib):
+    cfg = tfl.make_config(1, 64, 4, 128, 2, 16, "f16")
+    good = {k: 0x10000 for k in tfl.LAYER_KEYS}
+    for key, val in (("w_qkv", 0), ("w_1", 0x10008), ("b_o", 0x10001), ("ln2_b", 0)):
+        bad = dict(good)
+        bad[key] = val
+        with pytest.raises(tfl.TflError) as e:
+            tfl.Handle(cfg, [bad])
+        assert e.value.status == 1
+
+
+def test_forward_argument_checks_before_any_device_call(lib):
+    cfg = tfl.make_config(1, 64, 4, 128, 2, 16, "f16")
+    h = tfl.Handle(cfg, [{k: 0x10000 for k in tfl.LAYER_KEYS}])
+    n = h.workspace_bytes
+    X, Y, LN, WS = 0x100000, 0x200000, 0x300000, 0x400000
+    cases = [
+        ((0, LN, Y, WS, n), 1),           # null x
+        ((X, 0, Y, WS, n), 1),            # null lens
+        ((X + 8, LN, Y, WS, n), 1),       # misaligned x
+        ((X, LN, Y, WS, n - 1), 3),       # workspace too small
+        ((X, LN, Y, WS + 16, n), 1),      # workspace misaligned
+        ((X, LN, X + 256, WS, n), 1),     # y overlaps x
+        ((X, LN, WS + 512, WS, n), 1),    # y overlaps workspace
+    ]
+    for args, status in cases:
+        with pytest.raises(tfl.TflError) as e:
+            h.forward_raw(*args, 0)
+        assert e.value.status == status, args
+    st = lib.tfl_forward(None, X, LN, Y, WS, n, None)
+    assert st == 1
+    h.close()
+
+
+def test_null_handle_queries(lib):
+    assert lib.tfl_plan_path(None) == -1
+    assert lib.tfl_destroy(None) == 0
+    n = ctypes.c_size_t()
+    assert lib.tfl_workspace_bytes(None, ctypes.byref(n)) == 1
+
+
+def test_library_does_not_link_the_oracle():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", tfl.LIB_PATH], capture_output=True, text=True).stdout
+    assert "orc_" not in out
+    src = os.path.join(ROOT, "masked_attention_causal_amd", "csrc")
+    for f in os.listdir(src):
+        with open(os.path.join(src, f)) as fh:
+            assert "oracle" not in fh.read().lower(), f

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every comparison is element by element under the gate of ``tests/gate.py``
+(atol 0.002 OR rtol 0.02 against the unrounded fp64 oracle).  Small shapes
+span several GEMM/attention tiles with ragged tails; the five named
+workloads run at full size, with the oracle evaluated on sampled sequences
+(batch independence) or on a causal prefix (rows < n depend on nothing past
+n) where the whole oracle would take minutes.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from masked_attention_causal_amd import synth
+from tests.gate import assert_gate, gate, gpu_forward, oracle_forward, say
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+
+def _case(w, seed, scale=None, affine=False, lens=None):
+    return synth.make_inputs(w, seed, scale=scale, affine=affine, lens=lens)
+
+
+SMALL = [
+    W("s_f32_dh16", 2, 64, 4, 96, 3, 150, "f32", 1, 150, 1.0),
+    W("s_f32_dh64", 2, 128, 2, 256, 2, 200, "f32", 1, 200, 1.0),
+    W("s_f16_dh16", 2, 64, 4, 128, 3, 130, "f16", 1, 130, 1.0),
+    W("s_f16_dh32", 2, 96, 3, 160, 2, 70, "f16", 1, 70, 1.0),
+    W("s_f16_dh64", 2, 256, 4, 512, 5, 64, "f16", 8, 64, 1.0),
+    W("s_bf16_dh64", 3, 128, 2, 256, 2, 190, "bf16", 1, 190, 1.0),
+    W("s_bf16_d1024", 2, 1024, 16, 4096, 1, 100, "bf16", 60, 100, 1.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+def test_small_shapes(w, scale):
+    for seed in (0, 1):
+        inp = _case(w, seed, scale, affine=(seed == 1))
+        inp.lens[0] = w.L                       # one full-length and one length-1 sequence
+        if w.B > 1:
+            inp.lens[1] = 1
+        say(f"[small] {w.name} seed={seed} scale={scale} lens={inp.lens.tolist()}")
+        y = gpu_forward(inp)
+        assert_gate(y, oracle_forward(inp), f"{w.name} seed {seed} scale {scale}")
+
+
+# ---------------------------------------------------------------- the five workloads at full size
+
+TINY = synth.WORKLOADS["tiny_d32_b4_l32"]
+BATCH = synth.WORKLOADS["batch4096_d256_l64"]
+GEMM = synth.WORKLOADS["gemm_d1024_b8_l512"]
+LAT = synth.WORKLOADS["latency_d128_b1_l4096"]
+STREAM = synth.WORKLOADS["stream_d64_b1_l100000"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_workload(seed):
+    for scale, affine in [(1.0, False), (1e-3, False), (1e-2, False), (1e-1, False), (10.0, False),
+                          (1e2, False), (1e3, False), (1.0, True)]:
+        inp = _case(TINY, seed, scale, affine)
+        say(f"[tiny] seed={seed} scale={scale} affine={affine}")
+        assert_gate(gpu_forward(inp), oracle_forward(inp), f"tiny seed {seed} scale {scale}")
+
+
+def _sample_rows(lens, n, rng):
+    order = np.argsort(lens, kind="stable")
+    pick = set([int(order[0]), int(order[-1])])
+    while len(pick) < n:
+        pick.add(int(rng.integers(0, len(lens))))
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("seed,scale", [(0, None), (1, None), (2, None), (0, 1e-3), (0, 1e-2), (0, 1e-1),
+                                        (0, 1.0), (0, 10.0), (0, 1e2), (0, 1e3)])
+def test_batch4096_workload(seed, scale):
+    inp = _case(BATCH, seed, scale)
+    say(f"[batch4096] seed={seed} scale={inp.scale:.4g}")
+    y = gpu_forward(inp)
+    rows = _sample_rows(inp.lens, 16, np.random.default_rng(seed))
+    ref = oracle_forward(synth.subset(inp, rows))
+    assert_gate(y[rows], ref, f"batch4096 seed {seed} scale {inp.scale}")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("seed,scale", [(0, 1.0), (1, 1.0), (2, 1.0), (0, 1e-3), (0, 1e3)])
+def test_gemm_workload(seed, scale):
+    inp = _case(GEMM, seed, scale)
+    say(f"[gemm] seed={seed} scale={scale}")
+    y = gpu_forward(inp)
+    rows = np.array([int(np.argmin(inp.lens)), int(np.argmax(inp.lens))])
+    ref = oracle_forward(synth.subset(inp, rows))
+    assert_gate(y[rows], ref, f"gemm seed {seed} scale {scale}")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+def test_latency_workload(scale):
+    inp = _case(LAT, 0, scale)
+    say(f"[latency] scale={scale}")
+    assert_gate(gpu_forward(inp), oracle_forward(inp), f"latency scale {scale}")
+
+
+def test_stream_workload_prefix_and_golden_rows():
+    inp = _case(STREAM, 0, 1.0)
+    say("[stream] full 100000-token forward")
+    y = gpu_forward(inp)
+    assert np.isfinite(y).all()
+    n = 3000
+    say(f"[stream] oracle on the first {n} rows")
+    assert_gate(y[:, :n], oracle_forward(synth.prefix(inp, n)), "stream prefix")
+    path = os.path.join(os.path.dirname(__file__), "golden", "stream_d64_l100000_seed0_rows.json")
+    with open(path) as fh:
+        gold = json.load(fh)
+    rows = np.array(gold["rows"])
+    ref = np.array(gold["values"], np.float64)
+    say(f"[stream] {len(rows)} stored oracle rows")
+    assert_gate(y[0, rows], ref, "stream golden rows")
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_edge_shapes(dtype):
+    cases = [
+        (W("e_l1", 2, 64, 4, 64, 3, 1, dtype, 1, 1, 1.0), None),
+        (W("e_len1", 2, 64, 2, 64, 3, 70, dtype, 1, 1, 1.0), None),
+        (W("e_full", 2, 64, 2, 64, 2, 65, dtype, 65, 65, 1.0), None),
+        (W("e_l17", 1, 32, 2, 32, 1, 17, dtype, 1, 17, 1.0), None),
+        (W("e_l63", 2, 64, 1, 64, 2, 63, dtype, 1, 63, 1.0), None),
+    ]
+    for w, lens in cases:
+        inp = _case(w, 3, lens=lens)
+        say(f"[edge] {w.name} {dtype} lens={inp.lens.tolist()}")
+        assert_gate(gpu_forward(inp), oracle_forward(inp), f"{w.name} {dtype}")
+
+
+# ---------------------------------------------------------------- bit-exact invariants on the GPU
+
+INV = W("inv", 2, 64, 4, 128, 3, 140, "f16", 1, 140, 1.0)
+
+
+def test_gpu_padding_and_causal_invariance():
+    inp = _case(INV, 5, lens=np.array([140, 70, 3], np.int32))
+    y = gpu_forward(inp)
+    p = synth.make_inputs(INV, 5, lens=inp.lens)
+    p.x = inp.x.copy()
+    p.x[1, 100] = synth.round_to(synth.to_f64(p.x[1, 100], "f16") + 1.5, "f16")   # padding position
+    p.x[0, 90] = synth.round_to(synth.to_f64(p.x[0, 90], "f16") - 2.0, "f16")     # causal position
+    say("[invariance] perturbed padding and causal positions")
+    y2 = gpu_forward(p)
+    assert np.array_equal(y[0, :90], y2[0, :90])
+    assert not np.array_equal(y[0, 90:], y2[0, 90:])
+    keep = np.ones(140, bool)
+    keep[100] = False
+    assert np.array_equal(y[1, keep], y2[1, keep])
+    assert np.array_equal(y[2], y2[2])
+
+
+def test_gpu_batch_independence_and_determinism():
+    inp = _case(INV, 6)
+    y = gpu_forward(inp)
+    say("[determinism] second run")
+    assert np.array_equal(y, gpu_forward(inp))
+    for b in range(INV.B):
+        sub = synth.subset(inp, [b])
+        say(f"[batch independence] sequence {b} alone")
+        assert np.array_equal(gpu_forward(sub)[0], y[b])
+
+
+# ---------------------------------------------------------------- error statuses through the ABI
+
+
+def test_forward_error_statuses(monkeypatch):
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    w = W("err", 1, 64, 2, 64, 2, 16, "f16", 1, 16, 1.0)
+    inp = _case(w, 0)
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers)
+    x = tfl.to_device(inp.x, w.dtype)
+    lens = torch.from_numpy(inp.lens).cuda()
+    y = torch.empty_like(x)
+    h = enc.handle
+    ws = enc.workspace()
+    st = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(tfl.TflError) as e:
+        h.forward_raw(x.data_ptr(), lens.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes - 1, st)
+    assert e.value.status == 3
+    with pytest.raises(tfl.TflError) as e:
+        h.forward_raw(x.data_ptr(), lens.data_ptr(), x.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
+    assert e.value.status == 1
+    with pytest.raises(tfl.TflError) as e:
+        h.forward_raw(x.data_ptr(), 0, y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
+    assert e.value.status == 1
+    bad = torch.tensor([0, 17], dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("TFL_CHECK", "1")
+    with pytest.raises(tfl.TflError) as e:
+        h.forward_raw(x.data_ptr(), bad.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
+    assert e.value.status == 1
+    h.forward_raw(x.data_ptr(), lens.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
+    monkeypatch.delenv("TFL_CHECK")
+    # out-of-range lengths without the check are clamped: results equal those of the clamped lengths
+    say("[clamp] lengths 0 and 99 behave as 1 and L")
+    h.forward_raw(x.data_ptr(), bad.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
+    torch.cuda.synchronize()
+    clamped = synth.make_inputs(w, 0, lens=np.array([1, 16], np.int32))
+    assert_gate(tfl.to_numpy_f64(y), oracle_forward(clamped), "clamped lengths")
+    enc.close()
