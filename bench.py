@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the masked post-LN encoder-stack forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one full forward of the layer stack (every layer, every stage)
+over one batch of seeded synthetic input already resident in HBM.  The
+default workload is the 2-layer, d_model 256, 4-head, FFN 1024, fp16,
+batch 4096 x 64-token one with valid lengths uniform in [8, 64].
+
+Prints one JSON line: sequences/s (value), ms per forward, the roofline of
+the dominant kernel (its algorithmic bytes or FLOPs per launch over its
+average launch time, measured with HIP events on the forward's stream inside
+the timed region) and the fp64 CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+
+
+def allowed_pairs(lens, L):
+    """S = sum_b sum_{i<L} min(i+1, len_b): (query, key) pairs that pass the mask."""
+    s = 0
+    for n in lens:
+        n = int(n)
+        s += n * (n + 1) // 2 + (L - n) * n
+    return s
+
+
+def stage_work(w, stage, lens):
+    """Algorithmic (FLOPs, HBM bytes) of ONE launch of a stage (one layer).
+    Operand dtype: fp32 for fp32 I/O, fp16 otherwise; residual, Q and K fp32."""
+    T, d, f, H = w.B * w.L, w.d, w.f, w.H
+    io = 4 if w.dtype == "f32" else 2
+    op = io
+    wt = io
+    if stage == "prep":
+        return 0.0, T * d * (io + 4 + op)
+    if stage == "qkv":
+        return 2.0 * T * d * 3 * d, T * d * op + 3 * d * d * wt + 2 * T * d * 4 + T * d * op
+    if stage == "attn":
+        S = allowed_pairs(lens, w.L)
+        return 4.0 * d * S, 2 * T * d * 4 + T * d * op + T * d * op + 4 * w.B
+    if stage == "out":
+        return 2.0 * T * d * d, T * d * op + d * d * wt + 2 * T * d * 4
+    if stage == "ln":
+        return 0.0, T * d * 4 + T * d * (4 + op)
+    if stage == "ffn1":
+        return 2.0 * T * d * f, T * d * op + f * d * wt + T * f * op
+    if stage == "ffn2":
+        return 2.0 * T * f * d, T * f * op + d * f * wt + 2 * T * d * 4
+    if stage == "fused":
+        S = allowed_pairs(lens, w.L)
+        flops = w.n_layers * (2.0 * T * d * 3 * d + 4.0 * d * S + 2.0 * T * d * d + 4.0 * T * d * f)
+        weights = w.n_layers * (3 * d * d + d * d + 2 * d * f + 6 * d + f) * wt
+        return flops, 2 * T * d * io + weights + 4 * w.B
+    raise ValueError(stage)
+
+
+STAGES_TILED = ("prep", "qkv", "attn", "out", "ln", "ffn1", "ffn2")
+
+
+def launches_per_forward(stage, n_layers):
+    return {"prep": 1, "ln": 2 * n_layers, "fused": 1}.get(stage, n_layers)
+
+
+def roofline(w, stage, lens, avg_ms):
+    flops, nbytes = stage_work(w, stage, lens)
+    t_mfma = flops / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    sec = avg_ms / 1e3
+    if t_mfma >= t_hbm:
+        ach = flops / sec / 1e12
+        peak = PEAK_MFMA_TFLOPS[w.dtype]
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel_stage": stage,
+                "avg_launch_us": round(avg_ms * 1e3, 2), "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": nbytes}
+    ach = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel_stage": stage,
+            "avg_launch_us": round(avg_ms * 1e3, 2), "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": nbytes}
+
+
+def cpu_baseline(w, inp, target_s=15.0):
+    """The fp64 oracle, as it is, on a bounded sample of the same inputs."""
+    import numpy as np
+
+    import oracle
+    from masked_attention_causal_amd import synth
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    if w.B == 1:
+        if w.L > 8192:
+            return None
+        t0 = time.perf_counter()
+        oracle.forward(inp.x64(), inp.lens, inp.layers64(), w.H)
+        dt = time.perf_counter() - t0
+        return {"value": round(1.0 / dt, 4), "unit": "sequences/s", "cores": threads, "kind": "oracle",
+                "sample": f"the whole batch-1 workload once ({dt:.2f} s)"}
+    n0 = min(w.B, 16)
+    sub = synth.subset(inp, np.arange(n0))
+    t0 = time.perf_counter()
+    oracle.forward(sub.x64(), sub.lens, sub.layers64(), w.H)
+    dt0 = time.perf_counter() - t0
+    n = int(min(w.B, max(n0, n0 * target_s / max(dt0, 1e-3))))
+    sub = synth.subset(inp, np.arange(n))
+    x64, l64 = sub.x64(), sub.layers64()
+    t0 = time.perf_counter()
+    oracle.forward(x64, sub.lens, l64, w.H)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "sequences/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.B} sequences of the same seeded batch, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--path", default="auto", choices=["auto", "seq", "pq", "tiled"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    from masked_attention_causal_amd import synth
+
+    name = args.workload or synth.BENCH_WORKLOAD
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, args.seed)
+    torch.cuda.set_device(0)
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=args.path)
+    x = tfl.to_device(inp.x, w.dtype)
+    lens = torch.from_numpy(inp.lens).cuda()
+    y = torch.empty_like(x)
+    ws = enc.workspace()
+    h = enc.handle
+    print(f"# workload {name} plan {enc.plan_name} workspace {h.workspace_bytes / 2**20:.1f} MiB", file=sys.stderr,
+          flush=True)
+
+    # first call in this process, then warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    enc.forward(x, lens, y, ws)
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup):
+        enc.forward(x, lens, y, ws)
+    torch.cuda.synchronize()
+
+    # per-stage survey (not timed): which kernel dominates the forward
+    stages = ("fused",) if enc.plan_path in ("seq", "pq") else STAGES_TILED
+    survey = {}
+    for st in stages:
+        per = launches_per_forward(st, w.n_layers)
+        h.timer_arm(st, per * 3)
+        for _ in range(3):
+            enc.forward(x, lens, y, ws)
+        ms, n = h.timer_read()
+        survey[st] = ms / 3.0
+    dom = max(survey, key=survey.get)
+
+    # timed region: K steps, dominant stage timed with HIP events as it runs
+    per = launches_per_forward(dom, w.n_layers)
+    h.timer_arm(dom, per * args.steps)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        enc.forward(x, lens, y, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dom_ms, dom_n = h.timer_read()
+    ms_step = total_ms / args.steps
+    seqs = w.B / (ms_step / 1e3)
+    roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1))
+    roof["launches_timed"] = dom_n
+
+    # whole-forward roofline figure for context
+    tot_flops = 0.0
+    for st in (("fused",) if enc.plan_path in ("seq", "pq") else ("qkv", "attn", "out", "ffn1", "ffn2")):
+        tot_flops += stage_work(w, st, inp.lens)[0] * (1 if st == "fused" else w.n_layers)
+    fwd_tflops = tot_flops / (ms_step / 1e3) / 1e12
+
+    cpu = None if args.no_cpu else cpu_baseline(w, inp)
+    out = {
+        "metric": "sequences/s per stack forward (with us per forward and roofline fraction)",
+        "value": round(seqs, 1),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_forward": round(ms_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normals, weights N(0,0.02^2), random valid lengths)",
+        "config": {"workload": name, "n_layers": w.n_layers, "d_model": w.d, "n_heads": w.H, "d_ffn": w.f,
+                   "batch": w.B, "seq_len": w.L, "valid_len": [w.len_lo, w.len_hi],
+                   "input_scale": round(inp.scale, 6), "seed": args.seed, "plan": enc.plan_name,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "forward_tflops": round(fwd_tflops, 2),
+        "stage_ms_per_forward": {k: round(v, 4) for k, v in survey.items()},
+        "cold_first_call_ms": round(cold_ms, 2),
+        "cpu_baseline": cpu,
+    }
+    enc.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

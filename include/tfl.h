@@ -125,6 +125,29 @@ const char *tfl_plan_name(const tfl_handle *h);
 /* Path of the frozen plan (a tfl_path value), or -1 for a NULL handle. */
 int32_t tfl_plan_path(const tfl_handle *h);
 
+/* Kernel stages, for stage timing. */
+typedef enum {
+    TFL_STAGE_PREP = 1,  /* input staging: x -> fp32 residual + operand copy */
+    TFL_STAGE_QKV = 2,   /* fused QKV projection, head-major epilogue */
+    TFL_STAGE_ATTN = 3,  /* streaming masked attention */
+    TFL_STAGE_OUT = 4,   /* out-projection + bias + residual */
+    TFL_STAGE_LN = 5,    /* residual LayerNorm */
+    TFL_STAGE_FFN1 = 6,  /* FFN up-projection + exact-erf GELU */
+    TFL_STAGE_FFN2 = 7,  /* FFN down-projection + bias + residual */
+    TFL_STAGE_FUSED = 8  /* whole-stack kernels of the SEQ and PQ paths */
+} tfl_stage;
+
+/* Measurement aid.  Arms HIP-event timing of every launch of one stage in
+ * the following tfl_forward calls on this handle, up to max_launches
+ * launches (the events are recorded on the forward's stream around each
+ * launch of that stage, nothing else changes).  Re-arming discards earlier
+ * records.  No device memory is allocated (HIP events only). */
+tfl_status tfl_timer_arm(tfl_handle *h, int32_t stage, int32_t max_launches);
+
+/* Waits for the recorded events, returns the summed kernel time in ms and
+ * the number of launches timed, and disarms the timer. */
+tfl_status tfl_timer_read(tfl_handle *h, float *total_ms, int32_t *launches);
+
 /* Thread-local message describing the last non-OK status. */
 const char *tfl_last_error(void);
 

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(PKG, "libtfl.so")
 LAYER_KEYS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
               "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 SYMBOLS = ("tfl_create", "tfl_workspace_bytes", "tfl_forward", "tfl_destroy",
-           "tfl_plan_name", "tfl_plan_path", "tfl_last_error")
+           "tfl_plan_name", "tfl_plan_path", "tfl_timer_arm", "tfl_timer_read", "tfl_last_error")
+STAGES = {"prep": 1, "qkv": 2, "attn": 3, "out": 4, "ln": 5, "ffn1": 6, "ffn2": 7, "fused": 8}
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 PATHS = {"auto": 0, "seq": 1, "pq": 2, "tiled": 3}
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     L.tfl_plan_name.restype = ctypes.c_char_p
     L.tfl_plan_path.argtypes = [vp]
     L.tfl_plan_path.restype = ctypes.c_int32
+    L.tfl_timer_arm.argtypes = [vp, ctypes.c_int32, ctypes.c_int32]
+    L.tfl_timer_arm.restype = ctypes.c_int
+    L.tfl_timer_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
+    L.tfl_timer_read.restype = ctypes.c_int
     L.tfl_last_error.argtypes = []
     L.tfl_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -112,6 +117,16 @@ class Handle:
 
     def forward_raw(self, x: int, lens: int, y: int, ws: int, ws_bytes: int, stream: int) -> None:
         _check(load_library().tfl_forward(self._h, x, lens, y, ws, ws_bytes, stream))
+
+    def timer_arm(self, stage: str, max_launches: int) -> None:
+        _check(load_library().tfl_timer_arm(self._h, STAGES[stage], int(max_launches)))
+
+    def timer_read(self):
+        """(summed kernel ms, launches) of the armed stage since arming."""
+        ms = ctypes.c_float()
+        n = ctypes.c_int32()
+        _check(load_library().tfl_timer_read(self._h, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -22,6 +22,15 @@ struct Plan {
     size_t ws_bytes;
 };
 
+// HIP-event timing of one stage's launches (see tfl_timer_arm).
+struct StageTimer {
+    int stage = 0;
+    int cap = 0;
+    int n = 0;
+    hipEvent_t* start = nullptr;
+    hipEvent_t* stop = nullptr;
+};
+
 size_t dtype_size(int dtype);
 
 // The dispatcher's rule for a valid configuration (tfl_path, never AUTO).
@@ -30,6 +39,6 @@ int choose_path(const tfl_config& cfg);
 tfl_status make_plan(const tfl_config& cfg, Plan* p, std::string* why);
 
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
-                    char* ws, hipStream_t s);
+                    char* ws, hipStream_t s, StageTimer* timer);
 
 }  // namespace tfl

@@ -96,8 +96,25 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     return TFL_OK;
 }
 
+// Records the timer's events around one launch when its stage is armed.
+struct Timed {
+    StageTimer* t;
+    hipStream_t s;
+    int idx = -1;
+    Timed(StageTimer* t_, int stage, hipStream_t s_) : t(t_), s(s_) {
+        if (t && t->stage == stage && t->n < t->cap) {
+            idx = t->n++;
+            (void)hipEventRecord(t->start[idx], s);
+        }
+    }
+    hipError_t done(hipError_t e) {
+        if (idx >= 0) (void)hipEventRecord(t->stop[idx], s);
+        return e;
+    }
+};
+
 static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
-                            char* ws, hipStream_t s) {
+                            char* ws, hipStream_t s, StageTimer* T) {
     float* Xr = (float*)(ws + P.off_Xr);
     float* X1 = (float*)(ws + P.off_X1);
     float* Z = (float*)(ws + P.off_Z);
@@ -108,7 +125,11 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
     void* Vt = ws + P.off_Vt;
     void* G = ws + P.off_G;
     const int M = (int)P.T;
-    hipError_t e = launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s);
+    hipError_t e;
+    {
+        Timed tm(T, TFL_STAGE_PREP, s);
+        e = tm.done(launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s));
+    }
     if (e != hipSuccess) return e;
     for (int l = 0; l < P.n_layers; l++) {
         const tfl_layer& w = layers[l];
@@ -118,7 +139,10 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         g.M = M; g.N = 3 * P.d; g.K = P.d;
         g.Q = Q; g.Kd = K; g.Vt = Vt;
         g.L = P.L; g.Lp = P.Lp; g.H = P.H; g.dh = P.dh; g.d = P.d;
-        if ((e = launch_gemm(P.mode, EPI_QKV, g, s)) != hipSuccess) return e;
+        {
+            Timed tm(T, TFL_STAGE_QKV, s);
+            if ((e = tm.done(launch_gemm(P.mode, EPI_QKV, g, s))) != hipSuccess) return e;
+        }
 
         AttnArgs a{};
         a.Q = Q; a.K = K; a.Vt = Vt; a.O = O; a.lens = lens;
@@ -126,32 +150,51 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
         // Scores of the first layer see the raw input (up to 1e3 in scale):
         // fp32-accurate there; LayerNorm bounds every later layer's input.
-        if ((e = launch_attn(P.mode, P.dh, l == 0, a, s)) != hipSuccess) return e;
+        {
+            Timed tm(T, TFL_STAGE_ATTN, s);
+            if ((e = tm.done(launch_attn(P.mode, P.dh, l == 0, a, s))) != hipSuccess) return e;
+        }
 
         GemmArgs r{};
         r.A = O; r.W = w.w_o; r.bias = w.b_o; r.M = M; r.N = P.d; r.K = P.d; r.R = Xr; r.Z = Z;
-        if ((e = launch_gemm(P.mode, EPI_RES, r, s)) != hipSuccess) return e;
-        if ((e = launch_ln(P.mode, Z, w.ln1_g, w.ln1_b, P.eps, M, P.d, X1, A, nullptr, s)) != hipSuccess) return e;
+        {
+            Timed tm(T, TFL_STAGE_OUT, s);
+            if ((e = tm.done(launch_gemm(P.mode, EPI_RES, r, s))) != hipSuccess) return e;
+        }
+        {
+            Timed tm(T, TFL_STAGE_LN, s);
+            if ((e = tm.done(launch_ln(P.mode, Z, w.ln1_g, w.ln1_b, P.eps, M, P.d, X1, A, nullptr, s))) != hipSuccess)
+                return e;
+        }
 
         GemmArgs u{};
         u.A = A; u.W = w.w_1; u.bias = w.b_1; u.M = M; u.N = P.f; u.K = P.d; u.out = G;
-        if ((e = launch_gemm(P.mode, EPI_GELU, u, s)) != hipSuccess) return e;
+        {
+            Timed tm(T, TFL_STAGE_FFN1, s);
+            if ((e = tm.done(launch_gemm(P.mode, EPI_GELU, u, s))) != hipSuccess) return e;
+        }
         GemmArgs dn{};
         dn.A = G; dn.W = w.w_2; dn.bias = w.b_2; dn.M = M; dn.N = P.d; dn.K = P.f; dn.R = X1; dn.Z = Z;
-        if ((e = launch_gemm(P.mode, EPI_RES, dn, s)) != hipSuccess) return e;
-        if (last)
-            e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, nullptr, nullptr, y, s);
-        else
-            e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, Xr, A, nullptr, s);
-        if (e != hipSuccess) return e;
+        {
+            Timed tm(T, TFL_STAGE_FFN2, s);
+            if ((e = tm.done(launch_gemm(P.mode, EPI_RES, dn, s))) != hipSuccess) return e;
+        }
+        {
+            Timed tm(T, TFL_STAGE_LN, s);
+            if (last)
+                e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, nullptr, nullptr, y, s);
+            else
+                e = launch_ln(P.mode, Z, w.ln2_g, w.ln2_b, P.eps, M, P.d, Xr, A, nullptr, s);
+            if ((e = tm.done(e)) != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
 
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,
-                    hipStream_t s) {
+                    hipStream_t s, StageTimer* timer) {
     switch (p.path) {
-        case TFL_PATH_TILED: return run_tiled(p, layers, x, lens, y, ws, s);
+        case TFL_PATH_TILED: return run_tiled(p, layers, x, lens, y, ws, s, timer);
     }
     return hipErrorInvalidValue;
 }

@@ -14,6 +14,7 @@ struct tfl_handle {
     tfl_config cfg;
     std::vector<tfl_layer> layers;
     tfl::Plan plan;
+    tfl::StageTimer timer;
 };
 
 namespace {
@@ -105,12 +106,72 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
                 return fail(TFL_E_INVALID, "tfl_forward: valid_len[" + std::to_string(b) + "] = " +
                                                std::to_string(lens[b]) + " outside [1, seq_len]");
     }
-    const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s);
+    tfl::StageTimer* tm = h->timer.stage ? &h->timer : nullptr;
+    const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s, tm);
     if (e != hipSuccess) return hip_fail(e, "tfl_forward: kernel launch");
     return TFL_OK;
 }
 
+static void timer_release(tfl::StageTimer& t) {
+    for (int i = 0; i < t.cap; i++) {
+        if (t.start) (void)hipEventDestroy(t.start[i]);
+        if (t.stop) (void)hipEventDestroy(t.stop[i]);
+    }
+    delete[] t.start;
+    delete[] t.stop;
+    t = tfl::StageTimer{};
+}
+
+tfl_status tfl_timer_arm(tfl_handle* h, int32_t stage, int32_t max_launches) {
+    if (!h) return fail(TFL_E_INVALID, "tfl_timer_arm: null handle");
+    if (stage < TFL_STAGE_PREP || stage > TFL_STAGE_FUSED || max_launches < 1 || max_launches > 1 << 20)
+        return fail(TFL_E_INVALID, "tfl_timer_arm: bad stage or launch count");
+    timer_release(h->timer);
+    tfl::StageTimer t;
+    t.start = new (std::nothrow) hipEvent_t[max_launches]();
+    t.stop = new (std::nothrow) hipEvent_t[max_launches]();
+    if (!t.start || !t.stop) {
+        delete[] t.start;
+        delete[] t.stop;
+        return fail(TFL_E_INTERNAL, "tfl_timer_arm: out of host memory");
+    }
+    for (int i = 0; i < max_launches; i++) {
+        hipError_t e = hipEventCreate(&t.start[i]);
+        if (e == hipSuccess) e = hipEventCreate(&t.stop[i]);
+        if (e != hipSuccess) {
+            t.cap = i + 1;
+            timer_release(t);
+            return hip_fail(e, "tfl_timer_arm: hipEventCreate");
+        }
+    }
+    t.cap = max_launches;
+    t.stage = stage;
+    h->timer = t;
+    return TFL_OK;
+}
+
+tfl_status tfl_timer_read(tfl_handle* h, float* total_ms, int32_t* launches) {
+    if (!h || !total_ms || !launches) return fail(TFL_E_INVALID, "tfl_timer_read: null argument");
+    tfl::StageTimer& t = h->timer;
+    float sum = 0.f;
+    for (int i = 0; i < t.n; i++) {
+        hipError_t e = hipEventSynchronize(t.stop[i]);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+        if (e != hipSuccess) {
+            timer_release(t);
+            return hip_fail(e, "tfl_timer_read");
+        }
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = t.n;
+    timer_release(t);
+    return TFL_OK;
+}
+
 tfl_status tfl_destroy(tfl_handle* h) {
+    if (h) timer_release(h->timer);
     delete h;
     return TFL_OK;
 }
