@@ -42,6 +42,24 @@ struct AttnArgs {
     float scale_log2;  // log2(e) / sqrt(dh)
 };
 
+// Weight pointers of one layer (same fields as tfl_layer).
+struct LayerPtrs {
+    const void *w_qkv, *b_qkv, *w_o, *b_o, *ln1_g, *ln1_b, *w_1, *b_1, *w_2, *b_2, *ln2_g, *ln2_b;
+};
+
+constexpr int SEQ_MAX_LAYERS = 8;
+
+// Sequence-resident path: whole stack in one launch.
+struct SeqArgs {
+    const void* x;   // [B, L, d] I/O dtype
+    void* y;         // [B, L, d] I/O dtype
+    const int32_t* lens;
+    int B, L, F, n_layers;
+    float eps;
+    float scale_log2;
+    LayerPtrs lw[SEQ_MAX_LAYERS];
+};
+
 // Fixed tile shapes shared with the planner.
 constexpr int ATT_KT = 64;   // keys per attention tile
 constexpr int ATT_BQ = 64;   // queries per attention workgroup
@@ -51,6 +69,9 @@ hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
 hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta, float eps,
                      int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);
+
+hipError_t launch_seq(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
+bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers);
 
 // Row layout of the LayerNorm kernel: lanes per row and float4 chunks per lane.
 // Returns false when d is not supported.

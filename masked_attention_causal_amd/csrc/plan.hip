@@ -16,8 +16,13 @@ namespace tfl {
 
 size_t dtype_size(int dtype) { return dtype == TFL_F32 ? 4 : 2; }
 
-int choose_path(const tfl_config& cfg) {
-    (void)cfg;
+static Mode mode_of(int dtype) { return dtype == TFL_F32 ? MODE_F32 : (dtype == TFL_F16 ? MODE_F16 : MODE_BF16); }
+
+int choose_path(const tfl_config& c) {
+    const int dh = c.d_model / c.n_heads;
+    // Short sequences: one workgroup keeps two whole sequences on chip for the
+    // whole stack (one launch, no intermediate HBM traffic).
+    if (seq_supported(mode_of(c.dtype), c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
     return TFL_PATH_TILED;
 }
 
@@ -60,13 +65,15 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         return TFL_E_UNSUPPORTED;
     }
     int path = c.force_path == TFL_PATH_AUTO ? choose_path(c) : c.force_path;
-    if (path != TFL_PATH_TILED) {
+    const Mode mode = mode_of(c.dtype);
+    if (path == TFL_PATH_PQ ||
+        (path == TFL_PATH_SEQ && !seq_supported(mode, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers))) {
         *why = "requested path is not available for this shape";
         return TFL_E_UNSUPPORTED;
     }
     Plan q{};
     q.path = path;
-    q.mode = c.dtype == TFL_F32 ? MODE_F32 : (c.dtype == TFL_F16 ? MODE_F16 : MODE_BF16);
+    q.mode = mode;
     q.n_layers = c.n_layers;
     q.d = c.d_model;
     q.H = c.n_heads;
@@ -78,6 +85,12 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     q.T = T;
     q.eps = c.ln_eps > 0.f ? c.ln_eps : 1e-5f;
     q.op = q.mode == MODE_F32 ? 4 : 2;
+    if (path == TFL_PATH_SEQ) {
+        q.ws_bytes = 0;  // everything stays on chip
+        std::snprintf(q.name, sizeof(q.name), "SEQ/2x64tok/w8/f16op");
+        *p = q;
+        return TFL_OK;
+    }
     const size_t Td = (size_t)T * q.d;
     size_t o = 0;
     q.off_Xr = o; o += up256(Td * 4);
@@ -191,9 +204,31 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
     return hipSuccess;
 }
 
+static hipError_t run_seq(const Plan& P, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
+                          hipStream_t s, StageTimer* T) {
+    SeqArgs a{};
+    a.x = x;
+    a.y = y;
+    a.lens = lens;
+    a.B = P.B;
+    a.L = P.L;
+    a.F = P.f;
+    a.n_layers = P.n_layers;
+    a.eps = P.eps;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+    for (int l = 0; l < P.n_layers; l++) {
+        const tfl_layer& w = layers[l];
+        a.lw[l] = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b,
+                            w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
+    }
+    Timed tm(T, TFL_STAGE_FUSED, s);
+    return tm.done(launch_seq(P.mode, P.d, P.dh, a, s));
+}
+
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,
                     hipStream_t s, StageTimer* timer) {
     switch (p.path) {
+        case TFL_PATH_SEQ: return run_seq(p, layers, x, lens, y, s, timer);
         case TFL_PATH_TILED: return run_tiled(p, layers, x, lens, y, ws, s, timer);
     }
     return hipErrorInvalidValue;

@@ -176,23 +176,25 @@ def test_gpu_batch_independence_and_determinism():
 # ---------------------------------------------------------------- error statuses through the ABI
 
 
-def test_forward_error_statuses(monkeypatch):
+@pytest.mark.parametrize("path", ["tiled", "seq"])
+def test_forward_error_statuses(monkeypatch, path):
     import torch
 
     import masked_attention_causal_amd as tfl
     w = W("err", 1, 64, 2, 64, 2, 16, "f16", 1, 16, 1.0)
     inp = _case(w, 0)
     layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
-    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers)
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=path)
     x = tfl.to_device(inp.x, w.dtype)
     lens = torch.from_numpy(inp.lens).cuda()
     y = torch.empty_like(x)
     h = enc.handle
     ws = enc.workspace()
     st = torch.cuda.current_stream().cuda_stream
-    with pytest.raises(tfl.TflError) as e:
-        h.forward_raw(x.data_ptr(), lens.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes - 1, st)
-    assert e.value.status == 3
+    if h.workspace_bytes > 0:
+        with pytest.raises(tfl.TflError) as e:
+            h.forward_raw(x.data_ptr(), lens.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes - 1, st)
+        assert e.value.status == 3
     with pytest.raises(tfl.TflError) as e:
         h.forward_raw(x.data_ptr(), lens.data_ptr(), x.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
     assert e.value.status == 1
@@ -213,3 +215,52 @@ def test_forward_error_statuses(monkeypatch):
     clamped = synth.make_inputs(w, 0, lens=np.array([1, 16], np.int32))
     assert_gate(tfl.to_numpy_f64(y), oracle_forward(clamped), "clamped lengths")
     enc.close()
+
+
+# ---------------------------------------------------------------- every path that supports a shape
+
+PATH_SHAPES = [
+    W("p_f16_d256_dh64", 2, 256, 4, 512, 5, 64, "f16", 8, 64, 1.0),
+    W("p_bf16_d256_dh64", 2, 256, 4, 256, 3, 64, "bf16", 1, 64, 1.0),
+    W("p_f16_d128_dh32", 3, 128, 4, 192, 4, 50, "f16", 1, 50, 1.0),
+    W("p_bf16_d128_dh64", 2, 128, 2, 128, 2, 37, "bf16", 1, 37, 1.0),
+    W("p_f16_d64_dh64", 2, 64, 1, 64, 3, 64, "f16", 1, 64, 1.0),
+    W("p_f16_d64_dh32", 1, 64, 2, 128, 1, 17, "f16", 1, 17, 1.0),
+    W("p_f16_d256_dh32", 2, 256, 8, 256, 2, 64, "f16", 1, 64, 1.0),
+]
+
+
+@pytest.mark.parametrize("w", PATH_SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("path", ["seq", "tiled"])
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+def test_forced_paths(w, path, scale):
+    import masked_attention_causal_amd as tfl
+    plan, got, _ = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path=path)
+    assert got == path
+    for seed in (0, 1):
+        inp = _case(w, seed, scale, affine=(seed == 1))
+        inp.lens[0] = w.L
+        say(f"[path] {w.name} path={path} plan={plan} seed={seed} scale={scale} lens={inp.lens.tolist()}")
+        assert_gate(gpu_forward(inp, force_path=path), oracle_forward(inp), f"{w.name} {path} seed {seed}")
+
+
+def test_seq_invariances_bit_exact():
+    w = W("inv_seq", 2, 256, 4, 512, 4, 64, "f16", 1, 64, 1.0)
+    inp = _case(w, 9, lens=np.array([64, 40, 3, 64], np.int32))
+    y = gpu_forward(inp, force_path="seq")
+    p = synth.make_inputs(w, 9, lens=inp.lens)
+    p.x = inp.x.copy()
+    p.x[1, 50] = synth.round_to(synth.to_f64(p.x[1, 50], "f16") + 1.0, "f16")    # padding position
+    p.x[0, 20] = synth.round_to(synth.to_f64(p.x[0, 20], "f16") - 1.0, "f16")    # causal position
+    say("[seq invariance] perturbed padding and causal positions")
+    y2 = gpu_forward(p, force_path="seq")
+    assert np.array_equal(y[0, :20], y2[0, :20])
+    assert not np.array_equal(y[0, 20:], y2[0, 20:])
+    keep = np.ones(64, bool)
+    keep[50] = False
+    assert np.array_equal(y[1, keep], y2[1, keep])
+    assert np.array_equal(y[2:], y2[2:])
+    say("[seq determinism]")
+    assert np.array_equal(y, gpu_forward(inp, force_path="seq"))
+    for b in range(w.B):
+        assert np.array_equal(gpu_forward(synth.subset(inp, [b]), force_path="seq")[0], y[b])
