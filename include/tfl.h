@@ -82,8 +82,8 @@ typedef struct {
 
 /* One layer's parameters: device pointers in the I/O dtype, row-major,
  * nn.Linear layout ([out, in]).  w_qkv rows are q | k | v and head h owns
- * rows h*dh .. h*dh+dh-1 of each third.  Matrices must be 16-byte aligned,
- * vectors aligned to their element size. */
+ * rows h*dh .. h*dh+dh-1 of each third.  Every pointer, matrices and
+ * vectors alike, must be 16-byte aligned. */
 typedef struct {
     const void *w_qkv, *b_qkv; /* [3d, d], [3d] */
     const void *w_o, *b_o;     /* [d, d],  [d]  */

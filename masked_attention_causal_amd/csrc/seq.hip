@@ -2,29 +2,39 @@
 //
 // "Hyper-optimized megakernel-hybrid transformer inference", "Problem
 // decomposition": when sequences are short, a workgroup owns whole
-// sequences and keeps them on chip for every layer.  Here a workgroup of
-// 8 waves owns two sequences of up to 64 tokens; wave w owns 16 tokens
-// (sequence w/4, positions 16*(w%4) ..).  Each wave keeps the fp32
-// residual rows of its tokens in registers for the whole stack, in the MFMA
-// result layout of the transposed products below, so LayerNorm, the
-// residual adds and the fp16 operand copies never leave the wave.
+// sequences and keeps them on chip for every layer.  Here a workgroup of 8
+// waves (two per SIMD) owns two sequences of up to 64 tokens; wave w owns
+// the 16 tokens 16*(w%4) .. of sequence w/4 as one column block (the code
+// is written for TPW column blocks per wave).  Each wave keeps
+// the fp32 residual rows of its tokens in registers for the whole stack,
+// in the MFMA result layout of the transposed products below, so
+// LayerNorm, the residual adds and the fp16 operand copies never leave the
+// wave.
 //
-// Every projection is computed transposed, OUT^T = W ACT^T, with the
-// weights as the A operand (staged through LDS once per workgroup and read
-// by all eight waves) and the activations as the B operand straight from
-// registers.  A 16x16 MFMA result block leaves lane (g, c) with rows
-// 4g..4g+3 of column c; two adjacent blocks therefore give that lane rows
-// {4g..4g+3} and {16+4g..16+4g+3} of one 32-row chunk, which is a valid B
-// operand of a 16x16x32 MFMA once the A operand reads its K columns in the
-// same order.  The chain of GEMMs thus passes activations register to
-// register.
+// Every projection is computed transposed, OUT^T = W ACT^T: the weights are
+// the A operand, staged through LDS once per workgroup and read as one
+// 16-byte fragment that feeds one MFMA per token block; the
+// activations are the B operand, straight from registers.  A 16x16 MFMA
+// result block leaves lane (g, c) with rows 4g..4g+3 of column c, so two
+// adjacent blocks give the lane rows {4g..4g+3, 16+4g..16+4g+3} of a
+// 32-row chunk.  Weight tiles are gathered into LDS with their rows
+// permuted within every group of 32 (LDS row 16h + 4g + e holds weight row
+// 8g + 4h + e), so those result rows are the natural features 8g..8g+7:
+// exactly the K slice a lane holds in a 16x16x32 B operand, and the next
+// product's fragment is the natural 16 bytes at column 8g.  Activations
+// thus pass from one product to the next register to register.
 //
 // Attention (keys j <= i and j < len_b, "KernelForge", "What we built") is
-// computed per head: K and V^T of both sequences go to LDS, each wave
-// forms S^T = K Q^T for its 16 queries over at most 64 keys, a plain (not
-// online) softmax over the row, and O^T = V^T P^T, which is again a B
-// operand for the out-projection.  Key chunks past the wave's last query
-// or past len_b are skipped.
+// computed per head: K and V^T of both sequences go to LDS, each wave forms
+// S^T = K Q^T for its queries over at most 64 keys, a plain (not online)
+// softmax over the row, and O^T = V^T P^T, which is again a B operand of
+// the out-projection.  Key chunks past the wave's last query or past len_b
+// are skipped.
+//
+// Weight tiles (fp16) and the per-layer bias / LayerNorm vectors stream
+// from global memory straight into LDS with 16-byte global_load_lds, one
+// tile ahead of the MFMAs; bf16 weight tiles go through registers to be
+// widened to fp16.
 //
 // Precision matches the tiled path: fp32 residual and LayerNorm, fp16
 // operands with fp32 accumulation, first-layer scores from a hi/lo fp16
@@ -36,10 +46,13 @@ namespace tfl {
 
 namespace {
 
-constexpr int SEQ_THREADS = 512;
-constexpr int SEQ_SLOT = 64;   // tokens per sequence slot
-constexpr int SEQ_SEQS = 2;    // sequences per workgroup
+constexpr int SEQ_THREADS = 512;  // 8 waves, two per SIMD
+constexpr int SEQ_SLOT = 64;      // tokens per sequence slot
+constexpr int SEQ_SEQS = 2;       // sequences per workgroup
 constexpr int SEQ_TOK = SEQ_SLOT * SEQ_SEQS;
+constexpr int TPW = 1;            // 16-token column blocks per wave
+constexpr int SEQ_WPS = SEQ_SLOT / (16 * TPW);  // waves per sequence slot
+constexpr int SEQ_MAX_F = 4096;   // largest FFN width of the SEQ path
 constexpr int FCH = 64;        // FFN width per chunk
 
 struct TileDesc {
@@ -51,22 +64,66 @@ __device__ __forceinline__ f16x8 pack8(f32x4 a, f32x4 b) {
     return f16x8{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3], (f16)b[0], (f16)b[1], (f16)b[2], (f16)b[3]};
 }
 
-// LDS tiles that feed the A operand store each 32-column chunk permuted so
-// that the K order {4g..4g+3, 16+4g..16+4g+3} a lane needs is 8 contiguous
-// halves at offset 8g: column c of a chunk goes to position
-// 8*((c/4)%4) + 4*(c/16) + c%4.
-__device__ __forceinline__ int perm_pos(int c) { return 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3); }
+// Row permutation applied within every 32-row group of a staged tile: LDS
+// row 16h + 4g + e holds source row 8g + 4h + e.
+__device__ __forceinline__ int sigma32(int r) { return 8 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3); }
 
+// Natural feature held by element e of result block `blk` in lane group g
+// (after the sigma32 row gather): 4 consecutive features per block.
+__device__ __forceinline__ int feat4(int blk, int g) { return (blk >> 1) * 32 + 8 * g + 4 * (blk & 1); }
+
+// A operand fragment: 8 consecutive halves of LDS row `row` at column col0 + 8g.
 __device__ __forceinline__ f16x8 afrag(const f16* buf, int ldw, int row, int col0, int g) {
     return *(const f16x8*)(buf + row * ldw + col0 + 8 * g);
 }
 
-#define TFL_FENCE()
+// Four consecutive stored values as fp32.
+template <class T>
+__device__ __forceinline__ f32x4 load4(const T* q) {
+    const uint2 r = *(const uint2*)q;
+    if constexpr (std::is_same<T, f16>::value) {
+        const f16x4 h = *(const f16x4*)&r;
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    } else {
+        return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                     __uint_as_float(r.y & 0xFFFF0000u)};
+    }
+}
+
+typedef __attribute__((address_space(3))) f16 lds_f16;
+
+// 16-byte LDS-DMA: lane i of the wave writes its 16 source bytes to
+// lds_wave_base + 16 i.  Issued through asm so the compiler does not make
+// every later LDS read wait for it; the caller waits (vmcnt) before the
+// barrier that publishes the data.  M0 has no other user in this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, f16* lds_wave_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_f16*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Scheduling order for a fully unrolled product of NM MFMAs fed by NDS LDS
+// reads, MPR MFMAs per read: AHEAD reads are issued first, then MPR MFMAs
+// and one read alternate, so every fragment is in flight well before use.
+template <int NDS, int NM, int MPR, int AHEAD>
+__device__ __forceinline__ void pipeline_order() {
+#pragma unroll
+    for (int i = 0; i < AHEAD; i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NM / MPR; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+        if (AHEAD + i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
+constexpr int SEQ_AHEAD = 8;
 
 }  // namespace
 
 template <class WT, int D, int DH>
 __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
+    constexpr bool DIRECT = std::is_same<WT, f16>::value;  // fp16 weights: global -> LDS directly
     constexpr int H = D / DH;
     constexpr int NDB = D / 16;   // residual blocks per token column
     constexpr int NKC = D / 32;   // 32-wide K chunks over d_model
@@ -75,17 +132,17 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     constexpr int NCB = NQB > FCH / 16 ? NQB : FCH / 16;  // carried blocks (Q of a head, or a GELU chunk)
     constexpr int KLD = DH + 8;               // K rows in LDS
     constexpr int VLD = SEQ_TOK + 8;          // V^T rows in LDS
-    // staged weight tiles (halves; every row padded by 8):
-    //   Q/K/V rows of one head: DH x D      W_o columns of one head: D x DH
-    //   W_1 rows of one chunk:  FCH x D     W_2 columns of one chunk: D x FCH
+    // Staged weight tiles, rows padded by 8 halves and sigma32-gathered:
+    //   kinds 0-2: Q/K/V rows of one head, DH x D;  3: W_o columns of one head, D x DH;
+    //   4: W_1 rows of one chunk, FCH x D;          5: W_2 columns of one chunk, D x FCH.
     constexpr int T1 = DH * (D + 8) > D * (DH + 8) ? DH * (D + 8) : D * (DH + 8);
     constexpr int T2 = FCH * (D + 8) > D * (FCH + 8) ? FCH * (D + 8) : D * (FCH + 8);
     constexpr int TBUF = T1 > T2 ? T1 : T2;
-    constexpr int EMAX = (DH > FCH ? DH : FCH) * D;  // elements of the largest tile
-    constexpr int MAXCH = (EMAX / 8 + SEQ_THREADS - 1) / SEQ_THREADS;
+    constexpr int MAXCH = (TBUF / 8 + SEQ_THREADS - 1) / SEQ_THREADS;  // 16-byte chunks per thread
     static_assert(D % 32 == 0 && DH % 32 == 0 && D % DH == 0, "unsupported SEQ shape");
 
-    __shared__ __attribute__((aligned(16))) f16 Wb[2][TBUF];
+    __shared__ __attribute__((aligned(16))) f16 Wb0[TBUF];
+    __shared__ __attribute__((aligned(16))) f16 Wb1[TBUF];
     __shared__ __attribute__((aligned(16))) f16 Kh[SEQ_TOK * KLD];
     __shared__ __attribute__((aligned(16))) f16 Kl[SEQ_TOK * KLD];
     __shared__ __attribute__((aligned(16))) f16 Vt[DH * VLD];
@@ -93,15 +150,28 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     // parity: b_qkv | b_o | ln1_g | ln1_b | b_1 | b_2 | ln2_g | ln2_b.
     constexpr int P_BQKV = 0, P_BO = 3 * D, P_G1 = 4 * D, P_BE1 = 5 * D, P_B1 = 6 * D;
     extern __shared__ __attribute__((aligned(16))) uint16_t seq_dyn_lds[];
-    WT* const Pm = (WT*)seq_dyn_lds;  // 2 * (9 D + F) elements
+    WT* const Pm = (WT*)seq_dyn_lds;  // 2 * PLENP elements
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c16 = lane & 15, g = lane >> 4;
-    const int sq = wave >> 2, tb = wave & 3;
+    // Lane coordinates are re-derived from an opaque copy of the thread id
+    // at every step (refresh_lane below), so per-lane addresses are
+    // recomputed where they are used instead of being hoisted out of the
+    // tile loop and pinned in registers for the whole kernel.
+    int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int c16 = lane & 15, g = lane >> 4;
+    const int wave0 = threadIdx.x >> 6;
+    const int sq = wave0 / SEQ_WPS;              // sequence slot of this wave
+    const int q0 = (wave0 % SEQ_WPS) * 16 * TPW; // first position of this wave's tokens
     const int b = blockIdx.x * SEQ_SEQS + sq;
+    auto refresh_lane = [&]() {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        tid = t;
+        lane = t & 63;
+        wave = t >> 6;
+        c16 = lane & 15;
+        g = lane >> 4;
+    };
     const int L = p.L;
-    const int pos = tb * 16 + c16;              // this lane's token column
-    const bool live = b < p.B && pos < L;
     int len = b < p.B ? p.lens[b] : 1;
     len = len < 1 ? 1 : (len > L ? L : len);
     const int F = p.F;
@@ -109,22 +179,27 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     const int per_layer = 4 * H + 2 * NF;
     const int ntiles = per_layer * p.n_layers;
     const int PLEN = 9 * D + F;
+    const int PLENP = (PLEN + 7) & ~7;          // 16-byte aligned parity buffers
     const int P_B2 = 6 * D + F, P_G2 = 7 * D + F, P_BE2 = 8 * D + F;
-    auto load_params = [&](int layer) {
+
+    // Per-layer vectors: 16-byte chunk c of the concatenation (every vector
+    // is 16-byte aligned and a multiple of 8 long), fetched straight into LDS.
+    auto param_src = [&](const LayerPtrs& w, int j) -> const WT* {
+        if (j < 3 * D) return (const WT*)w.b_qkv + j;
+        if ((j -= 3 * D) < D) return (const WT*)w.b_o + j;
+        if ((j -= D) < D) return (const WT*)w.ln1_g + j;
+        if ((j -= D) < D) return (const WT*)w.ln1_b + j;
+        if ((j -= D) < F) return (const WT*)w.b_1 + j;
+        if ((j -= F) < D) return (const WT*)w.b_2 + j;
+        if ((j -= D) < D) return (const WT*)w.ln2_g + j;
+        return (const WT*)w.ln2_b + (j - D);
+    };
+    auto param_fetch = [&](int layer) {
         const LayerPtrs& w = p.lw[layer];
-        WT* dst = Pm + (layer & 1) * PLEN;
-        for (int i = tid; i < PLEN; i += SEQ_THREADS) {
-            const WT* src;
-            int j = i;
-            if (j < 3 * D) src = (const WT*)w.b_qkv + j;
-            else if ((j -= 3 * D) < D) src = (const WT*)w.b_o + j;
-            else if ((j -= D) < D) src = (const WT*)w.ln1_g + j;
-            else if ((j -= D) < D) src = (const WT*)w.ln1_b + j;
-            else if ((j -= D) < F) src = (const WT*)w.b_1 + j;
-            else if ((j -= F) < D) src = (const WT*)w.b_2 + j;
-            else if ((j -= D) < D) src = (const WT*)w.ln2_g + j;
-            else src = (const WT*)w.ln2_b + (j - D);
-            dst[i] = *src;
+        WT* dst = Pm + (layer & 1) * PLENP;
+        for (int i = 0; i * SEQ_THREADS * 8 < PLEN; i++) {
+            const int c = i * SEQ_THREADS + tid;
+            if (c * 8 < PLEN) dma16(param_src(w, c * 8), (f16*)(dst + (i * SEQ_THREADS + wave * 64) * 8));
         }
     };
 
@@ -145,321 +220,401 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
         }
         return d;
     };
-    // rows, columns and the source of row r of a tile
-    auto tile_geom = [&](const TileDesc& d, int* rows, int* cols) {
-        if (d.kind <= 2) { *rows = DH; *cols = D; }
-        else if (d.kind == 3) { *rows = D; *cols = DH; }
-        else if (d.kind == 4) { *rows = FCH; *cols = D; }
-        else { *rows = D; *cols = FCH; }
+    // Row r of a tile starts at base + r * rstride (elements); cols elements per row.
+    struct Geom {
+        const WT* base;
+        long rstride;
+        int rows, cols;
     };
-    auto tile_row = [&](const TileDesc& d, int r) -> const WT* {
+    auto geom = [&](const TileDesc& d) {
         const LayerPtrs& w = p.lw[d.layer];
-        switch (d.kind) {
-            case 0: case 1: case 2: return (const WT*)w.w_qkv + (size_t)(d.kind * D + d.h * DH + r) * D;
-            case 3: return (const WT*)w.w_o + (size_t)r * D + d.h * DH;
-            case 4: return (const WT*)w.w_1 + (size_t)(d.fc * FCH + r) * D;
-            default: return (const WT*)w.w_2 + (size_t)r * F + d.fc * FCH;
+        Geom q;
+        if (d.kind <= 2) {
+            q.base = (const WT*)w.w_qkv + (size_t)(d.kind * D + d.h * DH) * D;
+            q.rstride = D; q.rows = DH; q.cols = D;
+        } else if (d.kind == 3) {
+            q.base = (const WT*)w.w_o + d.h * DH;
+            q.rstride = D; q.rows = D; q.cols = DH;
+        } else if (d.kind == 4) {
+            q.base = (const WT*)w.w_1 + (size_t)d.fc * FCH * D;
+            q.rstride = D; q.rows = FCH; q.cols = D;
+        } else {
+            q.base = (const WT*)w.w_2 + d.fc * FCH;
+            q.rstride = F; q.rows = D; q.cols = FCH;
         }
+        return q;
     };
 
-    uint4 stg[MAXCH];
-    auto tile_load = [&](int t) {
-        const TileDesc d = describe(t);
-        int rows, cols;
-        tile_geom(d, &rows, &cols);
-        const int cpr = cols / 8, n = rows * cpr;
+    // Every 16-byte chunk of the padded, row-gathered LDS image of a tile;
+    // pad chunks re-read the row's first chunk.
+    uint4 stg[DIRECT ? 1 : MAXCH];
+    auto tile_fetch = [&](int t, f16* buf) {
+        const Geom q = geom(describe(t));
+        const int cpr = q.cols / 8, cpp = cpr + 1, n = q.rows * cpp;
 #pragma unroll
         for (int i = 0; i < MAXCH; i++) {
             const int c = tid + i * SEQ_THREADS;
             if (c < n) {
-                const int r = c / cpr, cc = (c - r * cpr) * 8;
-                stg[i] = *(const uint4*)(tile_row(d, r) + cc);
-            }
-        }
-    };
-    auto tile_store = [&](int t, f16* buf) {
-        const TileDesc d = describe(t);
-        int rows, cols;
-        tile_geom(d, &rows, &cols);
-        const int cpr = cols / 8, n = rows * cpr, ldw = cols + 8;
-#pragma unroll
-        for (int i = 0; i < MAXCH; i++) {
-            const int c = tid + i * SEQ_THREADS;
-            if (c < n) {
-                const int r = c / cpr, cc = (c - r * cpr) * 8;
-                f16x8 v;
-                if constexpr (!std::is_same<WT, f16>::value) {
-                    v = load8_as_f16((const WT*)&stg[i]);
+                const int r = c / cpp, k8 = c - r * cpp;
+                const int gr = (r & ~31) + sigma32(r & 31);
+                const WT* src = q.base + gr * q.rstride + (k8 < cpr ? k8 : 0) * 8;
+                if constexpr (DIRECT) {
+                    dma16(src, buf + (i * SEQ_THREADS + wave * 64) * 8);
                 } else {
-                    v = *(const f16x8*)&stg[i];
+                    stg[i] = *(const uint4*)src;
                 }
-                // columns cc..cc+3 and cc+4..cc+7 land at two permuted 4-half slots
-                const int base = r * ldw + (cc & ~31), c0 = cc & 31;
-                *(f16x4*)&buf[base + perm_pos(c0)] = f16x4{v[0], v[1], v[2], v[3]};
-                *(f16x4*)&buf[base + perm_pos(c0 + 4)] = f16x4{v[4], v[5], v[6], v[7]};
             }
         }
     };
+    auto tile_commit = [&](int t, f16* buf) {
+        if constexpr (!DIRECT) {
+            const Geom q = geom(describe(t));
+            const int cpp = q.cols / 8 + 1, n = q.rows * cpp;
+#pragma unroll
+            for (int i = 0; i < MAXCH; i++) {
+                const int c = tid + i * SEQ_THREADS;
+                if (c < n) *(f16x8*)&buf[c * 8] = load8_as_f16((const WT*)&stg[i]);
+            }
+        }
+        // direct loads of the tile and of the vectors land before the barrier
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
 
-    // ---- registers: residual X^T (fp32) and its fp16 B-operand copy
-    f32x4 R[NDB];
-    f16x8 XB[NKC];
-    {
-        const WT* x = (const WT*)p.x;
+    // ---- registers: residual X^T (fp32) and its fp16 B-operand copy, per token block
+    f32x4 R[NDB][TPW];
+    f16x8 XB[NKC][TPW];
+#pragma unroll
+    for (int tb = 0; tb < TPW; tb++) {
+        const int pos = q0 + tb * 16 + c16;
+        const bool live = b < p.B && pos < L;
+        const WT* x = (const WT*)p.x + ((size_t)(live ? b : 0) * L + (live ? pos : 0)) * D;
 #pragma unroll
         for (int db = 0; db < NDB; db++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                R[db][e] = live ? to_f32(x[((size_t)b * L + pos) * D + db * 16 + 4 * g + e]) : 0.f;
+            const f32x4 v = load4(x + feat4(db, g));
+            R[db][tb] = live ? v : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int kk = 0; kk < NKC; kk++) XB[kk] = pack8(R[2 * kk], R[2 * kk + 1]);
+        for (int kk = 0; kk < NKC; kk++) XB[kk][tb] = pack8(R[2 * kk][tb], R[2 * kk + 1][tb]);
     }
     // Q^T of the current head (from its tile until attention) or the GELU
     // output of the current FFN chunk (from W_1 to W_2).
-    f32x4 carry[NCB];
+    f32x4 carry[NCB][TPW];
 
     auto layer_norm = [&](const WT* gam, const WT* bet) {  // LDS pointers
-        float s = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; db++) s += (R[db][0] + R[db][1]) + (R[db][2] + R[db][3]);
-        s += __shfl_xor(s, 16, WAVE);
-        s += __shfl_xor(s, 32, WAVE);
-        const float mean = s / (float)D;
-        float q = 0.f;
+        for (int tb = 0; tb < TPW; tb++) {
+            float s = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; db++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                R[db][e] -= mean;
-                q += R[db][e] * R[db][e];
-            }
-        }
-        q += __shfl_xor(q, 16, WAVE);
-        q += __shfl_xor(q, 32, WAVE);
-        const float rstd = 1.0f / sqrtf(q / (float)D + p.eps);
-#pragma unroll
-        for (int db = 0; db < NDB; db++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int col = db * 16 + 4 * g + e;
-                R[db][e] = R[db][e] * rstd * to_f32(gam[col]) + to_f32(bet[col]);
-            }
-            if ((db & 3) == 3) TFL_FENCE();
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKC; kk++) XB[kk] = pack8(R[2 * kk], R[2 * kk + 1]);
-    };
-
-    load_params(0);
-    tile_load(0);
-    tile_store(0, Wb[0]);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; t++) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) tile_load(t + 1);
-        const f16* W = Wb[buf];
-        const TileDesc d = describe(t);
-        const WT* P = Pm + (d.layer & 1) * PLEN;
-        const bool split = d.layer == 0;
-        // next layer's vectors go to the other parity buffer, visible after this step's barrier
-        if (t - d.layer * per_layer == 0 && d.layer + 1 < p.n_layers) load_params(d.layer + 1);
-
-        if (d.kind <= 2) {
-            // ---- Q^T, K^T or V^T of head h: [DH x 16 tokens] = W rows . X^T
-            constexpr int ldw = D + 8;
-            f32x4 acc[NQB];
-#pragma unroll
-            for (int ob = 0; ob < NQB; ob++) acc[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < NKC; kk++) {
-#pragma unroll
-                for (int ob = 0; ob < NQB; ob++) acc[ob] = mfma_16x16x32(afrag(W, ldw, ob * 16 + c16, kk * 32, g), XB[kk], acc[ob]);
-                TFL_FENCE();
-            }
-            const WT* bq = P + P_BQKV + d.kind * D + d.h * DH;
-#pragma unroll
-            for (int ob = 0; ob < NQB; ob++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) acc[ob][e] += to_f32(bq[ob * 16 + 4 * g + e]);
-            const int tok = sq * SEQ_SLOT + pos;
-            if (d.kind == 0) {
-#pragma unroll
-                for (int ob = 0; ob < NQB; ob++) carry[ob] = acc[ob];
-            } else if (d.kind == 1) {
-#pragma unroll
-                for (int kb = 0; kb < NQB; kb++) {
-                    f16x4 hv, lv;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        hv[e] = (f16)acc[kb][e];
-                        lv[e] = (f16)(acc[kb][e] - (float)hv[e]);
-                    }
-                    // head-dim column kb*16 + 4g + e, stored permuted within its 32-chunk
-                    const int col = (kb >> 1) * 32 + perm_pos((kb & 1) * 16 + 4 * g);
-                    *(f16x4*)&Kh[tok * KLD + col] = hv;
-                    if (split) *(f16x4*)&Kl[tok * KLD + col] = lv;
-                }
-            } else {
-#pragma unroll
-                for (int vb = 0; vb < NQB; vb++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) Vt[(vb * 16 + 4 * g + e) * VLD + tok] = (f16)acc[vb][e];
-            }
-        } else if (d.kind == 3) {
-            // ---- attention of head h for this wave's 16 queries
-            const int kbase = sq * SEQ_SLOT;
-            const int kmax = min(tb * 16 + 16, len);
-            const int nch = (kmax + 31) >> 5;  // 32-key chunks that matter (1 or 2)
-            f16x8 qh[NHC], ql[NHC];
-#pragma unroll
-            for (int kk = 0; kk < NHC; kk++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float a = carry[2 * kk][e], c = carry[2 * kk + 1][e];
-                    const f16 ah = (f16)a, ch = (f16)c;
-                    qh[kk][e] = ah;
-                    qh[kk][4 + e] = ch;
-                    ql[kk][e] = (f16)(a - (float)ah);
-                    ql[kk][4 + e] = (f16)(c - (float)ch);
-                }
-            }
-            f32x4 s[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if ((kb >> 1) < nch) {
-                    const int krow = kbase + (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
-#pragma unroll
-                    for (int kk = 0; kk < NHC; kk++) {
-                        const f16x8 a = afrag(Kh, KLD, krow, kk * 32, g);
-                        s[kb] = mfma_16x16x32(a, qh[kk], s[kb]);
-                        if (split) {
-                            s[kb] = mfma_16x16x32(afrag(Kl, KLD, krow, kk * 32, g), qh[kk], s[kb]);
-                            s[kb] = mfma_16x16x32(a, ql[kk], s[kb]);
-                        }
-                    }
-                }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int key = (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
-                    float v = s[kb][e] * p.scale_log2;
-                    if (key > pos || key >= len) v = -INFINITY;
-                    s[kb][e] = v;
-                    mx = fmaxf(mx, v);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-            float l = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float pv = exp2f(s[kb][e] - mx);
-                    s[kb][e] = pv;
-                    l += pv;
-                }
-            }
-            l += __shfl_xor(l, 16, WAVE);
-            l += __shfl_xor(l, 32, WAVE);
-            f32x4 o[NQB];
-#pragma unroll
-            for (int db = 0; db < NQB; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int cc = 0; cc < 2; cc++) {
-                if (cc < nch) {
-                    const f16x8 pb = pack8(s[2 * cc], s[2 * cc + 1]);
-#pragma unroll
-                    for (int db = 0; db < NQB; db++) {
-                        const f16x8 va = *(const f16x8*)&Vt[(db * 16 + c16) * VLD + kbase + cc * 32 + 8 * g];
-                        o[db] = mfma_16x16x32(va, pb, o[db]);
-                    }
-                }
-            }
-            const float inv = 1.0f / l;
-            f16x8 OB[NHC];
-#pragma unroll
-            for (int kk = 0; kk < NHC; kk++) OB[kk] = pack8(o[2 * kk] * inv, o[2 * kk + 1] * inv);
-
-            // ---- out-projection of head h accumulated into the residual
-            if (d.h == 0) {
-                const WT* bo = P + P_BO;
-#pragma unroll
-                for (int db = 0; db < NDB; db++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) R[db][e] += to_f32(bo[db * 16 + 4 * g + e]);
-            }
-            constexpr int ldw = DH + 8;
+            for (int db = 0; db < NDB; db++) s += (R[db][tb][0] + R[db][tb][1]) + (R[db][tb][2] + R[db][tb][3]);
+            s += __shfl_xor(s, 16, WAVE);
+            s += __shfl_xor(s, 32, WAVE);
+            const float mean = s / (float)D;
+            float q = 0.f;
 #pragma unroll
             for (int db = 0; db < NDB; db++) {
 #pragma unroll
-                for (int kk = 0; kk < NHC; kk++) R[db] = mfma_16x16x32(afrag(W, ldw, db * 16 + c16, kk * 32, g), OB[kk], R[db]);
-                if (db & 1) TFL_FENCE();
+                for (int e = 0; e < 4; e++) {
+                    R[db][tb][e] -= mean;
+                    q += R[db][tb][e] * R[db][tb][e];
+                }
             }
+            q += __shfl_xor(q, 16, WAVE);
+            q += __shfl_xor(q, 32, WAVE);
+            const float rstd = 1.0f / sqrtf(q / (float)D + p.eps);
+#pragma unroll
+            for (int db = 0; db < NDB; db++) {
+                const f32x4 ga = load4(gam + feat4(db, g)), be = load4(bet + feat4(db, g));
+#pragma unroll
+                for (int e = 0; e < 4; e++) R[db][tb][e] = R[db][tb][e] * rstd * ga[e] + be[e];
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKC; kk++) XB[kk][tb] = pack8(R[2 * kk][tb], R[2 * kk + 1][tb]);
+        }
+    };
+
+    auto step = [&](int t, const f16* W) {
+        const TileDesc d = describe(t);
+        const WT* P = Pm + (d.layer & 1) * PLENP;
+        const bool split = d.layer == 0;
+
+        if (d.kind <= 2) {
+            // ---- Q^T, K^T or V^T of head h: [DH x tokens] = W rows . X^T
+            constexpr int ldw = D + 8;
+            f32x4 acc[NQB][TPW];
+            const WT* bq = P + P_BQKV + d.kind * D + d.h * DH;
+#pragma unroll
+            for (int ob = 0; ob < NQB; ob++) {
+                const f32x4 bv = load4(bq + feat4(ob, g));
+#pragma unroll
+                for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = bv;
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKC; kk++)
+#pragma unroll
+                for (int ob = 0; ob < NQB; ob++) {
+                    const f16x8 a = afrag(W, ldw, ob * 16 + c16, kk * 32, g);
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = mfma_16x16x32(a, XB[kk][tb], acc[ob][tb]);
+                }
+            pipeline_order<NQB + NKC * NQB, NKC * NQB * TPW, TPW, SEQ_AHEAD>();
+            if (d.kind == 0) {
+#pragma unroll
+                for (int ob = 0; ob < NQB; ob++)
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) carry[ob][tb] = acc[ob][tb];
+            } else if (d.kind == 1) {
+#pragma unroll
+                for (int tb = 0; tb < TPW; tb++) {
+                    const int tok = sq * SEQ_SLOT + q0 + tb * 16 + c16;
+#pragma unroll
+                    for (int kb = 0; kb < NQB; kb++) {
+                        f16x4 hv, lv;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            hv[e] = (f16)acc[kb][tb][e];
+                            lv[e] = (f16)(acc[kb][tb][e] - (float)hv[e]);
+                        }
+                        *(f16x4*)&Kh[tok * KLD + feat4(kb, g)] = hv;
+                        if (split) *(f16x4*)&Kl[tok * KLD + feat4(kb, g)] = lv;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int tb = 0; tb < TPW; tb++) {
+                    const int tok = sq * SEQ_SLOT + q0 + tb * 16 + c16;
+#pragma unroll
+                    for (int vb = 0; vb < NQB; vb++)
+#pragma unroll
+                        for (int e = 0; e < 4; e++) Vt[(feat4(vb, g) + e) * VLD + tok] = (f16)acc[vb][tb][e];
+                }
+            }
+        } else if (d.kind == 3) {
+            // ---- attention of head h for this wave's queries
+            const int kbase = sq * SEQ_SLOT;
+            const int kmax = min(q0 + 16 * TPW, len);
+            const int nch = (kmax + 31) >> 5;  // 32-key chunks that matter (1 or 2)
+            f16x8 qh[NHC][TPW], ql[NHC][TPW];
+#pragma unroll
+            for (int tb = 0; tb < TPW; tb++)
+#pragma unroll
+                for (int kk = 0; kk < NHC; kk++) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float a = carry[2 * kk][tb][e], c = carry[2 * kk + 1][tb][e];
+                        const f16 ah = (f16)a, ch = (f16)c;
+                        qh[kk][tb][e] = ah;
+                        qh[kk][tb][4 + e] = ch;
+                        ql[kk][tb][e] = (f16)(a - (float)ah);
+                        ql[kk][tb][4 + e] = (f16)(c - (float)ch);
+                    }
+                }
+            // Two 32-key chunks, online softmax across them (running max and sum
+            // per query, live in the 4 lanes that share the query).
+            f32x4 o[NQB][TPW];
+            float mrun[TPW], lrun[TPW];
+#pragma unroll
+            for (int tb = 0; tb < TPW; tb++) {
+                mrun[tb] = -INFINITY;
+                lrun[tb] = 0.f;
+#pragma unroll
+                for (int db = 0; db < NQB; db++) o[db][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; cc++) {
+                if (cc < nch) {
+                    f32x4 s[2][TPW];
+#pragma unroll
+                    for (int hb = 0; hb < 2; hb++) {
+#pragma unroll
+                        for (int tb = 0; tb < TPW; tb++) s[hb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        const int krow = kbase + cc * 32 + sigma32(hb * 16 + c16);
+#pragma unroll
+                        for (int kk = 0; kk < NHC; kk++) {
+                            const f16x8 a = afrag(Kh, KLD, krow, kk * 32, g);
+#pragma unroll
+                            for (int tb = 0; tb < TPW; tb++) {
+                                s[hb][tb] = mfma_16x16x32(a, qh[kk][tb], s[hb][tb]);
+                                if (split) {
+                                    s[hb][tb] = mfma_16x16x32(afrag(Kl, KLD, krow, kk * 32, g), qh[kk][tb], s[hb][tb]);
+                                    s[hb][tb] = mfma_16x16x32(a, ql[kk][tb], s[hb][tb]);
+                                }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) {
+                        const int pos = q0 + tb * 16 + c16;
+                        float mx = -INFINITY;
+#pragma unroll
+                        for (int hb = 0; hb < 2; hb++) {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                const int key = cc * 32 + 8 * g + 4 * hb + e;
+                                float v = s[hb][tb][e] * p.scale_log2;
+                                if (key > pos || key >= len) v = -INFINITY;
+                                s[hb][tb][e] = v;
+                                mx = fmaxf(mx, v);
+                            }
+                        }
+                        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                        const float mnew = fmaxf(mrun[tb], mx);  // finite: key 0 is in chunk 0
+                        const float alpha = exp2f(mrun[tb] - mnew);
+                        mrun[tb] = mnew;
+                        float ls = 0.f;
+#pragma unroll
+                        for (int hb = 0; hb < 2; hb++) {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                const float pv = exp2f(s[hb][tb][e] - mnew);
+                                s[hb][tb][e] = pv;
+                                ls += pv;
+                            }
+                        }
+                        lrun[tb] = lrun[tb] * alpha + ls;
+#pragma unroll
+                        for (int db = 0; db < NQB; db++) o[db][tb] *= alpha;
+                    }
+#pragma unroll
+                    for (int db = 0; db < NQB; db++) {
+                        const int vrow = (db >> 1) * 32 + sigma32((db & 1) * 16 + c16);
+                        const f16x8 va = afrag(Vt, VLD, vrow, kbase + cc * 32, g);
+#pragma unroll
+                        for (int tb = 0; tb < TPW; tb++) o[db][tb] = mfma_16x16x32(va, pack8(s[0][tb], s[1][tb]), o[db][tb]);
+                    }
+                }
+            }
+            f16x8 OB[NHC][TPW];
+#pragma unroll
+            for (int tb = 0; tb < TPW; tb++) {
+                float l = lrun[tb];
+                l += __shfl_xor(l, 16, WAVE);
+                l += __shfl_xor(l, 32, WAVE);
+                const float inv = 1.0f / l;
+#pragma unroll
+                for (int kk = 0; kk < NHC; kk++) OB[kk][tb] = pack8(o[2 * kk][tb] * inv, o[2 * kk + 1][tb] * inv);
+            }
+
+            // ---- out-projection of head h accumulated into the residual
+            if (d.h == 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; db++) {
+                    const f32x4 bv = load4(P + P_BO + feat4(db, g));
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
+                }
+            }
+            constexpr int ldw = DH + 8;
+#pragma unroll
+            for (int db = 0; db < NDB; db++)
+#pragma unroll
+                for (int kk = 0; kk < NHC; kk++) {
+                    const f16x8 a = afrag(W, ldw, db * 16 + c16, kk * 32, g);
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) R[db][tb] = mfma_16x16x32(a, OB[kk][tb], R[db][tb]);
+                }
+            pipeline_order<NDB * NHC, NDB * NHC * TPW, TPW, SEQ_AHEAD>();
         } else if (d.kind == 4) {
             // ---- FFN up-projection chunk + GELU, carried to the next tile
             constexpr int ldw = D + 8;
 #pragma unroll
-            for (int ob = 0; ob < FCH / 16; ob++) carry[ob] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ob = 0; ob < FCH / 16; ob++) {
+                const f32x4 bv = load4(P + P_B1 + d.fc * FCH + feat4(ob, g));
 #pragma unroll
-            for (int kk = 0; kk < NKC; kk++) {
-#pragma unroll
-                for (int ob = 0; ob < FCH / 16; ob++) carry[ob] = mfma_16x16x32(afrag(W, ldw, ob * 16 + c16, kk * 32, g), XB[kk], carry[ob]);
-                TFL_FENCE();
+                for (int tb = 0; tb < TPW; tb++) carry[ob][tb] = bv;
             }
-            const WT* b1 = P + P_B1 + d.fc * FCH;
+#pragma unroll
+            for (int kk = 0; kk < NKC; kk++)
+#pragma unroll
+                for (int ob = 0; ob < FCH / 16; ob++) {
+                    const f16x8 a = afrag(W, ldw, ob * 16 + c16, kk * 32, g);
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) carry[ob][tb] = mfma_16x16x32(a, XB[kk][tb], carry[ob][tb]);
+                }
+            pipeline_order<FCH / 16 + NKC * FCH / 16, NKC * FCH / 16 * TPW, TPW, SEQ_AHEAD>();
 #pragma unroll
             for (int ob = 0; ob < FCH / 16; ob++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) carry[ob][e] = gelu_erf(carry[ob][e] + to_f32(b1[ob * 16 + 4 * g + e]));
+                for (int tb = 0; tb < TPW; tb++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) carry[ob][tb][e] = gelu_erf(carry[ob][tb][e]);
         } else {
             // ---- FFN down-projection chunk accumulated into the residual
             if (d.fc == 0) {
-                const WT* b2 = P + P_B2;
-#pragma unroll
-                for (int db = 0; db < NDB; db++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) R[db][e] += to_f32(b2[db * 16 + 4 * g + e]);
-            }
-            constexpr int ldw = FCH + 8;
-#pragma unroll
-            for (int kk = 0; kk < FCH / 32; kk++) {
-                const f16x8 gb = pack8(carry[2 * kk], carry[2 * kk + 1]);
 #pragma unroll
                 for (int db = 0; db < NDB; db++) {
-                    R[db] = mfma_16x16x32(afrag(W, ldw, db * 16 + c16, kk * 32, g), gb, R[db]);
-                    if ((db & 3) == 3) TFL_FENCE();
+                    const f32x4 bv = load4(P + P_B2 + feat4(db, g));
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
                 }
             }
+            constexpr int ldw = FCH + 8;
+            f16x8 gb[FCH / 32][TPW];
+#pragma unroll
+            for (int kk = 0; kk < FCH / 32; kk++)
+#pragma unroll
+                for (int tb = 0; tb < TPW; tb++) gb[kk][tb] = pack8(carry[2 * kk][tb], carry[2 * kk + 1][tb]);
+#pragma unroll
+            for (int db = 0; db < NDB; db++)
+#pragma unroll
+                for (int kk = 0; kk < FCH / 32; kk++) {
+                    const f16x8 a = afrag(W, ldw, db * 16 + c16, kk * 32, g);
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) R[db][tb] = mfma_16x16x32(a, gb[kk][tb], R[db][tb]);
+                }
+            pipeline_order<NDB * FCH / 32, NDB * FCH / 32 * TPW, TPW, SEQ_AHEAD>();
         }
-
         // LayerNorm after the last head (LN1) and after the last FFN chunk (LN2);
         // one call site keeps a single inlined copy.
         if ((d.kind == 3 && d.h == H - 1) || (d.kind == 5 && d.fc == NF - 1))
             layer_norm(P + (d.kind == 3 ? P_G1 : P_G2), P + (d.kind == 3 ? P_BE1 : P_BE2));
-        if (t + 1 < ntiles) tile_store(t + 1, Wb[buf ^ 1]);
+    };
+
+    param_fetch(0);
+    tile_fetch(0, Wb0);
+    tile_commit(0, Wb0);
+    __syncthreads();
+    // The next layer's vectors stream into the other parity buffer during the
+    // first step of a layer and land with that step's tile.
+    auto next_params = [&](int t) { return (t % per_layer) == 0 && t / per_layer + 1 < p.n_layers; };
+    // Two steps per iteration so each step's LDS buffers are fixed at compile
+    // time: tile t is read from one buffer while tile t + 1 streams into the other.
+    for (int t = 0; t < ntiles; t += 2) {
+        refresh_lane();
+        if (t + 1 < ntiles) tile_fetch(t + 1, Wb1);
+        if (next_params(t)) param_fetch(t / per_layer + 1);
+        step(t, Wb0);
+        if (t + 1 < ntiles) tile_commit(t + 1, Wb1);
+        __syncthreads();
+        if (t + 1 >= ntiles) break;
+        refresh_lane();
+        if (t + 2 < ntiles) tile_fetch(t + 2, Wb0);
+        if (next_params(t + 1)) param_fetch((t + 1) / per_layer + 1);
+        step(t + 1, Wb1);
+        if (t + 2 < ntiles) tile_commit(t + 2, Wb0);
         __syncthreads();
     }
 
     // ---- output rows
-    if (live) {
-        WT* y = (WT*)p.y;
 #pragma unroll
-        for (int db = 0; db < NDB; db++) {
+    for (int tb = 0; tb < TPW; tb++) {
+        const int pos = q0 + tb * 16 + c16;
+        if (b < p.B && pos < L) {
+            WT* y = (WT*)p.y + ((size_t)b * L + pos) * D;
 #pragma unroll
-            for (int e = 0; e < 4; e++) y[((size_t)b * L + pos) * D + db * 16 + 4 * g + e] = from_f32<WT>(R[db][e]);
+            for (int db = 0; db < NDB; db++) {
+                uint2 o;
+                WT* ov = (WT*)&o;
+#pragma unroll
+                for (int e = 0; e < 4; e++) ov[e] = from_f32<WT>(R[db][tb][e]);
+                *(uint2*)(y + feat4(db, g)) = o;
+            }
         }
     }
 }
 
 bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers) {
-    if (m == MODE_F32 || L > SEQ_SLOT || f % FCH != 0 || n_layers > SEQ_MAX_LAYERS) return false;
+    if (m == MODE_F32 || L > SEQ_SLOT || f % FCH != 0 || f > SEQ_MAX_F || n_layers > SEQ_MAX_LAYERS) return false;
     return (d == 256 && dh == 64) || (d == 256 && dh == 32) || (d == 128 && dh == 64) || (d == 128 && dh == 32) ||
            (d == 64 && dh == 64) || (d == 64 && dh == 32);
 }
@@ -467,7 +622,7 @@ bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers) {
 template <class WT>
 static hipError_t seq_mode(int d, int dh, const SeqArgs& a, hipStream_t s) {
     dim3 grid((a.B + SEQ_SEQS - 1) / SEQ_SEQS);
-    const size_t pbytes = 2 * (size_t)(9 * d + a.F) * sizeof(WT);
+    const size_t pbytes = 2 * (size_t)(((9 * d + a.F) + 7) & ~7) * sizeof(WT);
 #define TFL_SEQ_CASE(DD, HH)                                                                    \
     if (d == DD && dh == HH) {                                                                  \
         hipLaunchKernelGGL((seq_kernel<WT, DD, HH>), grid, dim3(SEQ_THREADS), pbytes, s, a);   \

@@ -48,7 +48,6 @@ tfl_status tfl_create(const tfl_config* cfg, const tfl_layer* layers, tfl_handle
     tfl::Plan plan;
     const tfl_status st = tfl::make_plan(*cfg, &plan, &why);
     if (st != TFL_OK) return fail(st, "tfl_create: " + why);
-    const size_t es = tfl::dtype_size(cfg->dtype);
     for (int l = 0; l < cfg->n_layers; l++) {
         const tfl_layer& w = layers[l];
         const void* mats[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
@@ -58,9 +57,9 @@ tfl_status tfl_create(const tfl_config* cfg, const tfl_layer* layers, tfl_handle
                 return fail(TFL_E_INVALID, "tfl_create: layer " + std::to_string(l) +
                                                ": weight matrix pointer null or not 16-byte aligned");
         for (const void* v : vecs)
-            if (!v || !aligned(v, es))
+            if (!v || !aligned(v, 16))
                 return fail(TFL_E_INVALID, "tfl_create: layer " + std::to_string(l) +
-                                               ": bias/LayerNorm pointer null or misaligned");
+                                               ": bias/LayerNorm pointer null or not 16-byte aligned");
     }
     tfl_handle* h = new (std::nothrow) tfl_handle;
     if (!h) return fail(TFL_E_INTERNAL, "tfl_create: out of host memory");

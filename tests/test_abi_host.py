@@ -81,7 +81,7 @@ def test_create_rejects(cfg, status):
 def test_create_rejects_bad_layer_pointers(lib):
     cfg = tfl.make_config(1, 64, 4, 128, 2, 16, "f16")
     good = {k: 0x10000 for k in tfl.LAYER_KEYS}
-    for key, val in (("w_qkv", 0), ("w_1", 0x10008), ("b_o", 0x10001), ("ln2_b", 0)):
+    for key, val in (("w_qkv", 0), ("w_1", 0x10008), ("b_o", 0x10001), ("ln1_g", 0x10002), ("ln2_b", 0)):
         bad = dict(good)
         bad[key] = val
         with pytest.raises(tfl.TflError) as e:
