@@ -72,6 +72,43 @@ def stage_work(w, stage, lens):
 
 STAGES_TILED = ("prep", "qkv", "attn", "out", "ln", "ffn1", "ffn2")
 
+# Kernel sources behind each stage: a traffic figure taken with rocprofv3 is
+# used only while these files are unchanged.
+STAGE_KERNEL = {"fused": ("seq_kernel", ("seq.hip", "common.h", "kernels.h")),
+                "attn": ("attn_kernel", ("attn.hip", "common.h", "kernels.h")),
+                "qkv": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
+                "out": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
+                "ffn1": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
+                "ffn2": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
+                "ln": ("ln_kernel", ("ln.hip", "common.h", "kernels.h")),
+                "prep": ("prep_kernel", ("ln.hip", "common.h", "kernels.h"))}
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch recorded in profiles/*.md for this kernel and
+    workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    kern, files = STAGE_KERNEL.get(stage, (None, ()))
+    if kern is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "masked_attention_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()
+    for md in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(md) as fh:
+            for line in fh:
+                if not line.startswith("machine-readable:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+                if (kv.get("kernel") == kern and kv.get("workload") == workload
+                        and kv.get("source_sha256") == digest and "traffic_bytes_per_launch" in kv):
+                    return int(kv["traffic_bytes_per_launch"])
+    return None
+
 
 def launches_per_forward(stage, n_layers):
     return {"prep": 1, "ln": 2 * n_layers, "fused": 1}.get(stage, n_layers)
@@ -201,6 +238,7 @@ def main():
     seqs = w.B / (ms_step / 1e3)
     roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1))
     roof["launches_timed"] = dom_n
+    roof["traffic"] = measured_traffic(dom, name)
 
     # whole-forward roofline figure for context
     tot_flops = 0.0
