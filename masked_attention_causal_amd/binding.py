@@ -52,6 +52,11 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is not built; run "
                            "`python -m masked_attention_causal_amd.build` (or __graft_entry__.build())")
+    # torch ships its own HIP runtime under the same soname as the system one.
+    # Importing torch first makes libtfl.so bind to the runtime torch uses;
+    # loaded the other way round, the process ends up with two runtimes and
+    # every launch fails with "no ROCm-capable device is detected".
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     L.tfl_create.argtypes = [ctypes.POINTER(TflConfig), ctypes.POINTER(TflLayer), ctypes.POINTER(vp)]

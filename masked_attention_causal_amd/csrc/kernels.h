@@ -60,6 +60,34 @@ struct SeqArgs {
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
+// Persistent task-queue path: whole stack in one launch, tasks popped from an
+// atomic queue in dependency order.  Counter block layout (int32):
+//   [0] queue head, [1] watchdog flag, [PQ_CTR_HDR ..) ready[n_layers][B*NT],
+//   then done[n_layers][B*NT].
+constexpr int PQ_CTR_HDR = 64;
+
+struct PqArgs {
+    const void* x;   // [B, L, d] I/O dtype
+    void* y;         // [B, L, d] I/O dtype
+    const int32_t* lens;
+    int B, L, Lp, NT, F, n_layers;
+    int KS;          // key tiles per attention split
+    int Ctot;        // (tile, split) pairs per (sequence, head)
+    int n_tasks;
+    float eps;
+    float scale_log2;
+    int* ctr;        // counter block (zeroed by the launcher each forward)
+    float* X;        // [B*L, d] fp32 residual stream between layers
+    _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 (hi part for layer 0)
+    _Float16* Kh;
+    _Float16* Ql;    // [B, H, L, dh] fp16 lo parts of layer 0
+    _Float16* Kl;
+    _Float16* Vt;    // [n_layers][B, H, dh, Lp] fp16
+    float* Op;       // [B*H*Ctot][64][dh] fp32 partial attention outputs
+    float2* ML;      // [B*H*Ctot][64] (running max in log2 units, sum)
+    LayerPtrs lw[SEQ_MAX_LAYERS];
+};
+
 // Fixed tile shapes shared with the planner.
 constexpr int ATT_KT = 64;   // keys per attention tile
 constexpr int ATT_BQ = 64;   // queries per attention workgroup
@@ -71,6 +99,10 @@ hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta
                      int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);
 
 hipError_t launch_seq(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
+bool pq_supported(Mode m, int d, int dh, int f, int n_layers);
+// single_launch: one persistent launch that resolves dependencies with
+// counters; otherwise one launch per stage (QKV0, then ATT and ROW per layer).
+hipError_t launch_pq(Mode m, int d, int dh, const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s);
 bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers);
 
 // Row layout of the LayerNorm kernel: lanes per row and float4 chunks per lane.

@@ -18,11 +18,21 @@ size_t dtype_size(int dtype) { return dtype == TFL_F32 ? 4 : 2; }
 
 static Mode mode_of(int dtype) { return dtype == TFL_F32 ? MODE_F32 : (dtype == TFL_F16 ? MODE_F16 : MODE_BF16); }
 
+// Compute units of the target part (MI355X); the rule below compares the
+// number of attention work units against it.
+constexpr long PQ_CU_COUNT = 256;
+
 int choose_path(const tfl_config& c) {
     const int dh = c.d_model / c.n_heads;
+    const Mode m = mode_of(c.dtype);
     // Short sequences: one workgroup keeps two whole sequences on chip for the
     // whole stack (one launch, no intermediate HBM traffic).
-    if (seq_supported(mode_of(c.dtype), c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
+    if (seq_supported(m, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
+    // Few long sequences: fewer (sequence, head, 64-query tile) units than
+    // compute units, so per-stage launches leave most of the chip idle; one
+    // persistent launch with split-K attention tasks fills it instead.
+    const long units = (long)c.batch * c.n_heads * ((c.seq_len + 63) / 64);
+    if (units < PQ_CU_COUNT && pq_supported(m, c.d_model, dh, c.d_ffn, c.n_layers)) return TFL_PATH_PQ;
     return TFL_PATH_TILED;
 }
 
@@ -66,7 +76,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     }
     int path = c.force_path == TFL_PATH_AUTO ? choose_path(c) : c.force_path;
     const Mode mode = mode_of(c.dtype);
-    if (path == TFL_PATH_PQ ||
+    if ((path == TFL_PATH_PQ && !pq_supported(mode, c.d_model, dh, c.d_ffn, c.n_layers)) ||
         (path == TFL_PATH_SEQ && !seq_supported(mode, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers))) {
         *why = "requested path is not available for this shape";
         return TFL_E_UNSUPPORTED;
@@ -92,6 +102,38 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         return TFL_OK;
     }
     const size_t Td = (size_t)T * q.d;
+    if (path == TFL_PATH_PQ) {
+        const int NT = q.Lp / ATT_KT;
+        const int BNT = q.B * NT;
+        q.pq_ks = 8;
+        q.pq_ctot = NT + q.pq_ks * (NT / q.pq_ks) * (NT / q.pq_ks - 1) / 2 + (NT / q.pq_ks) * (NT % q.pq_ks);
+        const long n_att = (long)q.B * q.H * q.pq_ctot;
+        const long n_tasks = BNT + (long)q.n_layers * (n_att + BNT);
+        if (n_tasks > INT_MAX / 2) {
+            *why = "too many tasks for the persistent path";
+            return TFL_E_UNSUPPORTED;
+        }
+        q.pq_tasks = (int)n_tasks;
+        // The single persistent launch stays off: one GPU run of it did not
+        // finish, with no cause found yet.  Stage launches run the same tasks.
+        q.pq_single = false;
+        q.pq_nctr = PQ_CTR_HDR + 2 * q.n_layers * BNT;
+        const size_t slots = (size_t)n_att;
+        size_t o = 0;
+        q.off_ctr = o; o += up256((size_t)q.pq_nctr * 4);
+        q.off_pX = o;  o += up256(Td * 4);
+        q.off_Qh = o;  o += up256(Td * 2 * q.n_layers);
+        q.off_Kh = o;  o += up256(Td * 2 * q.n_layers);
+        q.off_Ql = o;  o += up256(Td * 2);
+        q.off_Kl = o;  o += up256(Td * 2);
+        q.off_pVt = o; o += up256((size_t)q.B * q.d * q.Lp * 2 * q.n_layers);
+        q.off_Op = o;  o += up256(slots * 64 * q.dh * 4);
+        q.off_ML = o;  o += up256(slots * 64 * 8);
+        q.ws_bytes = o;
+        std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d/%s/%s", q.pq_ks, q.pq_single ? "queue" : "staged", q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
+        *p = q;
+        return TFL_OK;
+    }
     size_t o = 0;
     q.off_Xr = o; o += up256(Td * 4);
     q.off_X1 = o; o += up256(Td * 4);
@@ -225,10 +267,46 @@ static hipError_t run_seq(const Plan& P, const tfl_layer* layers, const void* x,
     return tm.done(launch_seq(P.mode, P.d, P.dh, a, s));
 }
 
+static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
+                         char* ws, hipStream_t s, StageTimer* T) {
+    PqArgs a{};
+    a.x = x;
+    a.y = y;
+    a.lens = lens;
+    a.B = P.B;
+    a.L = P.L;
+    a.Lp = P.Lp;
+    a.NT = P.Lp / ATT_KT;
+    a.F = P.f;
+    a.n_layers = P.n_layers;
+    a.KS = P.pq_ks;
+    a.Ctot = P.pq_ctot;
+    a.n_tasks = P.pq_tasks;
+    a.eps = P.eps;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+    a.ctr = (int*)(ws + P.off_ctr);
+    a.X = (float*)(ws + P.off_pX);
+    a.Qh = (_Float16*)(ws + P.off_Qh);
+    a.Kh = (_Float16*)(ws + P.off_Kh);
+    a.Ql = (_Float16*)(ws + P.off_Ql);
+    a.Kl = (_Float16*)(ws + P.off_Kl);
+    a.Vt = (_Float16*)(ws + P.off_pVt);
+    a.Op = (float*)(ws + P.off_Op);
+    a.ML = (float2*)(ws + P.off_ML);
+    for (int l = 0; l < P.n_layers; l++) {
+        const tfl_layer& w = layers[l];
+        a.lw[l] = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b,
+                            w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
+    }
+    Timed tm(T, TFL_STAGE_FUSED, s);
+    return tm.done(launch_pq(P.mode, P.d, P.dh, a, P.pq_nctr, P.pq_single, s));
+}
+
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,
                     hipStream_t s, StageTimer* timer) {
     switch (p.path) {
         case TFL_PATH_SEQ: return run_seq(p, layers, x, lens, y, s, timer);
+        case TFL_PATH_PQ: return run_pq(p, layers, x, lens, y, ws, s, timer);
         case TFL_PATH_TILED: return run_tiled(p, layers, x, lens, y, ws, s, timer);
     }
     return hipErrorInvalidValue;

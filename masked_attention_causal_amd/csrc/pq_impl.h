@@ -1,0 +1,945 @@
+// Persistent task-queue path (PQ): the whole encoder stack in one launch for
+// few, long sequences.  Every workgroup of a resident grid repeatedly takes
+// the next task id from an atomic queue head, waits on the dependency
+// counters of that task, runs it and releases its own counter; there is no
+// device-wide barrier.  This is the persistent, DAG-scheduled family of
+// "Hyper-optimized megakernel-hybrid transformer inference" ("Problem
+// decomposition" and "Performance optimization": a task graph fixed per
+// shape ahead of time, workgroups pop tasks until none are left, no grid
+// synchronisation).
+//
+// Task graph (64-row tiles of one sequence; t = tile, s = key split):
+//   QKV0(b,t)           layer-0 projection of x rows      -> ready[0][b,t]
+//   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
+//                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
+//                       needs ready[l][b,t'] for its key tiles and t
+//                                                          -> done[l][b,t]
+//   ROW(l,b,t)          merge of the partials, out-projection + residual +
+//                       LayerNorm, FFN (exact-erf GELU) + residual +
+//                       LayerNorm, then the next layer's QKV projection of
+//                       the same rows (or y after the last layer)
+//                       needs done[l][b,t] == H * nsplit(t)
+//                                                          -> ready[l+1][b,t]
+// Ids are handed out in a topological order (QKV0, then per layer all ATT,
+// then all ROW), so a task only ever waits on tasks that were taken before
+// it by running workgroups: the grid cannot deadlock whatever its size.
+//
+// Splitting one query tile's keys over several tasks and combining the
+// partial softmax states (m, l, O) exactly is the split-K attention of
+// "KernelForge" ("Challenges": balancing causal work by construction).
+// Key split boundaries depend on seq_len only, so the task list is fixed
+// per plan; splits past a sequence's valid length do no work.
+//
+// Products: activations of the 64 tile rows sit in LDS as fp16 (B operand);
+// each wave streams its own slice of output features' weight rows straight
+// from global memory into registers (A operand), so weights are never
+// staged through LDS and each weight fragment feeds four MFMAs.
+//
+// Precision: fp32 residual stream and LayerNorm; fp16 operands (bf16 and
+// fp32 weights are rounded to fp16 as they are loaded) except where the
+// first layer sees raw inputs: its attention scores use hi + lo fp16 parts
+// of fp32 Q and K (three MFMAs), and with fp32 I/O its QKV projection uses
+// hi + 2^11-scaled lo parts of both x and the weights (three MFMAs, two
+// accumulators), which keeps scores near 1e5 fp32-accurate.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace tfl {
+
+constexpr int PQ_THREADS = 256;
+constexpr int PQ_RT = 64;     // rows per tile (one tile = one attention query tile)
+constexpr int PQ_FC = 128;    // FFN features per chunk
+constexpr int PQ_GRID_CUS = 256;   // MI355X compute units
+// A dependency wait longer than this (in ticks of the 100 MHz constant clock
+// read by wall_clock64) is treated as a broken schedule: 0.5 s, far beyond the
+// run time of any forward this path is chosen for.
+constexpr uint64_t PQ_WAIT_TICKS = 50000000ull;
+
+// Index helpers of the task list (host and device).
+__host__ __device__ inline int pq_nsplit(int t, int ks) { return t / ks + 1; }
+// Number of (tile, split) pairs of tiles [0, t).
+__host__ __device__ inline int pq_pairs_before(int t, int ks) {
+    const int q = t / ks, r = t % ks;
+    return t + ks * q * (q - 1) / 2 + q * r;
+}
+
+template <class WT>
+__device__ __forceinline__ void load4_f32(const WT* p, float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) v[e] = to_f32(p[e]);
+}
+__device__ __forceinline__ void load4_f32(const float* p, float (&v)[4]) {
+    const float4 a = *(const float4*)p;
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void load4_f32(const f16* p, float (&v)[4]) {
+    const f16x4 a = *(const f16x4*)p;
+#pragma unroll
+    for (int e = 0; e < 4; e++) v[e] = (float)a[e];
+}
+
+template <class WT>
+__device__ __forceinline__ void store4(WT* p, const float (&v)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) p[e] = from_f32<WT>(v[e]);
+}
+__device__ __forceinline__ void store4(float* p, const float (&v)[4]) { *(float4*)p = float4{v[0], v[1], v[2], v[3]}; }
+__device__ __forceinline__ void store4(f16* p, const float (&v)[4]) {
+    *(f16x4*)p = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+}
+
+// Eight fp32 weights -> hi fp16 and lo fp16 scaled by 2^11 (w = hi + lo * 2^-11
+// to about 22 significant bits).
+__device__ __forceinline__ void load8_split(const float* p, f16x8& hi, f16x8& lo) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const f16 h = (f16)v[e];
+        hi[e] = h;
+        lo[e] = (f16)((v[e] - (float)h) * 2048.0f);
+    }
+}
+
+// acc[nb][rb] += W[n0 + 16 nb + i][k0 + k] * act[16 rb + j][k] for k < K:
+// the wave's 16*NBW output features (rows of W, A operand from global memory)
+// for the 64 tile rows (B operand from LDS, row pitch ald halves).
+// Result element e of acc[nb][rb] in lane (c16, g) is feature n0+16nb+4g+e
+// of tile row 16rb+c16.
+template <int NBW, int K, class WT>
+__device__ __forceinline__ void mm_rows(f32x4 (&acc)[NBW][4], const WT* W, int ldw, int n0, int k0, const f16* act,
+                                        int ald, int c16, int g) {
+    // K is walked in groups of at most 128; a group's weight fragments are
+    // all requested before its first MFMA.
+    constexpr int KS = (K > 128 ? 128 : K) / 32;
+    static_assert(K % (32 * KS) == 0, "K must be a multiple of the group");
+#pragma unroll 1
+    for (int kg = 0; kg < K; kg += 32 * KS) {
+        f16x8 a[KS][NBW];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int nb = 0; nb < NBW; nb++)
+                a[ks][nb] = load8_as_f16(W + (size_t)(n0 + 16 * nb + c16) * ldw + k0 + kg + ks * 32 + 8 * g);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            f16x8 bf[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++)
+                bf[rb] = *(const f16x8*)(act + (16 * rb + c16) * ald + kg + ks * 32 + 8 * g);
+#pragma unroll
+            for (int nb = 0; nb < NBW; nb++)
+#pragma unroll
+                for (int rb = 0; rb < 4; rb++) acc[nb][rb] = mfma_16x16x32(a[ks][nb], bf[rb], acc[nb][rb]);
+        }
+    }
+}
+
+// Three-pass version for fp32 weights and a hi/lo activation pair:
+// main += Wh*Ah, lo += Wl*Ah + Wh*Al (lo parts carry a 2^11 scale).
+template <int NBW, int K>
+__device__ __forceinline__ void mm_rows_split(f32x4 (&main)[NBW][4], f32x4 (&lo)[NBW][4], const float* W, int ldw,
+                                              int n0, const f16* act, const f16* act_lo, int ald, int c16, int g) {
+    constexpr int KS = K / 32;
+    static_assert(KS % 2 == 0, "K must be a multiple of 64");
+#pragma unroll 1
+    for (int ks2 = 0; ks2 < KS; ks2 += 2)
+#pragma unroll
+    for (int ks = ks2; ks < ks2 + 2; ks++) {
+        f16x8 wh[NBW], wl[NBW];
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++)
+            load8_split(W + (size_t)(n0 + 16 * nb + c16) * ldw + ks * 32 + 8 * g, wh[nb], wl[nb]);
+        f16x8 bh[4], bl[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            bh[rb] = *(const f16x8*)(act + (16 * rb + c16) * ald + ks * 32 + 8 * g);
+            bl[rb] = *(const f16x8*)(act_lo + (16 * rb + c16) * ald + ks * 32 + 8 * g);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) {
+                main[nb][rb] = mfma_16x16x32(wh[nb], bh[rb], main[nb][rb]);
+                lo[nb][rb] = mfma_16x16x32(wl[nb], bh[rb], lo[nb][rb]);
+                lo[nb][rb] = mfma_16x16x32(wh[nb], bl[rb], lo[nb][rb]);
+            }
+    }
+}
+
+// Sum over the D features of each tile row, features spread over the four
+// waves as in mm_rows.  red: 256 floats of LDS.  out[rb] = row 16rb+c16.
+template <int NB>
+__device__ __forceinline__ void row_sum(const f32x4 (&v)[NB][4], float* red, int wave, int c16, int g,
+                                        float (&out)[4]) {
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+        float s = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) s += (v[nb][rb][0] + v[nb][rb][1]) + (v[nb][rb][2] + v[nb][rb][3]);
+        s += __shfl_xor(s, 16, WAVE);
+        s += __shfl_xor(s, 32, WAVE);
+        if (g == 0) red[wave * 64 + 16 * rb + c16] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+        const int r = 16 * rb + c16;
+        out[rb] = (red[r] + red[64 + r]) + (red[128 + r] + red[192 + r]);
+    }
+}
+
+// Two-pass LayerNorm of the tile rows in place (fp32).
+template <int D, int NB, class WT>
+__device__ __forceinline__ void row_layernorm(f32x4 (&v)[NB][4], const WT* gamma, const WT* beta, float eps,
+                                              float* red0, float* red1, int n0, int wave, int c16, int g) {
+    float mean[4], var[4];
+    row_sum<NB>(v, red0, wave, c16, g, mean);
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) mean[rb] *= (1.0f / D);
+    f32x4 dv[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float c = v[nb][rb][e] - mean[rb];
+                dv[nb][rb][e] = c * c;
+            }
+    row_sum<NB>(dv, red1, wave, c16, g, var);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        float gm[4], bt[4];
+        load4_f32(gamma + n0 + 16 * nb + 4 * g, gm);
+        load4_f32(beta + n0 + 16 * nb + 4 * g, bt);
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const float rs = 1.0f / sqrtf(var[rb] * (1.0f / D) + eps);
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[nb][rb][e] = (v[nb][rb][e] - mean[rb]) * rs * gm[e] + bt[e];
+        }
+    }
+}
+
+template <class WT, int D, int DH>
+struct PqTile {
+    static constexpr bool F32 = sizeof(WT) == 4;
+    static constexpr int H = D / DH;
+    static constexpr int ALD = D + 8;                   // activation row pitch (halves)
+    static constexpr int GLD = PQ_FC + 8;               // FFN chunk row pitch
+    static constexpr int VLDT = PQ_RT + 8;              // V^T staging row pitch
+    static constexpr int NB = D / 64;                   // 16-feature blocks per wave for D outputs
+    static constexpr int QNB = (3 * D / 4) % 32 == 0 ? 2 : 1;   // blocks per QKV pass
+    static constexpr int QPASS = (3 * D / 4) / (16 * QNB);     // QKV passes per wave
+    static constexpr int ACT_BYTES = PQ_RT * ALD * 2;
+    static constexpr int G_BYTES = 2 * PQ_RT * GLD * 2;
+    static constexpr int VT_BYTES = D * VLDT * 2;
+    static constexpr int GV_BYTES = G_BYTES > VT_BYTES ? G_BYTES : VT_BYTES;
+    static constexpr int OFF_ACT = 0;
+    static constexpr int OFF_ACT2 = ACT_BYTES;                      // fp32 I/O: lo part of x (layer 0)
+    static constexpr int OFF_GV = OFF_ACT2 + (F32 ? ACT_BYTES : 0);
+    static constexpr int OFF_RED = OFF_GV + GV_BYTES;
+    static constexpr int ROW_BYTES = OFF_RED + 2 * 256 * 4;
+    // attention task
+    static constexpr int KLD = DH + 8, VLD = 64 + 8;
+    static constexpr int ATT_BYTES = 2 * (2 * 64 * KLD * 2) + 2 * DH * VLD * 2;
+    static constexpr int SMEM = ROW_BYTES > ATT_BYTES ? ROW_BYTES : ATT_BYTES;
+};
+
+// ------------------------------------------------------------------ QKV epilogue
+// One pass of QNB feature blocks starting at global QKV feature n0 (0..3D):
+// adds the bias, sends q and k rows to the head-major fp16 buffers (hi, and
+// lo when `lo_parts`), and v into the LDS V^T staging area.
+template <class WT, int D, int DH, int QNB>
+__device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqArgs& p, int layer, bool lo_parts,
+                                          int b, int t, int n0, f16* vts, int c16, int g) {
+    constexpr int H = D / DH;
+    const WT* bias = (const WT*)p.lw[layer].b_qkv;
+    const size_t TD = (size_t)p.B * p.L * D;
+#pragma unroll
+    for (int nb = 0; nb < QNB; nb++) {
+        const int n = n0 + 16 * nb + 4 * g;             // first of four consecutive features
+        float bv[4];
+        load4_f32(bias + n, bv);
+        const int which = n / D, nn = n - which * D;
+        const int h = nn / DH, dd = nn - h * DH;
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const int r = 16 * rb + c16, pos = t * PQ_RT + r;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[e] = acc[nb][rb][e] + bv[e];
+            if (which == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
+            } else if (pos < p.L) {
+                const size_t off = (size_t)layer * TD + (((size_t)b * H + h) * p.L + pos) * DH + dd;
+                f16* hi = (which == 0 ? p.Qh : p.Kh) + off;
+                f16x4 hv, lv;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    hv[e] = (f16)v[e];
+                    lv[e] = (f16)(v[e] - (float)hv[e]);
+                }
+                *(f16x4*)hi = hv;
+                if (lo_parts) *(f16x4*)((which == 0 ? p.Ql : p.Kl) + (off - (size_t)layer * TD)) = lv;
+            }
+        }
+    }
+}
+
+// Copies the staged V^T block [D][64] of tile t to the layer's V^T buffer.
+template <class WT, int D, int DH>
+__device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int t, const f16* vts, int tid) {
+    constexpr int H = D / DH;
+    constexpr int CH = D * (PQ_RT / 8);
+    f16* Vt = p.Vt + (size_t)layer * p.B * D * p.Lp;
+#pragma unroll
+    for (int i = 0; i < (CH + PQ_THREADS - 1) / PQ_THREADS; i++) {
+        const int c = tid + i * PQ_THREADS;
+        if (CH % PQ_THREADS != 0 && c >= CH) break;
+        const int nn = c / (PQ_RT / 8), c8 = (c % (PQ_RT / 8)) * 8;
+        const int h = nn / DH, dd = nn - h * DH;
+        *(uint4*)(Vt + (((size_t)b * H + h) * DH + dd) * p.Lp + t * PQ_RT + c8) =
+            *(const uint4*)(vts + nn * PqTile<WT, D, DH>::VLDT + c8);
+    }
+}
+
+// QKV projection of the 64 rows held in LDS (act; act_lo with fp32 I/O on
+// layer 0), then V^T flush.  Caller has synchronised after filling act.
+template <class WT, int D, int DH>
+__device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int t, char* smem, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    const f16* act = (const f16*)(smem + TL::OFF_ACT);
+    f16* vts = (f16*)(smem + TL::OFF_GV);
+    const WT* W = (const WT*)p.lw[layer].w_qkv;
+    const bool first = layer == 0;
+#pragma unroll 1
+    for (int ps = 0; ps < TL::QPASS; ps++) {
+        const int n0 = wave * (3 * D / 4) + ps * 16 * TL::QNB;
+        f32x4 acc[TL::QNB][4];
+#pragma unroll
+        for (int nb = 0; nb < TL::QNB; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) acc[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (TL::F32) {
+            if (first) {
+                f32x4 lo[TL::QNB][4];
+#pragma unroll
+                for (int nb = 0; nb < TL::QNB; nb++)
+#pragma unroll
+                    for (int rb = 0; rb < 4; rb++) lo[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                mm_rows_split<TL::QNB, D>(acc, lo, (const float*)W, D, n0, act,
+                                          (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
+#pragma unroll
+                for (int nb = 0; nb < TL::QNB; nb++)
+#pragma unroll
+                    for (int rb = 0; rb < 4; rb++) acc[nb][rb] += lo[nb][rb] * (1.0f / 2048.0f);
+            } else {
+                mm_rows<TL::QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
+            }
+        } else {
+            mm_rows<TL::QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
+        }
+        qkv_store<WT, D, DH, TL::QNB>(acc, p, layer, first, b, t, n0, vts, c16, g);
+    }
+    __syncthreads();
+    vt_flush<WT, D, DH>(p, layer, b, t, vts, tid);
+}
+
+// ------------------------------------------------------------------ tasks
+
+template <class WT, int D, int DH>
+__device__ void task_qkv0(const PqArgs& p, int b, int t, char* smem, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    f16* act = (f16*)(smem + TL::OFF_ACT);
+    f16* act_lo = (f16*)(smem + TL::OFF_ACT2);
+    const WT* x = (const WT*)p.x;
+    constexpr int CH = PQ_RT * D / 8;
+#pragma unroll
+    for (int i = 0; i < CH / PQ_THREADS; i++) {
+        const int c = tid + i * PQ_THREADS;
+        const int r = c / (D / 8), k = (c % (D / 8)) * 8;
+        const int pos = t * PQ_RT + r;
+        const bool ok = pos < p.L;
+        const WT* src = x + ((size_t)b * p.L + pos) * D + k;
+        if constexpr (TL::F32) {
+            f16x8 hi = {}, lo = {};
+            if (ok) {
+                const float4 a = *(const float4*)src, c2 = *(const float4*)(src + 4);
+                const float v[8] = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const f16 h = (f16)v[e];
+                    hi[e] = h;
+                    lo[e] = (f16)((v[e] - (float)h) * 2048.0f);
+                }
+            }
+            *(f16x8*)(act + r * TL::ALD + k) = hi;
+            *(f16x8*)(act_lo + r * TL::ALD + k) = lo;
+        } else {
+            *(f16x8*)(act + r * TL::ALD + k) = ok ? load8_as_f16(src) : f16x8{};
+        }
+    }
+    __syncthreads();
+    qkv_rows<WT, D, DH>(p, 0, b, t, smem, tid);
+}
+
+template <class WT, int D, int DH, bool SPLIT>
+__device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, char* smem, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    constexpr int KT = 64, KLD = TL::KLD, VLD = TL::VLD, ND = DH / 16, QK = DH / 32;
+    constexpr int H = D / DH;
+    f16* Ks = (f16*)smem;                  // [2][KT * KLD]
+    f16* Kls = Ks + 2 * KT * KLD;          // [2][KT * KLD]
+    f16* Vs = Kls + 2 * KT * KLD;          // [2][DH * VLD]
+    const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    const int L = p.L, Lp = p.Lp;
+    int len = p.lens[b];
+    len = len < 1 ? 1 : (len > L ? L : len);
+    const int q0 = t * PQ_RT, qw0 = q0 + 16 * wave;
+    const int kend = min(q0 + PQ_RT, len);
+    const int kt0 = s * p.KS;
+    const int kt1 = min(min(kt0 + p.KS, t + 1), (kend + KT - 1) / KT);
+    const int ntl = kt1 - kt0;             // may be <= 0: split past the valid length
+    const size_t TD = (size_t)p.B * L * D;
+    const size_t bh = (size_t)b * H + h;
+    const f16* Qg = p.Qh + (size_t)l * TD + bh * L * DH;
+    const f16* Qlg = p.Ql + bh * L * DH;
+    const f16* Kg = p.Kh + (size_t)l * TD + bh * L * DH;
+    const f16* Klg = p.Kl + bh * L * DH;
+    const f16* Vg = p.Vt + (size_t)l * p.B * D * Lp + bh * DH * Lp;
+
+    const int myq = qw0 + c16;
+    const bool qok = myq < L;
+    f16x8 qh[QK], ql[SPLIT ? QK : 1];
+#pragma unroll
+    for (int kk = 0; kk < QK; kk++) {
+        qh[kk] = qok ? *(const f16x8*)(Qg + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
+        if constexpr (SPLIT) ql[kk] = qok ? *(const f16x8*)(Qlg + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
+    }
+
+    constexpr int KCH = KT * DH / 8;       // 16-byte chunks of a K tile
+    constexpr int KPT = KCH / PQ_THREADS;
+    constexpr int VCH = DH * KT / 8;
+    constexpr int VPT = VCH / PQ_THREADS;
+    static_assert(KPT >= 1 && VPT >= 1, "tile too small");
+    uint4 rk[KPT], rkl[SPLIT ? KPT : 1], rv[VPT];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int c = tid + i * PQ_THREADS, key = c / (DH / 8), col = (c % (DH / 8)) * 8;
+            const bool ok = k0 + key < L;
+            rk[i] = ok ? *(const uint4*)(Kg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
+            if constexpr (SPLIT) rkl[i] = ok ? *(const uint4*)(Klg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+            const int c = tid + i * PQ_THREADS, row = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+            const f16* src = Vg + (size_t)row * Lp + k0 + kc;
+            if (k0 + kc + 8 <= L) {
+                rv[i] = *(const uint4*)src;
+            } else {
+                union { uint4 u; f16 e[8]; } tmp;
+#pragma unroll
+                for (int e = 0; e < 8; e++) tmp.e[e] = (k0 + kc + e < L) ? src[e] : (f16)0.f;
+                rv[i] = tmp.u;
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int c = tid + i * PQ_THREADS, key = c / (DH / 8), col = (c % (DH / 8)) * 8;
+            *(uint4*)&Ks[buf * KT * KLD + key * KLD + col] = rk[i];
+            if constexpr (SPLIT) *(uint4*)&Kls[buf * KT * KLD + key * KLD + col] = rkl[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; i++) {
+            const int c = tid + i * PQ_THREADS, row = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+            *(uint4*)&Vs[buf * DH * VLD + row * VLD + kc] = rv[i];
+        }
+    };
+
+    f32x4 o[ND];
+#pragma unroll
+    for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+
+    if (ntl > 0) {
+        gload(kt0 * KT);
+        sstore(0);
+        __syncthreads();
+#pragma unroll 1
+        for (int it = 0; it < ntl; it++) {
+            const int buf = it & 1;
+            const int k0 = (kt0 + it) * KT;
+            if (it + 1 < ntl) gload(k0 + KT);
+            if (k0 <= qw0 + 15) {
+                const f16* ks = Ks + buf * KT * KLD;
+                const f16* kls = Kls + buf * KT * KLD;
+                const f16* vs = Vs + buf * DH * VLD;
+                // S^T = K Q^T; key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
+                f32x4 sc[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++) {
+                    sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const int krow = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
+#pragma unroll
+                    for (int kk = 0; kk < QK; kk++) {
+                        const f16x8 a = *(const f16x8*)&ks[krow * KLD + kk * 32 + g * 8];
+                        sc[kb] = mfma_16x16x32(a, qh[kk], sc[kb]);
+                        if constexpr (SPLIT) {
+                            const f16x8 al = *(const f16x8*)&kls[krow * KLD + kk * 32 + g * 8];
+                            sc[kb] = mfma_16x16x32(al, qh[kk], sc[kb]);
+                            sc[kb] = mfma_16x16x32(a, ql[kk], sc[kb]);
+                        }
+                    }
+                }
+                const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        float v = sc[kb][e] * sl2;
+                        if (need_mask) {
+                            const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
+                            if (key > myq || key >= len) v = -INFINITY;
+                        }
+                        sc[kb][e] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                const float m_new = fmaxf(m_run, mx);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = exp2f(m_run - m_use);
+                m_run = m_new;
+                float ls = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float pv = exp2f(sc[kb][e] - m_use);
+                        sc[kb][e] = pv;
+                        ls += pv;
+                    }
+                l_run = l_run * alpha + ls;
+#pragma unroll
+                for (int db = 0; db < ND; db++) o[db] *= alpha;
+#pragma unroll
+                for (int cc = 0; cc < 2; cc++) {
+                    f16x8 pb;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        pb[e] = (f16)sc[2 * cc][e];
+                        pb[4 + e] = (f16)sc[2 * cc + 1][e];
+                    }
+#pragma unroll
+                    for (int db = 0; db < ND; db++) {
+                        const f16x8 va = *(const f16x8*)&vs[(db * 16 + c16) * VLD + cc * 32 + g * 8];
+                        o[db] = mfma_16x16x32(va, pb, o[db]);
+                    }
+                }
+            }
+            if (it + 1 < ntl) sstore(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    l_run += __shfl_xor(l_run, 16, WAVE);
+    l_run += __shfl_xor(l_run, 32, WAVE);
+    // partial state of (b, h, t, s): unnormalised O, running max (log2 units), sum
+    const size_t slot = ((size_t)b * H + h) * p.Ctot + pq_pairs_before(t, p.KS) + s;
+    const int qr = 16 * wave + c16;
+    float* op = p.Op + (slot * PQ_RT + qr) * DH;
+#pragma unroll
+    for (int db = 0; db < ND; db++) *(float4*)(op + db * 16 + 4 * g) = float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+    if (g == 0) p.ML[slot * PQ_RT + qr] = float2{m_run, l_run};
+}
+
+// Merge of the split partials of tile t into fp16 attention output rows in LDS.
+template <class WT, int D, int DH>
+__device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* act, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    constexpr int H = D / DH, QD = DH / 4;
+    const int r = tid >> 2, qd = (tid & 3) * QD;
+    const int pos = t * PQ_RT + r;
+    const int ns = pq_nsplit(t, p.KS);
+    const int pb = pq_pairs_before(t, p.KS);
+#pragma unroll 1
+    for (int h = 0; h < H; h++) {
+        float acc[QD];
+#pragma unroll
+        for (int i = 0; i < QD; i++) acc[i] = 0.f;
+        if (pos < p.L) {
+            const size_t slot0 = ((size_t)b * H + h) * p.Ctot + pb;
+            float M = -INFINITY;
+#pragma unroll 1
+            for (int s = 0; s < ns; s++) M = fmaxf(M, p.ML[(slot0 + s) * PQ_RT + r].x);
+            float lsum = 0.f;
+#pragma unroll 1
+            for (int s = 0; s < ns; s++) {
+                const float2 ml = p.ML[(slot0 + s) * PQ_RT + r];
+                if (ml.x == -INFINITY) continue;
+                const float w = exp2f(ml.x - M);
+                lsum += w * ml.y;
+                const float* op = p.Op + ((slot0 + s) * PQ_RT + r) * DH + qd;
+#pragma unroll
+                for (int i = 0; i < QD; i += 4) {
+                    const float4 v = *(const float4*)(op + i);
+                    acc[i] += w * v.x;
+                    acc[i + 1] += w * v.y;
+                    acc[i + 2] += w * v.z;
+                    acc[i + 3] += w * v.w;
+                }
+            }
+            const float inv = 1.0f / lsum;
+#pragma unroll
+            for (int i = 0; i < QD; i++) acc[i] *= inv;
+        }
+#pragma unroll
+        for (int i = 0; i < QD; i += 8) {
+            f16x8 hv;
+#pragma unroll
+            for (int e = 0; e < 8; e++) hv[e] = (f16)acc[i + e];
+            *(f16x8*)(act + r * TL::ALD + h * DH + qd + i) = hv;
+        }
+    }
+}
+
+template <class WT, int D, int DH>
+__device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    constexpr int NB = TL::NB;
+    const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    f16* act = (f16*)(smem + TL::OFF_ACT);
+    f16* gs = (f16*)(smem + TL::OFF_GV);
+    float* red0 = (float*)(smem + TL::OFF_RED);
+    float* red1 = red0 + 256;
+    const LayerPtrs& w = p.lw[l];
+    const int n0 = wave * (D / 4);          // this wave's output features
+    const bool last = l == p.n_layers - 1;
+
+    merge_att<WT, D, DH>(p, b, t, act, tid);
+    __syncthreads();
+
+    // ---- out-projection + bias + residual
+    f32x4 z[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) z[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NB == 1) {
+        mm_rows<1, D>(z, (const WT*)w.w_o, D, n0, 0, act, TL::ALD, c16, g);
+    } else {
+#pragma unroll
+        for (int half = 0; half < NB / 2; half++) {
+            f32x4 (&zz)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&z[2 * half]);
+            mm_rows<2, D>(zz, (const WT*)w.w_o, D, n0 + 32 * half, 0, act, TL::ALD, c16, g);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        const int n = n0 + 16 * nb + 4 * g;
+        float bv[4];
+        load4_f32((const WT*)w.b_o + n, bv);
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const int pos = t * PQ_RT + 16 * rb + c16;
+            float xr[4] = {0.f, 0.f, 0.f, 0.f};
+            if (pos < p.L) {
+                const size_t row = (size_t)b * p.L + pos;
+                if (l == 0)
+                    load4_f32((const WT*)p.x + row * D + n, xr);
+                else
+                    load4_f32(p.X + row * D + n, xr);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) z[nb][rb][e] += bv[e] + xr[e];
+        }
+    }
+    row_layernorm<D, NB>(z, (const WT*)w.ln1_g, (const WT*)w.ln1_b, p.eps, red0, red1, n0, wave, c16, g);
+    // X1: fp16 operand copy in LDS (every wave is past its out-projection
+    // reads: row_sum synchronised) and the fp32 value in this tile's rows of
+    // the residual buffer, read back by the same lanes after the FFN (the
+    // layer input there is no longer needed).
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const int r = 16 * rb + c16, pos = t * PQ_RT + r;
+            const float v[4] = {z[nb][rb][0], z[nb][rb][1], z[nb][rb][2], z[nb][rb][3]};
+            store4(act + r * TL::ALD + n0 + 16 * nb + 4 * g, v);
+            if (pos < p.L) store4(p.X + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
+        }
+    __syncthreads();
+
+    // ---- FFN in chunks of PQ_FC features: G chunk to LDS, then accumulate W2 G^T
+    f32x4 y2[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) y2[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nch = p.F / PQ_FC;
+#pragma unroll 1
+    for (int c = 0; c < nch; c++) {
+        f16* gb = gs + (c & 1) * PQ_RT * TL::GLD;
+        const int f0 = c * PQ_FC + wave * (PQ_FC / 4);
+        f32x4 ga[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) ga[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mm_rows<2, D>(ga, (const WT*)w.w_1, D, f0, 0, act, TL::ALD, c16, g);
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++) {
+            float bv[4];
+            load4_f32((const WT*)w.b_1 + f0 + 16 * nb + 4 * g, bv);
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) {
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; e++) hv[e] = (f16)gelu_erf(ga[nb][rb][e] + bv[e]);
+                *(f16x4*)(gb + (16 * rb + c16) * TL::GLD + wave * (PQ_FC / 4) + 16 * nb + 4 * g) = hv;
+            }
+        }
+        __syncthreads();
+        if constexpr (NB == 1) {
+            mm_rows<1, PQ_FC>(y2, (const WT*)w.w_2, p.F, n0, c * PQ_FC, gb, TL::GLD, c16, g);
+        } else {
+#pragma unroll
+            for (int half = 0; half < NB / 2; half++) {
+                f32x4 (&yy)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&y2[2 * half]);
+                mm_rows<2, PQ_FC>(yy, (const WT*)w.w_2, p.F, n0 + 32 * half, c * PQ_FC, gb, TL::GLD, c16, g);
+            }
+        }
+    }
+    // ---- + bias + residual (X1), LayerNorm
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        float bv[4];
+        load4_f32((const WT*)w.b_2 + n0 + 16 * nb + 4 * g, bv);
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const int pos = t * PQ_RT + 16 * rb + c16;
+            float xr[4] = {0.f, 0.f, 0.f, 0.f};
+            if (pos < p.L) load4_f32(p.X + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, xr);
+#pragma unroll
+            for (int e = 0; e < 4; e++) y2[nb][rb][e] += bv[e] + xr[e];
+        }
+    }
+    row_layernorm<D, NB>(y2, (const WT*)w.ln2_g, (const WT*)w.ln2_b, p.eps, red0, red1, n0, wave, c16, g);
+
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        const int n = n0 + 16 * nb + 4 * g;
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            const int r = 16 * rb + c16, pos = t * PQ_RT + r;
+            const float v[4] = {y2[nb][rb][0], y2[nb][rb][1], y2[nb][rb][2], y2[nb][rb][3]};
+            if (pos < p.L) {
+                const size_t row = (size_t)b * p.L + pos;
+                if (last)
+                    store4((WT*)p.y + row * D + n, v);
+                else
+                    store4(p.X + row * D + n, v);
+            }
+            if (!last) store4(act + r * TL::ALD + n, v);
+        }
+    }
+    if (last) return;
+    __syncthreads();
+    qkv_rows<WT, D, DH>(p, l + 1, b, t, smem, tid);
+}
+
+// ------------------------------------------------------------------ scheduler
+
+// Waits until every counter ctr[i], i in [first, first + count), and ctr[extra]
+// reaches `need`.  Wave 0 polls; on a wait far beyond any legal run time the
+// watchdog flag is raised and the wait abandoned, so every wave still exits.
+__device__ __forceinline__ void pq_wait(int* flags, int first, int count, int extra, int need, int* err, int tid) {
+    if (tid < 64) {
+        const int lane = tid;
+        const bool mine = lane < count || lane == 63;
+        int* f = flags + (lane == 63 ? extra : first + lane);
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            bool ok = true;
+            if (mine) ok = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
+            if (__all(ok)) break;
+            if (wall_clock64() - t0 > PQ_WAIT_TICKS) {
+                if (lane == 0) __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ void pq_release(int* flag, int tid) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Task id -> (kind, layer, sequence, head, tile, split).  kind: 0 QKV0, 1 ATT, 2 ROW.
+struct PqTask {
+    int kind, l, b, h, t, s;
+};
+template <int H>
+__device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
+    PqTask k{};
+    const int BNT = p.B * p.NT;
+    if (task < BNT) {                            // QKV0(b, t): tile-major order
+        k.kind = 0;
+        k.t = task / p.B;
+        k.b = task - k.t * p.B;
+        return k;
+    }
+    task -= BNT;
+    const int n_att = p.B * H * p.Ctot;
+    const int seg = n_att + BNT;                 // tasks per layer after QKV0
+    k.l = task / seg;
+    int r = task - k.l * seg;
+    if (r < n_att) {                             // ATT(l, b, h, t, s)
+        const int BH = p.B * H;
+        const int pair = r / BH, bh = r - pair * BH;
+        int lo = 0, hi = p.NT - 1;               // tile t with pairs_before(t) <= pair < pairs_before(t+1)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pq_pairs_before(mid, p.KS) <= pair) lo = mid; else hi = mid - 1;
+        }
+        k.kind = 1;
+        k.t = lo;
+        k.s = pair - pq_pairs_before(lo, p.KS);
+        k.b = bh / H;
+        k.h = bh - k.b * H;
+    } else {                                     // ROW(l, b, t)
+        r -= n_att;
+        k.kind = 2;
+        k.t = r / p.B;
+        k.b = r - k.t * p.B;
+    }
+    return k;
+}
+
+template <class WT, int D, int DH>
+__device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* smem, int tid) {
+    if (k.kind == 0)
+        task_qkv0<WT, D, DH>(p, k.b, k.t, smem, tid);
+    else if (k.kind == 1 && k.l == 0)
+        task_att<WT, D, DH, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+    else if (k.kind == 1)
+        task_att<WT, D, DH, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+    else
+        task_row<WT, D, DH>(p, k.l, k.b, k.t, smem, tid);
+}
+
+// Stage-ordered execution of the same task list: one launch per stage
+// (QKV0, then ATT and ROW of every layer), workgroup i running task
+// begin + i.  Every dependency of a stage was completed by an earlier launch
+// on the stream, so no workgroup ever waits on another.
+template <class WT, int D, int DH>
+__global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int begin) {
+    typedef PqTile<WT, D, DH> TL;
+    __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
+    const PqTask k = pq_decode<D / DH>(p, begin + (int)blockIdx.x);
+    pq_run<WT, D, DH>(p, k, smem, threadIdx.x);
+}
+
+template <class WT, int D, int DH>
+__global__ __launch_bounds__(PQ_THREADS, 2) void pq_kernel(PqArgs p) {
+    typedef PqTile<WT, D, DH> TL;
+    constexpr int H = D / DH;
+    __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
+    __shared__ int s_task;
+    const int tid = threadIdx.x;
+    const int BNT = p.B * p.NT;
+    int* ready = p.ctr + PQ_CTR_HDR;
+    int* done = ready + p.n_layers * BNT;
+#pragma unroll 1
+    for (;;) {
+        if (tid == 0) s_task = __hip_atomic_fetch_add(p.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int task = s_task;
+        __syncthreads();
+        if (task >= p.n_tasks) break;
+        const PqTask k = pq_decode<H>(p, task);
+        if (k.kind == 0) {
+            pq_run<WT, D, DH>(p, k, smem, tid);
+            pq_release(ready + k.b * p.NT + k.t, tid);
+        } else if (k.kind == 1) {
+            const int kt0 = k.s * p.KS, kt1 = min(kt0 + p.KS, k.t + 1);
+            pq_wait(ready + k.l * BNT + k.b * p.NT, kt0, kt1 - kt0, k.t, 1, p.ctr + 1, tid);
+            pq_run<WT, D, DH>(p, k, smem, tid);
+            pq_release(done + k.l * BNT + k.b * p.NT + k.t, tid);
+        } else {
+            const int idx = k.l * BNT + k.b * p.NT + k.t;
+            pq_wait(done, idx, 1, idx, H * pq_nsplit(k.t, p.KS), p.ctr + 1, tid);
+            pq_run<WT, D, DH>(p, k, smem, tid);
+            if (k.l + 1 < p.n_layers)
+                pq_release(ready + (k.l + 1) * BNT + k.b * p.NT + k.t, tid);
+            else
+                __syncthreads();
+        }
+    }
+}
+
+static __global__ void pq_zero_kernel(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+template <class WT, int D, int DH>
+hipError_t pq_launch_t(const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s) {
+    typedef PqTile<WT, D, DH> TL;
+    static_assert(TL::SMEM <= 160 * 1024, "LDS budget");
+    // Resident grid: the part's compute units times the workgroups one of
+    // them holds (LDS-limited; registers are bounded to two waves per SIMD).
+    // The queue makes progress with any grid size, so this only sets how
+    // many tasks run at once.
+    constexpr int PER_CU = TL::SMEM <= 80 * 1024 ? 2 : 1;
+    hipError_t e;
+    if (!single_launch) {
+        const int BNT = a.B * a.NT, n_att = a.B * (D / DH) * a.Ctot;
+        int begin = 0;
+        auto stage = [&](int n) {
+            hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, begin);
+            begin += n;
+            return hipGetLastError();
+        };
+        if ((e = stage(BNT)) != hipSuccess) return e;
+        for (int l = 0; l < a.n_layers; l++) {
+            if ((e = stage(n_att)) != hipSuccess) return e;
+            if ((e = stage(BNT)) != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int grid = min(a.n_tasks, PQ_GRID_CUS * PER_CU);
+    hipLaunchKernelGGL(pq_zero_kernel, dim3((n_ctr + 255) / 256), dim3(256), 0, s, a.ctr, n_ctr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((pq_kernel<WT, D, DH>), dim3(grid), dim3(PQ_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class WT>
+hipError_t pq_launch_mode(int d, int dh, const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s) {
+    if (dh == 64) {
+        if (d == 64) return pq_launch_t<WT, 64, 64>(a, n_ctr, single_launch, s);
+        if (d == 128) return pq_launch_t<WT, 128, 64>(a, n_ctr, single_launch, s);
+        if (d == 256) return pq_launch_t<WT, 256, 64>(a, n_ctr, single_launch, s);
+    } else if (dh == 32) {
+        if (d == 64) return pq_launch_t<WT, 64, 32>(a, n_ctr, single_launch, s);
+        if (d == 128) return pq_launch_t<WT, 128, 32>(a, n_ctr, single_launch, s);
+        if (d == 256) return pq_launch_t<WT, 256, 32>(a, n_ctr, single_launch, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tfl

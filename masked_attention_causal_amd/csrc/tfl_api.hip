@@ -95,7 +95,8 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
     hipStream_t s = (hipStream_t)hip_stream;
 
     const char* chk = std::getenv("TFL_CHECK");
-    if (chk && chk[0] == '1') {
+    const bool check = chk && chk[0] == '1';
+    if (check) {
         std::vector<int32_t> lens(P.B);
         hipError_t e = hipMemcpyAsync(lens.data(), valid_len, sizeof(int32_t) * P.B, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -108,6 +109,16 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
     tfl::StageTimer* tm = h->timer.stage ? &h->timer : nullptr;
     const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s, tm);
     if (e != hipSuccess) return hip_fail(e, "tfl_forward: kernel launch");
+    if (check && P.path == TFL_PATH_PQ && P.pq_single) {
+        // The persistent path raises a flag instead of waiting forever on a
+        // dependency that never completes; read it back.
+        int32_t flag = 0;
+        hipError_t e2 = hipMemcpyAsync(&flag, (char*)workspace + P.off_ctr + sizeof(int32_t), sizeof(flag),
+                                       hipMemcpyDeviceToHost, s);
+        if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
+        if (e2 != hipSuccess) return hip_fail(e2, "tfl_forward: TFL_CHECK read of the task-queue flag");
+        if (flag != 0) return fail(TFL_E_INTERNAL, "tfl_forward: task-queue dependency wait timed out");
+    }
     return TFL_OK;
 }
 

@@ -54,6 +54,35 @@ def test_dispatcher_rules():
         tfl.plan_for(2, 64, 4, 256, 4, 32, "f32", force_path="seq")
 
 
+def test_pq_dispatch_rules():
+    # fewer (sequence, head, 64-query tile) units than compute units and no
+    # sequence-resident fit -> persistent task-queue path
+    assert tfl.plan_for(2, 128, 2, 512, 1, 4096, "f32")[1] == "pq"
+    assert tfl.plan_for(2, 256, 4, 1024, 1, 1000, "bf16")[1] == "pq"
+    assert tfl.plan_for(2, 128, 2, 512, 2, 4096, "f32")[1] == "tiled"    # 256 units
+    assert tfl.plan_for(2, 128, 2, 96 * 5, 1, 4096, "f16")[1] == "tiled"  # FFN width not a multiple of 128
+    assert tfl.plan_for(2, 64, 4, 256, 1, 4096, "f16")[1] == "tiled"      # head dim 16
+    with pytest.raises(tfl.TflError) as e:
+        tfl.plan_for(2, 64, 4, 256, 1, 300, "f16", force_path="pq")
+    assert e.value.status == 2
+
+
+def test_pq_workspace_layout():
+    n_layers, d, H, f, B, L = 2, 128, 2, 512, 1, 4096
+    plan, path, ws = tfl.plan_for(n_layers, d, H, f, B, L, "f32", force_path="pq")
+    assert path == "pq" and plan.startswith("PQ/")
+    up = lambda v: (v + 255) // 256 * 256
+    NT = (L + 63) // 64
+    ks = 8
+    q, r = NT // ks, NT % ks
+    pairs = NT + ks * q * (q - 1) // 2 + q * r          # (tile, split) pairs per (sequence, head)
+    assert pairs == sum(t // ks + 1 for t in range(NT))
+    T, dh, Lp = B * L, d // H, NT * 64
+    need = (up((64 + 2 * n_layers * B * NT) * 4) + up(T * d * 4) + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
+            + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8))
+    assert ws == need
+
+
 def test_workspace_covers_the_tiled_buffers():
     w = synth.WORKLOADS["stream_d64_b1_l100000"]
     _, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
