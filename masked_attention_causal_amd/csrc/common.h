@@ -73,6 +73,23 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- LDS-DMA
+
+typedef __attribute__((address_space(3))) f16 lds_f16;
+
+// 16-byte global-to-LDS load: lane i of the wave writes its 16 source bytes
+// to lds_wave_base + 16 i (lds_wave_base is wave-uniform).  Issued through
+// asm so the compiler does not make every later LDS read wait for it; the
+// caller waits (s_waitcnt vmcnt) before the barrier that publishes the data.
+// M0 is written here and has no other user in the kernels that call this.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_f16*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // ---------------------------------------------------------------- wave reductions
 
 template <int WIDTH>

@@ -16,6 +16,8 @@
 // (BM/2) x (BN/2) block of 16 x 16 MFMA tiles.  A and W tiles are staged in
 // LDS, double-buffered, with the next tile's global loads in flight while
 // the current one is multiplied.
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -203,6 +205,13 @@ static hipError_t gemm_mode(Epi e, const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+    // TFL_GEMM_BASIC=1 keeps every product on the kernel above (for A/B
+    // comparisons of the two GEMM kernels).
+    static const bool basic_only = [] {
+        const char* v = std::getenv("TFL_GEMM_BASIC");
+        return v && v[0] == '1';
+    }();
+    if (m != MODE_F32 && !basic_only && gemm_pipe_ok(a)) return launch_gemm_pipe(m, e, a, s);
     switch (m) {
         case MODE_F32: return gemm_mode<float, float>(e, a, s);
         case MODE_F16: return gemm_mode<f16, f16>(e, a, s);

@@ -94,6 +94,9 @@ constexpr int ATT_BQ = 64;   // queries per attention workgroup
 
 hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s);
 hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
+// Multi-stage LDS-DMA pipelined GEMM (16-bit operand modes, K % 64 == 0).
+bool gemm_pipe_ok(const GemmArgs& a);
+hipError_t launch_gemm_pipe(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
 hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta, float eps,
                      int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);

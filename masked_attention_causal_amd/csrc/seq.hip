@@ -90,19 +90,7 @@ __device__ __forceinline__ f32x4 load4(const T* q) {
     }
 }
 
-typedef __attribute__((address_space(3))) f16 lds_f16;
 
-// 16-byte LDS-DMA: lane i of the wave writes its 16 source bytes to
-// lds_wave_base + 16 i.  Issued through asm so the compiler does not make
-// every later LDS read wait for it; the caller waits (vmcnt) before the
-// barrier that publishes the data.  M0 has no other user in this kernel.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, f16* lds_wave_base) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_f16*)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Scheduling order for a fully unrolled product of NM MFMAs fed by NDS LDS
 // reads, MPR MFMAs per read: AHEAD reads are issued first, then MPR MFMAs

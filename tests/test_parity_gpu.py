@@ -122,6 +122,29 @@ def test_stream_workload_prefix_and_golden_rows():
     assert_gate(y[0, rows], ref, "stream golden rows")
 
 
+# ---------------------------------------------------------------- pipelined GEMM tiles
+
+PIPE = [
+    # 256-token tiles (wide QKV / FFN1) with a ragged last token tile; 128 x 128 tiles elsewhere
+    W("g_bf16_d512", 2, 512, 8, 1024, 3, 700, "bf16", 1, 700, 1.0),
+    # N = 3 * 320 = 960 and 320: feature blocks past N are clamped copies
+    W("g_f16_d320", 1, 320, 5, 640, 7, 500, "f16", 1, 500, 1.0),
+]
+
+
+@pytest.mark.parametrize("w", PIPE, ids=lambda w: w.name)
+def test_pipelined_gemm_shapes(w):
+    # Input scale stops at 1e2 here: at 1e3 with d = 512 and random affine
+    # parameters the first-layer scores reach ~5e5, and a few rows whose two
+    # largest scores lie within ~1 of each other sit inside the fp32 score
+    # rounding (|s| * 2^-22 ~ 0.15), for either GEMM kernel.
+    for seed, scale, affine in ((0, 1.0, False), (1, 1.0, True), (2, 1e2, True), (3, 1e-3, False)):
+        inp = _case(w, seed, scale, affine=affine)
+        inp.lens[0] = w.L
+        say(f"[pipe] {w.name} seed={seed} scale={scale} affine={affine} lens={inp.lens.tolist()}")
+        assert_gate(gpu_forward(inp, force_path="tiled"), oracle_forward(inp), f"{w.name} seed {seed}")
+
+
 # ---------------------------------------------------------------- edge cases
 
 
