@@ -22,12 +22,18 @@
 // that owns the query, and the running max needs only a reduction across
 // the four 16-lane groups of the wave.
 //
-// Precision: Q and K arrive in fp32.  F32 mode multiplies them on fp32 MFMA.
-// F16/BF16 modes either round them to fp16 (one MFMA), or, for the first
-// layer where raw inputs up to 1e3 give scores near 1e5, split each into
-// hi + lo fp16 parts and form hi*hi + hi*lo + lo*hi (three MFMAs), which
-// keeps the scores at about fp32 accuracy.  P is rounded to the operand
-// dtype (fp16 or fp32) for the P V product; the row sum uses fp32 P.
+// Precision: F32 mode takes fp32 Q and K and multiplies them on fp32 MFMA.
+// F16/BF16 modes take Q and K as fp16 planes written by the QKV epilogue:
+// the rounded value, and for the first layer (raw inputs up to 1e3 give
+// scores near 1e5) also the rounding remainder, so scores are formed as
+// hi*hi + hi*lo + lo*hi (three MFMAs) at about fp32 accuracy.  P is rounded
+// to the operand dtype (fp16 or fp32) for the P V product; the row sum uses
+// fp32 P.
+//
+// Two kernels: attn_kernel stages K and V^T through registers (F32 mode,
+// and head dim 16); attn_ring_kernel (16-bit modes, head dim 32 or 64)
+// streams them with LDS-DMA into a ring of three tile buffers, two tiles
+// ahead of the MFMAs.
 #include "common.h"
 #include "kernels.h"
 
@@ -61,8 +67,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     const int kend = min(q0 + BQ, len);          // keys [0, kend) matter to the workgroup
     const int ntiles = (kend + KT - 1) / KT;
     const size_t bh = (size_t)b * p.H + h;
-    const float* __restrict__ Qg = p.Q + bh * L * DH;
-    const float* __restrict__ Kg = p.K + bh * L * DH;
+    // F32: fp32 Q, K.  16-bit modes: fp16 hi planes (and lo planes when SPLIT).
+    const float* __restrict__ Qg = (const float*)p.Q + bh * L * DH;
+    const float* __restrict__ Kg = (const float*)p.K + bh * L * DH;
+    const f16* __restrict__ Qhg = (const f16*)p.Q + bh * L * DH;
+    const f16* __restrict__ Qlg = (const f16*)p.Ql + bh * L * DH;
+    const f16* __restrict__ Khg = (const f16*)p.K + bh * L * DH;
+    const f16* __restrict__ Klg = (const f16*)p.Kl + bh * L * DH;
     const OpT* __restrict__ Vg = (const OpT*)p.Vt + bh * DH * Lp;
 
     // ---- this lane's query operand (B operand of S^T = K Q^T), query qw0 + c16
@@ -78,31 +89,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     } else if constexpr (DH >= 32) {
 #pragma unroll
         for (int ks = 0; ks < QK; ks++) {
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float v = qok ? Qg[(size_t)myq * DH + ks * 32 + g * 8 + e] : 0.f;
-                const f16 hv = (f16)v;
-                qh8[ks][e] = hv;
-                if constexpr (SPLIT) ql8[ks][e] = (f16)(v - (float)hv);
-            }
+            qh8[ks] = qok ? *(const f16x8*)(Qhg + (size_t)myq * DH + ks * 32 + g * 8) : f16x8{};
+            if constexpr (SPLIT) ql8[ks] = qok ? *(const f16x8*)(Qlg + (size_t)myq * DH + ks * 32 + g * 8) : f16x8{};
         }
     } else {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const float v = qok ? Qg[(size_t)myq * DH + g * 4 + e] : 0.f;
-            const f16 hv = (f16)v;
-            qh4[e] = hv;
-            ql4[e] = (f16)(v - (float)hv);
-        }
+        qh4 = qok ? *(const f16x4*)(Qhg + (size_t)myq * DH + g * 4) : f16x4{};
+        if constexpr (SPLIT) ql4 = qok ? *(const f16x4*)(Qlg + (size_t)myq * DH + g * 4) : f16x4{};
     }
 
-    // ---- staging of one key tile: K rows (fp32 -> LDS) and V^T rows
-    constexpr int KCH = KT * DH / 4;                 // float4 chunks of the K tile
+    // ---- staging of one key tile: K rows and V^T rows through registers
+    // (F32: fp32 K, 4-float chunks; 16-bit: fp16 hi/lo planes, 8-half chunks)
+    constexpr int KE = F32 ? 4 : 8;
+    constexpr int KCH = KT * DH / KE;
     constexpr int KPT = (KCH + 255) / 256;
     constexpr int VE = F32 ? 4 : 8;                  // V elements per 16-byte chunk
     constexpr int VCH = DH * KT / VE;
     constexpr int VPT = (VCH + 255) / 256;
-    float4 rk[KPT];
+    float4 rk[F32 ? KPT : 1];
+    uint4 rkh[F32 ? 1 : KPT], rkl[(!F32 && SPLIT) ? KPT : 1];
     uint4 rv[VPT];
 
     auto gload = [&](int k0) {
@@ -110,9 +114,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
         for (int i = 0; i < KPT; i++) {
             const int c = tid + i * 256;
             if (KCH % 256 != 0 && c >= KCH) break;
-            const int key = c / (DH / 4), col = (c % (DH / 4)) * 4;
-            rk[i] = (k0 + key < L) ? *(const float4*)(Kg + (size_t)(k0 + key) * DH + col)
-                                   : float4{0.f, 0.f, 0.f, 0.f};
+            const int key = c / (DH / KE), col = (c % (DH / KE)) * KE;
+            const bool ok = k0 + key < L;
+            if constexpr (F32) {
+                rk[i] = ok ? *(const float4*)(Kg + (size_t)(k0 + key) * DH + col) : float4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                rkh[i] = ok ? *(const uint4*)(Khg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
+                if constexpr (SPLIT) rkl[i] = ok ? *(const uint4*)(Klg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
+            }
         }
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
@@ -135,20 +144,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
         for (int i = 0; i < KPT; i++) {
             const int c = tid + i * 256;
             if (KCH % 256 != 0 && c >= KCH) break;
-            const int key = c / (DH / 4), col = (c % (DH / 4)) * 4;
-            const float v[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
+            const int key = c / (DH / KE), col = (c % (DH / KE)) * KE;
             if constexpr (F32) {
+                const float v[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) Ks[buf][key * KLD + col + e] = v[e];
             } else {
-                f16x4 hv, lv;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    hv[e] = (f16)v[e];
-                    lv[e] = (f16)(v[e] - (float)hv[e]);
-                }
-                *(f16x4*)&Ks[buf][key * KLD + col] = hv;
-                if constexpr (SPLIT) *(f16x4*)&Kls[buf][key * KLD + col] = lv;
+                *(uint4*)&Ks[buf][key * KLD + col] = rkh[i];
+                if constexpr (SPLIT) *(uint4*)&Kls[buf][key * KLD + col] = rkl[i];
             }
         }
 #pragma unroll
@@ -299,6 +302,177 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     }
 }
 
+// ---------------------------------------------------------------- LDS-DMA ring
+template <int DH, bool SPLIT>
+__global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
+    constexpr int KT = ATT_KT, ST = 3;
+    constexpr int KROW = DH * 2, KCH = KROW / 16;    // bytes and 16-byte chunks per K row
+    constexpr int KB = KT * KROW;                    // one K plane tile
+    constexpr int VB = DH * KT * 2;                  // V^T tile: DH rows of 64 keys (128 bytes)
+    constexpr int SB = KB * (SPLIT ? 2 : 1) + VB;    // bytes per ring stage
+    constexpr int NKD = KT * KCH / 256, NVD = DH * 8 / 256;   // DMA chunks per thread per plane
+    constexpr int NDMA = NKD * (SPLIT ? 2 : 1) + NVD;
+    constexpr int ND = DH / 16, QK = DH / 32;
+    static_assert(NKD >= 1 && NVD >= 1 && NKD * 256 == KT * KCH && NVD * 256 == DH * 8, "head dim 32 or 64");
+    static_assert(4 * 16 == ATT_BQ, "planner and kernel disagree on the query tile");
+    __shared__ __attribute__((aligned(16))) char lds[ST * SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // heaviest query tiles first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int L = p.L, Lp = p.Lp;
+    int len = p.lens[b];
+    len = len < 1 ? 1 : (len > L ? L : len);
+    const int q0 = qt * ATT_BQ, qw0 = q0 + 16 * wave;
+    const int kend = min(q0 + ATT_BQ, len);
+    const int ntiles = (kend + KT - 1) / KT;
+    const size_t bh = (size_t)b * p.H + h;
+    const f16* Qh = (const f16*)p.Q + bh * L * DH;
+    const f16* Ql = (const f16*)p.Ql + bh * L * DH;
+    const char* Khg = (const char*)((const f16*)p.K + bh * L * DH);
+    const char* Klg = (const char*)((const f16*)p.Kl + bh * L * DH);
+    const char* Vg = (const char*)((const f16*)p.Vt + bh * DH * Lp);
+
+    const int myq = qw0 + c16;
+    const bool qok = myq < L;
+    f16x8 qh[QK], ql[SPLIT ? QK : 1];
+#pragma unroll
+    for (int kk = 0; kk < QK; kk++) {
+        qh[kk] = qok ? *(const f16x8*)(Qh + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
+        if constexpr (SPLIT) ql[kk] = qok ? *(const f16x8*)(Ql + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
+    }
+
+    // Swizzle: chunk c of row r of a tile lives in slot c ^ (r % chunks-per-row).
+    // DMA lane writes slot q of the tile; it fetches the chunk that belongs there.
+    int krow[NKD], kchk[NKD], vrow[NVD], vchk[NVD];
+#pragma unroll
+    for (int i = 0; i < NKD; i++) {
+        const int q = i * 256 + tid;
+        krow[i] = q / KCH;
+        kchk[i] = (q % KCH) ^ (krow[i] % KCH);
+    }
+#pragma unroll
+    for (int i = 0; i < NVD; i++) {
+        const int q = i * 256 + tid;
+        vrow[i] = q >> 3;
+        vchk[i] = (q & 7) ^ (vrow[i] & 7);
+    }
+    auto issue = [&](int t, int buf) {
+        char* base = lds + buf * SB;
+        const int k0 = t * KT;
+#pragma unroll
+        for (int i = 0; i < NKD; i++) {
+            const size_t off = (size_t)min(k0 + krow[i], L - 1) * KROW + 16 * kchk[i];   // rows past L: copies
+            dma16(Khg + off, base + (i * 256 + wave * 64) * 16);
+            if constexpr (SPLIT) dma16(Klg + off, base + KB + (i * 256 + wave * 64) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < NVD; i++)
+            dma16(Vg + ((size_t)vrow[i] * Lp + k0) * 2 + 16 * vchk[i],
+                  base + KB * (SPLIT ? 2 : 1) + (i * 256 + wave * 64) * 16);
+    };
+
+    f32x4 o[ND];
+#pragma unroll
+    for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
+
+#pragma unroll
+    for (int s = 0; s < ST - 1; s++)
+        if (s < ntiles) issue(s, s);
+    for (int t = 0; t < ntiles; t++) {
+        if (t + ST - 2 < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST - 2) * NDMA) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // tile t visible; every wave is done with tile t - 1
+        if (t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
+        const int k0 = t * KT;
+        if (k0 > qw0 + 15) continue;  // this wave's queries all precede the tile
+        const char* ks = lds + (t % ST) * SB;
+        const char* kls = ks + KB;
+        const char* vs = ks + KB * (SPLIT ? 2 : 1);
+        // S^T = K Q^T; key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
+        f32x4 sc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
+#pragma unroll
+            for (int kk = 0; kk < QK; kk++) {
+                const int slot = ((kk * 4 + g) ^ (r % KCH)) * 16;
+                const f16x8 a = *(const f16x8*)(ks + r * KROW + slot);
+                sc[kb] = mfma_16x16x32(a, qh[kk], sc[kb]);
+                if constexpr (SPLIT) {
+                    const f16x8 al = *(const f16x8*)(kls + r * KROW + slot);
+                    sc[kb] = mfma_16x16x32(al, qh[kk], sc[kb]);
+                    sc[kb] = mfma_16x16x32(a, ql[kk], sc[kb]);
+                }
+            }
+        }
+        // running max on raw scores (scale > 0), then one FMA per score into exp2
+        const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float v = sc[kb][e];
+                if (need_mask) {
+                    const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
+                    if (key > myq || key >= len) v = -INFINITY;
+                }
+                sc[kb][e] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float pv = exp2f(fmaf(sc[kb][e], sl2, -m_use));
+                sc[kb][e] = pv;
+                ls += pv;
+            }
+        l_run = l_run * alpha + ls;
+#pragma unroll
+        for (int db = 0; db < ND; db++) o[db] *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < 2; cc++) {
+            f16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                pb[e] = (f16)sc[2 * cc][e];
+                pb[4 + e] = (f16)sc[2 * cc + 1][e];
+            }
+#pragma unroll
+            for (int db = 0; db < ND; db++) {
+                const int r = db * 16 + c16;
+                const f16x8 va = *(const f16x8*)(vs + r * (KT * 2) + (((cc * 4 + g) ^ (r & 7)) * 16));
+                o[db] = mfma_16x16x32(va, pb, o[db]);
+            }
+        }
+    }
+
+    l_run += __shfl_xor(l_run, 16, WAVE);
+    l_run += __shfl_xor(l_run, 32, WAVE);
+    if (!qok) return;
+    const float inv = 1.0f / l_run;
+    f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
+#pragma unroll
+    for (int db = 0; db < ND; db++)
+        *(f16x4*)(out + db * 16 + 4 * g) =
+            f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+}
+
 template <class OpT, int DH>
 static hipError_t attn_dh(bool split, const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
@@ -322,6 +496,14 @@ static hipError_t attn_mode(int dh, bool split, const AttnArgs& a, hipStream_t s
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s) {
     if (a.B <= 0 || a.L <= 0) return hipSuccess;
     if (m == MODE_F32) return attn_mode<float>(dh, false, a, s);
+    if (dh == 32 || dh == 64) {
+        dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
+        if (dh == 64 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, true>), grid, dim3(256), 0, s, a);
+        if (dh == 64 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, false>), grid, dim3(256), 0, s, a);
+        if (dh == 32 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, true>), grid, dim3(256), 0, s, a);
+        if (dh == 32 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, false>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     return attn_mode<f16>(dh, split_qk, a, s);
 }
 

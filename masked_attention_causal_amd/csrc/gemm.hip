@@ -163,12 +163,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
                     const int h = nn / p.dh, t = nn - h * p.dh;
                     const int b = m / p.L, pos = m - b * p.L;
                     const size_t bh = (size_t)b * p.H + h;
-                    if (which == 0)
-                        p.Q[(bh * p.L + pos) * p.dh + t] = v;
-                    else if (which == 1)
-                        p.Kd[(bh * p.L + pos) * p.dh + t] = v;
-                    else
+                    const size_t o = (bh * p.L + pos) * p.dh + t;
+                    if (which == 2) {
                         ((OpT*)p.Vt)[(bh * p.dh + t) * p.Lp + pos] = from_f32<OpT>(v);
+                    } else if constexpr (F32) {
+                        (which == 0 ? p.Q : p.Kd)[o] = v;
+                    } else {
+                        f16* dst = (f16*)(which == 0 ? p.Q : p.Kd);
+                        const f16 hv = (f16)v;
+                        dst[o] = hv;
+                        if (p.split) dst[(size_t)M * p.d + o] = (f16)(v - (float)hv);
+                    }
                 } else if constexpr (EPI == EPI_GELU) {
                     ((OpT*)p.out)[(size_t)m * N + n] = from_f32<OpT>(gelu_erf(v));
                 } else {

@@ -167,8 +167,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe_kernel(GemmArgs p) {
                 const int b = m / p.L, pos = m - b * p.L;
                 const size_t bh = (size_t)b * p.H + h;
                 if (which < 2) {
-                    float* dst = (which == 0 ? p.Q : p.Kd) + (bh * p.L + pos) * p.dh + t;
-                    *(float4*)dst = float4{v[0], v[1], v[2], v[3]};
+                    f16* dst = (f16*)(which == 0 ? p.Q : p.Kd) + (bh * p.L + pos) * p.dh + t;
+                    f16x4 hv, lv;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        hv[e] = (f16)v[e];
+                        lv[e] = (f16)(v[e] - (float)hv[e]);
+                    }
+                    *(f16x4*)dst = hv;
+                    if (p.split) *(f16x4*)(dst + (size_t)M * p.d) = lv;
                 } else {
                     f16* vt = (f16*)p.Vt + (bh * p.dh + t) * p.Lp + pos;
 #pragma unroll

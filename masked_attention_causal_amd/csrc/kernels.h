@@ -20,11 +20,15 @@ struct GemmArgs {
     const void* W;     // [N, K] weight dtype (nn.Linear layout)
     const void* bias;  // [N] weight dtype
     int M, N, K;
-    // EPI_QKV: N = 3d; writes Q, K [B, H, L, dh] fp32 and V^T [B, H, dh, Lp] operand dtype
+    // EPI_QKV: N = 3d; writes Q, K [B, H, L, dh] and V^T [B, H, dh, Lp] operand dtype.
+    // F32 mode: Q, K fp32.  16-bit modes: Q and K as fp16 planes of M*d
+    // elements each: the rounded value (hi) at Q / K and, when split != 0,
+    // the rounding remainder (lo) one plane further.
     float* Q;
     float* Kd;
     void* Vt;
     int L, Lp, H, dh, d;
+    int split;
     // EPI_GELU: out [M, N] operand dtype
     void* out;
     // EPI_RES: Z = acc + bias + R, [M, N] fp32
@@ -33,9 +37,11 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
-    const float* Q;    // [B, H, L, dh]
-    const float* K;    // [B, H, L, dh]
-    const void* Vt;    // [B, H, dh, Lp] operand dtype
+    const void* Q;     // [B, H, L, dh]: fp32 (F32 mode) or fp16 hi plane (16-bit modes)
+    const void* K;     // [B, H, L, dh], same
+    const void* Ql;    // 16-bit modes, first layer: fp16 lo planes of Q and K
+    const void* Kl;
+    const void* Vt;    // [B, H, dh, Lp] operand dtype; columns >= L hold zeros in 16-bit modes
     void* O;           // [B*L, d] operand dtype, head h at columns h*dh
     const int32_t* lens;
     int B, H, L, Lp, d;
@@ -93,6 +99,8 @@ constexpr int ATT_KT = 64;   // keys per attention tile
 constexpr int ATT_BQ = 64;   // queries per attention workgroup
 
 hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s);
+// Zeroes columns [L, Lp) of every V^T row (rows of Lp fp16).
+hipError_t launch_vt_pad(void* Vt, long rows, int L, int Lp, hipStream_t s);
 hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
 // Multi-stage LDS-DMA pipelined GEMM (16-bit operand modes, K % 64 == 0).
 bool gemm_pipe_ok(const GemmArgs& a);

@@ -152,4 +152,23 @@ hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStr
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- V^T padding
+// Columns [L, Lp) of the V^T rows are read as whole 64-key tiles by the
+// attention kernel's LDS-DMA; they must hold finite values (zeros), since
+// a zero softmax weight times a NaN would still be NaN.
+__global__ __launch_bounds__(256) void vt_pad_kernel(f16* __restrict__ Vt, long rows, int L, int Lp) {
+    const int pad = Lp - L;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * pad) return;
+    const long r = i / pad;
+    Vt[r * Lp + L + (i - r * pad)] = (f16)0.f;
+}
+
+hipError_t launch_vt_pad(void* Vt, long rows, int L, int Lp, hipStream_t s) {
+    const long n = rows * (Lp - L);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(vt_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (f16*)Vt, rows, L, Lp);
+    return hipGetLastError();
+}
+
 }  // namespace tfl

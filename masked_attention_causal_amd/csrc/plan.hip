@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdio>
 
+#include "common.h"
 #include "plan.h"
 
 namespace tfl {
@@ -184,6 +185,7 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
     {
         Timed tm(T, TFL_STAGE_PREP, s);
         e = tm.done(launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s));
+        if (e == hipSuccess && P.mode != MODE_F32) e = launch_vt_pad(Vt, (long)P.B * P.d, P.L, P.Lp, s);
     }
     if (e != hipSuccess) return e;
     for (int l = 0; l < P.n_layers; l++) {
@@ -194,6 +196,9 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         g.M = M; g.N = 3 * P.d; g.K = P.d;
         g.Q = Q; g.Kd = K; g.Vt = Vt;
         g.L = P.L; g.Lp = P.Lp; g.H = P.H; g.dh = P.dh; g.d = P.d;
+        // Scores of the first layer see the raw input (up to 1e3 in scale):
+        // fp32-accurate there; LayerNorm bounds every later layer's input.
+        g.split = l == 0;
         {
             Timed tm(T, TFL_STAGE_QKV, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_QKV, g, s))) != hipSuccess) return e;
@@ -201,10 +206,11 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
 
         AttnArgs a{};
         a.Q = Q; a.K = K; a.Vt = Vt; a.O = O; a.lens = lens;
+        // 16-bit modes: fp16 lo planes follow the hi planes in the same buffers
+        a.Ql = (const f16*)Q + (size_t)P.T * P.d;
+        a.Kl = (const f16*)K + (size_t)P.T * P.d;
         a.B = P.B; a.H = P.H; a.L = P.L; a.Lp = P.Lp; a.d = P.d;
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
-        // Scores of the first layer see the raw input (up to 1e3 in scale):
-        // fp32-accurate there; LayerNorm bounds every later layer's input.
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
             if ((e = tm.done(launch_attn(P.mode, P.dh, l == 0, a, s))) != hipSuccess) return e;
