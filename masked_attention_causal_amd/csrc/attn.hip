@@ -473,6 +473,140 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
             f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
 }
 
+// ---------------------------------------------------------------- head dim 16
+// With 16-dim heads the products are a small part of the work and the
+// softmax arithmetic dominates ("KernelForge", "Challenges": the 100k-token
+// shape), so this variant trims VALU work per score: 128-key tiles per
+// barrier (32 scores per lane), the scale folded into one FMA feeding the
+// hardware exp2, and the softmax row sums taken on the MFMA by a ones row
+// appended to V^T (the sum of the same fp16 weights that multiply V).
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
+    constexpr int DH = 16, KT = 128, ST = 3;
+    constexpr int KROW = DH * 2;                     // 32-byte K rows: two 16-byte chunks
+    constexpr int KB = KT * KROW;                    // 4 KB per K plane tile
+    constexpr int VROW = KT * 2;                     // 256-byte V^T rows: sixteen chunks
+    constexpr int VB = DH * VROW;
+    constexpr int SB = KB * (SPLIT ? 2 : 1) + VB;
+    constexpr int NDMA = (SPLIT ? 2 : 1) + 1;        // one K chunk per plane and one V^T chunk per thread
+    static_assert(KT * 2 == 256 && DH * 16 == 256, "one DMA chunk per thread per plane");
+    __shared__ __attribute__((aligned(16))) char lds[ST * SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int L = p.L, Lp = p.Lp;
+    int len = p.lens[b];
+    len = len < 1 ? 1 : (len > L ? L : len);
+    const int q0 = qt * ATT_BQ, qw0 = q0 + 16 * wave;
+    const int kend = min(q0 + ATT_BQ, len);
+    const int ntiles = (kend + KT - 1) / KT;
+    const size_t bh = (size_t)b * p.H + h;
+    const f16* Qh = (const f16*)p.Q + bh * L * DH;
+    const f16* Ql = (const f16*)p.Ql + bh * L * DH;
+    const char* Khg = (const char*)((const f16*)p.K + bh * L * DH);
+    const char* Klg = (const char*)((const f16*)p.Kl + bh * L * DH);
+    const char* Vg = (const char*)((const f16*)p.Vt + bh * DH * Lp);
+
+    const int myq = qw0 + c16;
+    const bool qok = myq < L;
+    const f16x4 qh = qok ? *(const f16x4*)(Qh + (size_t)myq * DH + 4 * g) : f16x4{};
+    const f16x4 ql = (SPLIT && qok) ? *(const f16x4*)(Ql + (size_t)myq * DH + 4 * g) : f16x4{};
+
+    // DMA: thread tid fetches K row tid >> 1 (chunk slot tid & 1) and V^T row
+    // tid >> 4 (chunk slot tid & 15); chunk c of row r sits in slot c ^ (r mod chunks).
+    const int krow = tid >> 1, kchk = (tid & 1) ^ (krow & 1);
+    const int vrow = tid >> 4, vchk = (tid & 15) ^ (vrow & 15);
+    auto issue = [&](int t, int buf) {
+        char* base = lds + buf * SB;
+        const int k0 = t * KT;
+        const size_t off = (size_t)min(k0 + krow, L - 1) * KROW + 16 * kchk;   // rows past L: copies
+        dma16(Khg + off, base + wave * 64 * 16);
+        if constexpr (SPLIT) dma16(Klg + off, base + KB + wave * 64 * 16);
+        dma16(Vg + ((size_t)vrow * Lp + k0) * 2 + 16 * vchk, base + KB * (SPLIT ? 2 : 1) + wave * 64 * 16);
+    };
+
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};          // row 0 of (ones . P^T): the weight sums
+    const f16 one = (f16)(c16 == 0 ? 1.0f : 0.0f);
+    const f16x8 ones = {one, one, one, one, one, one, one, one};
+    float m_run = -INFINITY;
+    const float sl2 = p.scale_log2;
+
+#pragma unroll
+    for (int s = 0; s < ST - 1; s++)
+        if (s < ntiles) issue(s, s);
+    for (int t = 0; t < ntiles; t++) {
+        if (t + ST - 2 < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST - 2) * NDMA) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
+        const int k0 = t * KT;
+        if (k0 > qw0 + 15) continue;
+        const char* ks = lds + (t % ST) * SB;
+        const char* kls = ks + KB;
+        const char* vs = ks + KB * (SPLIT ? 2 : 1);
+        // key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
+        f32x4 sc[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++) {
+            const int r = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
+            const int off = r * KROW + (((g >> 1) ^ (r & 1)) * 16) + (g & 1) * 8;
+            const f16x4 a = *(const f16x4*)(ks + off);
+            sc[kb] = mfma_16x16x16(a, qh, f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (SPLIT) {
+                sc[kb] = mfma_16x16x16(*(const f16x4*)(kls + off), qh, sc[kb]);
+                sc[kb] = mfma_16x16x16(a, ql, sc[kb]);
+            }
+        }
+        const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
+                    if (key > myq || key >= len) sc[kb][e] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++)
+            mx = fmaxf(fmaxf(mx, fmaxf(sc[kb][0], sc[kb][1])), fmaxf(sc[kb][2], sc[kb][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        o *= alpha;
+        lsum *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) {
+            f16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                pb[e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc][e], sl2, -m_use));
+                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc + 1][e], sl2, -m_use));
+            }
+            const int r = c16;
+            const f16x8 va = *(const f16x8*)(vs + r * VROW + (((cc * 4 + g) ^ (r & 15)) * 16));
+            o = mfma_16x16x32(va, pb, o);
+            lsum = mfma_16x16x32(ones, pb, lsum);
+        }
+    }
+
+    // lsum row 0 (lanes 0..15, element 0) holds the weight sum of query c16
+    const float l = __shfl(lsum[0], c16, WAVE);
+    if (!qok) return;
+    const float inv = 1.0f / l;
+    f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
+    *(f16x4*)(out + 4 * g) = f16x4{(f16)(o[0] * inv), (f16)(o[1] * inv), (f16)(o[2] * inv), (f16)(o[3] * inv)};
+}
+
 template <class OpT, int DH>
 static hipError_t attn_dh(bool split, const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
@@ -502,6 +636,14 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
         if (dh == 64 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, false>), grid, dim3(256), 0, s, a);
         if (dh == 32 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, true>), grid, dim3(256), 0, s, a);
         if (dh == 32 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, false>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (dh == 16) {   // the plan pads V^T rows to whole 128-key tiles
+        dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
+        if (split_qk)
+            hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
     return attn_mode<f16>(dh, split_qk, a, s);

@@ -135,6 +135,9 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         *p = q;
         return TFL_OK;
     }
+    // V^T rows are padded to whole 128-key tiles (the head-dim-16 attention
+    // kernel reads 128 keys per tile).
+    q.Lp = (c.seq_len + 127) / 128 * 128;
     size_t o = 0;
     q.off_Xr = o; o += up256(Td * 4);
     q.off_X1 = o; o += up256(Td * 4);

@@ -87,7 +87,7 @@ def test_workspace_covers_the_tiled_buffers():
     w = synth.WORKLOADS["stream_d64_b1_l100000"]
     _, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
     T = w.B * w.L
-    Lp = (w.L + 63) // 64 * 64
+    Lp = (w.L + 127) // 128 * 128          # V^T rows padded to whole 128-key tiles
     need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2
     assert need <= ws <= need + 9 * 256
 
