@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtfl.so")
 
-SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "gemm_pipe.hip", "attn.hip", "ln.hip", "seq.hip",
+SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "gemm_pipe.hip", "attn.hip", "ln.hip", "seq.hip", "seq_small.hip",
            "pq.hip", "pq_f32.hip", "pq_f16.hip", "pq_bf16.hip"]
 ARCH = "gfx950"
 FLAGS = [

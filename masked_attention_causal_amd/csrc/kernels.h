@@ -110,6 +110,10 @@ hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta
                      int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);
 
 hipError_t launch_seq(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
+// Sequence-resident path for small shapes: one workgroup per sequence, fp32
+// VALU arithmetic, any I/O dtype.
+bool seq_small_supported(int d, int dh, int f, int L, int n_layers);
+hipError_t launch_seq_small(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
 bool pq_supported(Mode m, int d, int dh, int f, int n_layers);
 // single_launch: one persistent launch that resolves dependencies with
 // counters; otherwise one launch per stage (QKV0, then ATT and ROW per layer).

@@ -29,6 +29,8 @@ int choose_path(const tfl_config& c) {
     // Short sequences: one workgroup keeps two whole sequences on chip for the
     // whole stack (one launch, no intermediate HBM traffic).
     if (seq_supported(m, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
+    // Tiny widths: one workgroup per sequence, one launch for the stack.
+    if (seq_small_supported(c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
     // Few long sequences: fewer (sequence, head, 64-query tile) units than
     // compute units, so per-stage launches leave most of the chip idle; one
     // persistent launch with split-K attention tasks fills it instead.
@@ -78,7 +80,8 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     int path = c.force_path == TFL_PATH_AUTO ? choose_path(c) : c.force_path;
     const Mode mode = mode_of(c.dtype);
     if ((path == TFL_PATH_PQ && !pq_supported(mode, c.d_model, dh, c.d_ffn, c.n_layers)) ||
-        (path == TFL_PATH_SEQ && !seq_supported(mode, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers))) {
+        (path == TFL_PATH_SEQ && !seq_supported(mode, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers) &&
+         !seq_small_supported(c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers))) {
         *why = "requested path is not available for this shape";
         return TFL_E_UNSUPPORTED;
     }
@@ -98,7 +101,11 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     q.op = q.mode == MODE_F32 ? 4 : 2;
     if (path == TFL_PATH_SEQ) {
         q.ws_bytes = 0;  // everything stays on chip
-        std::snprintf(q.name, sizeof(q.name), "SEQ/2x64tok/w8/f16op");
+        q.seq_kind = seq_supported(mode, c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers) ? 0 : 1;
+        if (q.seq_kind == 0)
+            std::snprintf(q.name, sizeof(q.name), "SEQ/2x64tok/w8/f16op");
+        else
+            std::snprintf(q.name, sizeof(q.name), "SEQ/small/1seq/f32");
         *p = q;
         return TFL_OK;
     }
@@ -273,6 +280,7 @@ static hipError_t run_seq(const Plan& P, const tfl_layer* layers, const void* x,
                             w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
     }
     Timed tm(T, TFL_STAGE_FUSED, s);
+    if (P.seq_kind == 1) return tm.done(launch_seq_small(P.mode, P.d, P.dh, a, s));
     return tm.done(launch_seq(P.mode, P.d, P.dh, a, s));
 }
 

@@ -50,8 +50,12 @@ def test_dispatcher_rules():
     with pytest.raises(tfl.TflError) as e:
         tfl.plan_for(2, 256, 4, 1024, 4, 128, "f16", force_path="seq")
     assert e.value.status == 2
+    # tiny widths (d <= 64, L <= 64): the small sequence-resident kernel, any dtype
+    assert tfl.plan_for(2, 32, 2, 128, 4, 32, "f32") == ("SEQ/small/1seq/f32", "seq", 0)
+    assert tfl.plan_for(2, 64, 4, 256, 4, 32, "f32", force_path="seq")[1] == "seq"
+    assert tfl.plan_for(2, 32, 2, 128, 4, 65, "f32")[1] == "tiled"
     with pytest.raises(tfl.TflError):
-        tfl.plan_for(2, 64, 4, 256, 4, 32, "f32", force_path="seq")
+        tfl.plan_for(2, 128, 2, 512, 4, 64, "f32", force_path="seq")
 
 
 def test_pq_dispatch_rules():
@@ -119,7 +123,7 @@ def test_create_rejects_bad_layer_pointers(lib):
 
 
 def test_forward_argument_checks_before_any_device_call(lib):
-    cfg = tfl.make_config(1, 64, 4, 128, 2, 16, "f16")
+    cfg = tfl.make_config(1, 64, 4, 128, 2, 16, "f16", force_path="tiled")   # a plan with a workspace
     h = tfl.Handle(cfg, [{k: 0x10000 for k in tfl.LAYER_KEYS}])
     n = h.workspace_bytes
     X, Y, LN, WS = 0x100000, 0x200000, 0x300000, 0x400000

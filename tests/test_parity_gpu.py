@@ -122,6 +122,30 @@ def test_stream_workload_prefix_and_golden_rows():
     assert_gate(y[0, rows], ref, "stream golden rows")
 
 
+# ---------------------------------------------------------------- small-shape sequence-resident kernel
+
+SMALL_SEQ = [
+    W("t_f32_d32_dh16", 2, 32, 2, 128, 4, 32, "f32", 1, 32, 1.0),
+    W("t_f32_d64_dh64", 2, 64, 1, 128, 2, 32, "f32", 1, 32, 1.0),
+    W("t_bf16_d32_dh32", 3, 32, 1, 64, 3, 50, "bf16", 1, 50, 1.0),
+    W("t_f16_d32_dh16", 1, 32, 2, 96, 6, 64, "f16", 1, 64, 1.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_SEQ, ids=lambda w: w.name)
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+def test_small_sequence_resident(w, scale):
+    import masked_attention_causal_amd as tfl
+    plan, path, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype)
+    assert (path, ws) == ("seq", 0) and "small" in plan, plan
+    for seed in (0, 1):
+        inp = _case(w, seed, scale, affine=(seed == 1))
+        inp.lens[0] = w.L
+        inp.lens[1] = 1
+        say(f"[seq-small] {w.name} seed={seed} scale={scale} lens={inp.lens.tolist()}")
+        assert_gate(gpu_forward(inp), oracle_forward(inp), f"{w.name} seed {seed} scale {scale}")
+
+
 # ---------------------------------------------------------------- pipelined GEMM tiles
 
 PIPE = [
