@@ -72,25 +72,44 @@ def stage_work(w, stage, lens):
 
 STAGES_TILED = ("prep", "qkv", "attn", "out", "ln", "ffn1", "ffn2")
 
-# Kernel sources behind each stage: a traffic figure taken with rocprofv3 is
-# used only while these files are unchanged.
-STAGE_KERNEL = {"fused": ("seq_kernel", ("seq.hip", "common.h", "kernels.h")),
-                "attn": ("attn_kernel", ("attn.hip", "common.h", "kernels.h")),
-                "qkv": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
-                "out": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
-                "ffn1": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
-                "ffn2": ("gemm_kernel", ("gemm.hip", "common.h", "kernels.h")),
-                "ln": ("ln_kernel", ("ln.hip", "common.h", "kernels.h")),
-                "prep": ("prep_kernel", ("ln.hip", "common.h", "kernels.h"))}
+def arith_dtype(plan):
+    """Operand type the plan's products are computed in (fp16 operands with
+    fp32 accumulation, or fp32 throughout)."""
+    return "f16" if "f16op" in plan else "f32"
 
 
-def measured_traffic(stage, workload):
+def stage_kernel(stage, plan, w):
+    """(kernel name, source files) behind a stage of a plan.  A traffic figure
+    taken with rocprofv3 is used only while these files are unchanged."""
+    base = ("common.h", "kernels.h")
+    if stage == "fused":
+        if plan.startswith("SEQ/small"):
+            return "seq_small_kernel", ("seq_small.hip",) + base
+        if plan.startswith("SEQ"):
+            return "seq_kernel", ("seq.hip",) + base
+        return "pq_stage_kernel", ("pq_impl.h", "pq.hip") + base
+    if stage == "attn":
+        if arith_dtype(plan) == "f32":
+            return "attn_kernel", ("attn.hip",) + base
+        return ("attn_ring16_kernel" if w.dh == 16 else "attn_ring_kernel"), ("attn.hip",) + base
+    if stage in ("qkv", "out", "ffn1", "ffn2"):
+        if arith_dtype(plan) == "f32":
+            return "gemm_kernel", ("gemm.hip",) + base
+        return "gemm_pipe_kernel", ("gemm_pipe.hip", "gemm.hip") + base
+    if stage == "ln":
+        return "ln_kernel", ("ln.hip",) + base
+    if stage == "prep":
+        return "prep_kernel", ("ln.hip",) + base
+    return None, ()
+
+
+def measured_traffic(stage, workload, plan, w):
     """HBM bytes per launch recorded in profiles/*.md for this kernel and
     workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
     kernel's sources changed since the counters were taken."""
     import glob
     import hashlib
-    kern, files = STAGE_KERNEL.get(stage, (None, ()))
+    kern, files = stage_kernel(stage, plan, w)
     if kern is None:
         return None
     h = hashlib.sha256()
@@ -114,14 +133,14 @@ def launches_per_forward(stage, n_layers):
     return {"prep": 1, "ln": 2 * n_layers, "fused": 1}.get(stage, n_layers)
 
 
-def roofline(w, stage, lens, avg_ms):
+def roofline(w, stage, lens, avg_ms, plan):
     flops, nbytes = stage_work(w, stage, lens)
-    t_mfma = flops / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+    peak = PEAK_MFMA_TFLOPS[arith_dtype(plan)]
+    t_mfma = flops / (peak * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     sec = avg_ms / 1e3
     if t_mfma >= t_hbm:
         ach = flops / sec / 1e12
-        peak = PEAK_MFMA_TFLOPS[w.dtype]
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": None, "kernel_stage": stage,
                 "avg_launch_us": round(avg_ms * 1e3, 2), "algorithmic_flops_per_launch": flops,
@@ -236,9 +255,10 @@ def main():
     dom_ms, dom_n = h.timer_read()
     ms_step = total_ms / args.steps
     seqs = w.B / (ms_step / 1e3)
-    roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1))
+    roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1), enc.plan_name)
+    roof["kernel"] = stage_kernel(dom, enc.plan_name, w)[0]
     roof["launches_timed"] = dom_n
-    roof["traffic"] = measured_traffic(dom, name)
+    roof["traffic"] = measured_traffic(dom, name, enc.plan_name, w)
 
     # whole-forward roofline figure for context
     tot_flops = 0.0
@@ -259,9 +279,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": arith_dtype(enc.plan_name),
         "data": "synthetic (seeded normals, weights N(0,0.02^2), random valid lengths)",
-        "config": {"workload": name, "n_layers": w.n_layers, "d_model": w.d, "n_heads": w.H, "d_ffn": w.f,
+        "config": {"workload": name, "io_dtype": w.dtype, "n_layers": w.n_layers, "d_model": w.d, "n_heads": w.H, "d_ffn": w.f,
                    "batch": w.B, "seq_len": w.L, "valid_len": [w.len_lo, w.len_hi],
                    "input_scale": round(inp.scale, 6), "seed": args.seed, "plan": enc.plan_name,
                    "parallelism": "single GPU"},
