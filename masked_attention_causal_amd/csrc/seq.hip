@@ -25,7 +25,9 @@
 // thus pass from one product to the next register to register.
 //
 // Attention (keys j <= i and j < len_b, "KernelForge", "What we built") is
-// computed per head: K and V^T of both sequences go to LDS, each wave forms
+// computed per head: K and V^T of both sequences go to LDS (their rows
+// stored in the same sigma32 order as the weight tiles, so a fragment read
+// is a plain row read), each wave forms
 // S^T = K Q^T for its queries over at most 64 keys, a plain (not online)
 // softmax over the row, and O^T = V^T P^T, which is again a B operand of
 // the out-projection.  Key chunks past the wave's last query or past len_b
@@ -35,6 +37,11 @@
 // from global memory straight into LDS with 16-byte global_load_lds, one
 // tile ahead of the MFMAs; bf16 weight tiles go through registers to be
 // widened to fp16.
+//
+// LDS rows are padded to an odd multiple of 32 bytes (16 halves past a
+// multiple of 64): a 16-row x 16-byte fragment read then touches every bank
+// the same number of times.  A 16-byte pad (the usual choice elsewhere)
+// leaves half the reads taking two passes on this LDS.
 //
 // Precision matches the tiled path: fp32 residual and LayerNorm, fp16
 // operands with fp32 accumulation, first-layer scores from a hi/lo fp16
@@ -55,6 +62,24 @@ constexpr int SEQ_WPS = SEQ_SLOT / (16 * TPW);  // waves per sequence slot
 constexpr int SEQ_MAX_F = 4096;   // largest FFN width of the SEQ path
 constexpr int FCH = 64;        // FFN width per chunk
 
+constexpr int SEQ_PAD = 16;     // LDS row padding (halves)
+constexpr int SEQ_LDS_MAX = 160 * 1024;
+
+// Largest staged weight tile (halves), rows padded by SEQ_PAD:
+//   Q/K/V rows of one head DH x D, W_o columns of one head D x DH,
+//   W_1 rows of one chunk FCH x D, W_2 columns of one chunk D x FCH.
+constexpr int seq_tbuf(int D, int DH) {
+    const int t1 = DH * (D + SEQ_PAD) > D * (DH + SEQ_PAD) ? DH * (D + SEQ_PAD) : D * (DH + SEQ_PAD);
+    const int t2 = FCH * (D + SEQ_PAD) > D * (FCH + SEQ_PAD) ? FCH * (D + SEQ_PAD) : D * (FCH + SEQ_PAD);
+    return t1 > t2 ? t1 : t2;
+}
+// Static LDS of the kernel (bytes): two weight tiles, K hi/lo, V^T.
+constexpr int seq_static_lds(int D, int DH) {
+    return 2 * seq_tbuf(D, DH) * 2 + 2 * SEQ_TOK * (DH + SEQ_PAD) * 2 + DH * (SEQ_TOK + SEQ_PAD) * 2;
+}
+// Dynamic LDS (bytes): per-layer vectors, double-buffered by layer parity.
+inline size_t seq_param_lds(int d, int f, size_t elem) { return 2 * (size_t)(((9 * d + f) + 7) & ~7) * elem; }
+
 struct TileDesc {
     int kind;  // 0 Q, 1 K, 2 V rows of a head, 3 W_o columns of a head, 4 W_1 chunk, 5 W_2 chunk
     int layer, h, kc, fc;
@@ -67,6 +92,9 @@ __device__ __forceinline__ f16x8 pack8(f32x4 a, f32x4 b) {
 // Row permutation applied within every 32-row group of a staged tile: LDS
 // row 16h + 4g + e holds source row 8g + 4h + e.
 __device__ __forceinline__ int sigma32(int r) { return 8 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3); }
+
+// Inverse of sigma32: the LDS row that holds source row k of a 32-row group.
+__device__ __forceinline__ int sigma32_inv(int k) { return (k & 3) | ((k >> 3) << 2) | (((k >> 2) & 1) << 4); }
 
 // Natural feature held by element e of result block `blk` in lane group g
 // (after the sigma32 row gather): 4 consecutive features per block.
@@ -118,14 +146,13 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     constexpr int NQB = DH / 16;  // blocks per head
     constexpr int NHC = DH / 32;  // 32-wide K chunks over the head dim
     constexpr int NCB = NQB > FCH / 16 ? NQB : FCH / 16;  // carried blocks (Q of a head, or a GELU chunk)
-    constexpr int KLD = DH + 8;               // K rows in LDS
-    constexpr int VLD = SEQ_TOK + 8;          // V^T rows in LDS
-    // Staged weight tiles, rows padded by 8 halves and sigma32-gathered:
+    constexpr int PAD = SEQ_PAD;
+    constexpr int KLD = DH + PAD;             // K rows in LDS
+    constexpr int VLD = SEQ_TOK + PAD;        // V^T rows in LDS
+    // Staged weight tiles, rows padded by PAD halves and sigma32-gathered:
     //   kinds 0-2: Q/K/V rows of one head, DH x D;  3: W_o columns of one head, D x DH;
     //   4: W_1 rows of one chunk, FCH x D;          5: W_2 columns of one chunk, D x FCH.
-    constexpr int T1 = DH * (D + 8) > D * (DH + 8) ? DH * (D + 8) : D * (DH + 8);
-    constexpr int T2 = FCH * (D + 8) > D * (FCH + 8) ? FCH * (D + 8) : D * (FCH + 8);
-    constexpr int TBUF = T1 > T2 ? T1 : T2;
+    constexpr int TBUF = seq_tbuf(D, DH);
     constexpr int MAXCH = (TBUF / 8 + SEQ_THREADS - 1) / SEQ_THREADS;  // 16-byte chunks per thread
     static_assert(D % 32 == 0 && DH % 32 == 0 && D % DH == 0, "unsupported SEQ shape");
 
@@ -134,6 +161,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     __shared__ __attribute__((aligned(16))) f16 Kh[SEQ_TOK * KLD];
     __shared__ __attribute__((aligned(16))) f16 Kl[SEQ_TOK * KLD];
     __shared__ __attribute__((aligned(16))) f16 Vt[DH * VLD];
+    static_assert(seq_static_lds(D, DH) == (2 * TBUF + 2 * SEQ_TOK * KLD + DH * VLD) * 2, "LDS accounting");
     // Small per-layer vectors, raw I/O-dtype bits, double-buffered by layer
     // parity: b_qkv | b_o | ln1_g | ln1_b | b_1 | b_2 | ln2_g | ln2_b.
     constexpr int P_BQKV = 0, P_BO = 3 * D, P_G1 = 4 * D, P_BE1 = 5 * D, P_B1 = 6 * D;
@@ -208,61 +236,59 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
         }
         return d;
     };
-    // Row r of a tile starts at base + r * rstride (elements); cols elements per row.
-    struct Geom {
-        const WT* base;
-        long rstride;
-        int rows, cols;
-    };
-    auto geom = [&](const TileDesc& d) {
+    // Geometry of a tile, passed to fn as compile-time rows and columns of the
+    // staged image plus the global base and row stride (elements), so the
+    // per-lane chunk -> (row, column) split below divides by constants.
+    auto with_geom = [&](int t, auto&& fn) {
+        const TileDesc d = describe(t);
         const LayerPtrs& w = p.lw[d.layer];
-        Geom q;
-        if (d.kind <= 2) {
-            q.base = (const WT*)w.w_qkv + (size_t)(d.kind * D + d.h * DH) * D;
-            q.rstride = D; q.rows = DH; q.cols = D;
-        } else if (d.kind == 3) {
-            q.base = (const WT*)w.w_o + d.h * DH;
-            q.rstride = D; q.rows = D; q.cols = DH;
-        } else if (d.kind == 4) {
-            q.base = (const WT*)w.w_1 + (size_t)d.fc * FCH * D;
-            q.rstride = D; q.rows = FCH; q.cols = D;
-        } else {
-            q.base = (const WT*)w.w_2 + d.fc * FCH;
-            q.rstride = F; q.rows = D; q.cols = FCH;
-        }
-        return q;
+        if (d.kind <= 2)
+            fn(std::integral_constant<int, DH>{}, std::integral_constant<int, D>{},
+               (const WT*)w.w_qkv + (size_t)(d.kind * D + d.h * DH) * D, D);
+        else if (d.kind == 3)
+            fn(std::integral_constant<int, D>{}, std::integral_constant<int, DH>{}, (const WT*)w.w_o + d.h * DH, D);
+        else if (d.kind == 4)
+            fn(std::integral_constant<int, FCH>{}, std::integral_constant<int, D>{},
+               (const WT*)w.w_1 + (size_t)d.fc * FCH * D, D);
+        else
+            fn(std::integral_constant<int, D>{}, std::integral_constant<int, FCH>{}, (const WT*)w.w_2 + d.fc * FCH, F);
     };
 
     // Every 16-byte chunk of the padded, row-gathered LDS image of a tile;
-    // pad chunks re-read the row's first chunk.
+    // pad chunks re-read the row's first chunk.  Chunk c of the image is
+    // loaded by thread c mod 512 (the DMA destination of a lane is fixed).
     uint4 stg[DIRECT ? 1 : MAXCH];
     auto tile_fetch = [&](int t, f16* buf) {
-        const Geom q = geom(describe(t));
-        const int cpr = q.cols / 8, cpp = cpr + 1, n = q.rows * cpp;
-#pragma unroll
-        for (int i = 0; i < MAXCH; i++) {
-            const int c = tid + i * SEQ_THREADS;
-            if (c < n) {
-                const int r = c / cpp, k8 = c - r * cpp;
-                const int gr = (r & ~31) + sigma32(r & 31);
-                const WT* src = q.base + gr * q.rstride + (k8 < cpr ? k8 : 0) * 8;
-                if constexpr (DIRECT) {
-                    dma16(src, buf + (i * SEQ_THREADS + wave * 64) * 8);
-                } else {
-                    stg[i] = *(const uint4*)src;
-                }
-            }
-        }
-    };
-    auto tile_commit = [&](int t, f16* buf) {
-        if constexpr (!DIRECT) {
-            const Geom q = geom(describe(t));
-            const int cpp = q.cols / 8 + 1, n = q.rows * cpp;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        with_geom(t, [&](auto R, auto C, const WT* base, int rstride) {
+            constexpr int ROWS = decltype(R)::value, CPR = decltype(C)::value / 8, CPP = CPR + PAD / 8;
+            constexpr int N = ROWS * CPP;
 #pragma unroll
             for (int i = 0; i < MAXCH; i++) {
                 const int c = tid + i * SEQ_THREADS;
-                if (c < n) *(f16x8*)&buf[c * 8] = load8_as_f16((const WT*)&stg[i]);
+                if (i * SEQ_THREADS < N && c < N) {
+                    const int r = c / CPP, k8 = c - r * CPP;
+                    const int gr = (r & ~31) + sigma32(r & 31);
+                    const WT* src = base + (gr * rstride + (k8 < CPR ? k8 : 0) * 8);
+                    if constexpr (DIRECT) {
+                        dma16(src, buf + (i * SEQ_THREADS + wv * 64) * 8);
+                    } else {
+                        stg[i] = *(const uint4*)src;
+                    }
+                }
             }
+        });
+    };
+    auto tile_commit = [&](int t, f16* buf) {
+        if constexpr (!DIRECT) {
+            with_geom(t, [&](auto R, auto C, const WT*, int) {
+                constexpr int N = decltype(R)::value * (decltype(C)::value / 8 + PAD / 8);
+#pragma unroll
+                for (int i = 0; i < MAXCH; i++) {
+                    const int c = tid + i * SEQ_THREADS;
+                    if (i * SEQ_THREADS < N && c < N) *(f16x8*)&buf[c * 8] = load8_as_f16((const WT*)&stg[i]);
+                }
+            });
         }
         // direct loads of the tile and of the vectors land before the barrier
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -327,7 +353,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 
         if (d.kind <= 2) {
             // ---- Q^T, K^T or V^T of head h: [DH x tokens] = W rows . X^T
-            constexpr int ldw = D + 8;
+            constexpr int ldw = D + PAD;
             f32x4 acc[NQB][TPW];
             const WT* bq = P + P_BQKV + d.kind * D + d.h * DH;
 #pragma unroll
@@ -353,7 +379,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             } else if (d.kind == 1) {
 #pragma unroll
                 for (int tb = 0; tb < TPW; tb++) {
-                    const int tok = sq * SEQ_SLOT + q0 + tb * 16 + c16;
+                    const int key = sq * SEQ_SLOT + q0 + tb * 16 + c16;
+                    const int tok = (key & ~31) + sigma32_inv(key & 31);  // LDS row of this key
 #pragma unroll
                     for (int kb = 0; kb < NQB; kb++) {
                         f16x4 hv, lv;
@@ -373,7 +400,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 #pragma unroll
                     for (int vb = 0; vb < NQB; vb++)
 #pragma unroll
-                        for (int e = 0; e < 4; e++) Vt[(feat4(vb, g) + e) * VLD + tok] = (f16)acc[vb][tb][e];
+                        // feature feat4(vb, g) + e sits in LDS row sigma32_inv of it: vb * 16 + 4g + e
+                        for (int e = 0; e < 4; e++) Vt[(vb * 16 + 4 * g + e) * VLD + tok] = (f16)acc[vb][tb][e];
                 }
             }
         } else if (d.kind == 3) {
@@ -415,7 +443,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int hb = 0; hb < 2; hb++) {
 #pragma unroll
                         for (int tb = 0; tb < TPW; tb++) s[hb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        const int krow = kbase + cc * 32 + sigma32(hb * 16 + c16);
+                        const int krow = kbase + cc * 32 + hb * 16 + c16;  // holds key sigma32(hb * 16 + c16)
 #pragma unroll
                         for (int kk = 0; kk < NHC; kk++) {
                             const f16x8 a = afrag(Kh, KLD, krow, kk * 32, g);
@@ -465,7 +493,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     }
 #pragma unroll
                     for (int db = 0; db < NQB; db++) {
-                        const int vrow = (db >> 1) * 32 + sigma32((db & 1) * 16 + c16);
+                        const int vrow = db * 16 + c16;  // holds feature (db >> 1) * 32 + sigma32((db & 1) * 16 + c16)
                         const f16x8 va = afrag(Vt, VLD, vrow, kbase + cc * 32, g);
 #pragma unroll
                         for (int tb = 0; tb < TPW; tb++) o[db][tb] = mfma_16x16x32(va, pack8(s[0][tb], s[1][tb]), o[db][tb]);
@@ -492,7 +520,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
                 }
             }
-            constexpr int ldw = DH + 8;
+            constexpr int ldw = DH + PAD;
 #pragma unroll
             for (int db = 0; db < NDB; db++)
 #pragma unroll
@@ -504,7 +532,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             pipeline_order<NDB * NHC, NDB * NHC * TPW, TPW, SEQ_AHEAD>();
         } else if (d.kind == 4) {
             // ---- FFN up-projection chunk + GELU, carried to the next tile
-            constexpr int ldw = D + 8;
+            constexpr int ldw = D + PAD;
 #pragma unroll
             for (int ob = 0; ob < FCH / 16; ob++) {
                 const f32x4 bv = load4(P + P_B1 + d.fc * FCH + feat4(ob, g));
@@ -536,7 +564,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
                 }
             }
-            constexpr int ldw = FCH + 8;
+            constexpr int ldw = FCH + PAD;
             f16x8 gb[FCH / 32][TPW];
 #pragma unroll
             for (int kk = 0; kk < FCH / 32; kk++)
@@ -603,14 +631,16 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 
 bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers) {
     if (m == MODE_F32 || L > SEQ_SLOT || f % FCH != 0 || f > SEQ_MAX_F || n_layers > SEQ_MAX_LAYERS) return false;
-    return (d == 256 && dh == 64) || (d == 256 && dh == 32) || (d == 128 && dh == 64) || (d == 128 && dh == 32) ||
-           (d == 64 && dh == 64) || (d == 64 && dh == 32);
+    const bool shape = (d == 256 && dh == 64) || (d == 256 && dh == 32) || (d == 128 && dh == 64) ||
+                       (d == 128 && dh == 32) || (d == 64 && dh == 64) || (d == 64 && dh == 32);
+    // the per-layer vectors (dynamic LDS) must fit beside the static tiles
+    return shape && seq_static_lds(d, dh) + seq_param_lds(d, f, 2) <= (size_t)SEQ_LDS_MAX;
 }
 
 template <class WT>
 static hipError_t seq_mode(int d, int dh, const SeqArgs& a, hipStream_t s) {
     dim3 grid((a.B + SEQ_SEQS - 1) / SEQ_SEQS);
-    const size_t pbytes = 2 * (size_t)(((9 * d + a.F) + 7) & ~7) * sizeof(WT);
+    const size_t pbytes = seq_param_lds(d, a.F, sizeof(WT));
 #define TFL_SEQ_CASE(DD, HH)                                                                    \
     if (d == DD && dh == HH) {                                                                  \
         hipLaunchKernelGGL((seq_kernel<WT, DD, HH>), grid, dim3(SEQ_THREADS), pbytes, s, a);   \
