@@ -88,6 +88,12 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
     const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_f16*)lds_wave_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
 }
+// The same with a wave-uniform base address (SGPRs) and a per-lane 32-bit
+// byte offset, so a run of loads from one base differs only in scalar adds.
+__device__ __forceinline__ void dma16s(const void* sbase, unsigned voff, void* lds_wave_base) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_f16*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // ---------------------------------------------------------------- wave reductions

@@ -38,10 +38,12 @@
 // tile ahead of the MFMAs; bf16 weight tiles go through registers to be
 // widened to fp16.
 //
-// LDS rows are padded to an odd multiple of 32 bytes (16 halves past a
-// multiple of 64): a 16-row x 16-byte fragment read then touches every bank
-// the same number of times.  A 16-byte pad (the usual choice elsewhere)
-// leaves half the reads taking two passes on this LDS.
+// LDS images (weight tiles, K, V^T) are unpadded rows of 16-byte chunks
+// with the chunks of row r XOR-permuted by a few bits of r, so a 16-row x
+// 16-byte fragment read touches every bank equally.  Rows are a power of two
+// chunks long, so the lane -> (row, chunk) split of a tile load is a shift
+// and a mask, and the source offsets of one lane's loads differ by
+// constants.
 //
 // Precision matches the tiled path: fp32 residual and LayerNorm, fp16
 // operands with fp32 accumulation, first-layer scores from a hi/lo fp16
@@ -62,20 +64,15 @@ constexpr int SEQ_WPS = SEQ_SLOT / (16 * TPW);  // waves per sequence slot
 constexpr int SEQ_MAX_F = 4096;   // largest FFN width of the SEQ path
 constexpr int FCH = 64;        // FFN width per chunk
 
-constexpr int SEQ_PAD = 16;     // LDS row padding (halves)
 constexpr int SEQ_LDS_MAX = 160 * 1024;
 
-// Largest staged weight tile (halves), rows padded by SEQ_PAD:
-//   Q/K/V rows of one head DH x D, W_o columns of one head D x DH,
-//   W_1 rows of one chunk FCH x D, W_2 columns of one chunk D x FCH.
-constexpr int seq_tbuf(int D, int DH) {
-    const int t1 = DH * (D + SEQ_PAD) > D * (DH + SEQ_PAD) ? DH * (D + SEQ_PAD) : D * (DH + SEQ_PAD);
-    const int t2 = FCH * (D + SEQ_PAD) > D * (FCH + SEQ_PAD) ? FCH * (D + SEQ_PAD) : D * (FCH + SEQ_PAD);
-    return t1 > t2 ? t1 : t2;
-}
+// Largest staged weight tile (halves): Q/K/V rows of one head DH x D, W_o
+// columns of one head D x DH, W_1 rows of one chunk FCH x D, W_2 columns of
+// one chunk D x FCH.
+constexpr int seq_tbuf(int D, int DH) { return (DH > FCH ? DH : FCH) * D; }
 // Static LDS of the kernel (bytes): two weight tiles, K hi/lo, V^T.
 constexpr int seq_static_lds(int D, int DH) {
-    return 2 * seq_tbuf(D, DH) * 2 + 2 * SEQ_TOK * (DH + SEQ_PAD) * 2 + DH * (SEQ_TOK + SEQ_PAD) * 2;
+    return 2 * seq_tbuf(D, DH) * 2 + 2 * SEQ_TOK * DH * 2 + DH * SEQ_TOK * 2;
 }
 // Dynamic LDS (bytes): per-layer vectors, double-buffered by layer parity.
 inline size_t seq_param_lds(int d, int f, size_t elem) { return 2 * (size_t)(((9 * d + f) + 7) & ~7) * elem; }
@@ -100,9 +97,26 @@ __device__ __forceinline__ int sigma32_inv(int k) { return (k & 3) | ((k >> 3) <
 // (after the sigma32 row gather): 4 consecutive features per block.
 __device__ __forceinline__ int feat4(int blk, int g) { return (blk >> 1) * 32 + 8 * g + 4 * (blk & 1); }
 
-// A operand fragment: 8 consecutive halves of LDS row `row` at column col0 + 8g.
-__device__ __forceinline__ f16x8 afrag(const f16* buf, int ldw, int row, int col0, int g) {
-    return *(const f16x8*)(buf + row * ldw + col0 + 8 * g);
+// Chunk k of row r of an image with CPR chunks per row sits in slot
+// k ^ swz(r).  Measured on this LDS: folding r into the low chunk bits makes
+// 16-row fragment reads conflict-free for rows of 128 bytes and more; for
+// 64-byte rows (two per 128-byte line) bits 1-2 of r are used instead.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16 || CPR == 32, "rows of 4 to 32 chunks");
+    if constexpr (CPR >= 16) return r & 15;
+    else if constexpr (CPR == 8) return r & 7;
+    else return (r >> 1) & 3;
+}
+// Byte offset of chunk k of row r.
+template <int CPR>
+__device__ __forceinline__ int img_off(int r, int k) { return r * (CPR * 16) + ((k ^ swz<CPR>(r)) << 4); }
+
+// A operand fragment: chunk k of row 16 blk + c16 (sw = swz(c16), which is
+// swz of that row for every blk).
+template <int CPR>
+__device__ __forceinline__ f16x8 afrag16(const f16* buf, int blk, int c16, int k, int sw) {
+    return *(const f16x8*)((const char*)buf + (blk * 16 + c16) * (CPR * 16) + ((k ^ sw) << 4));
 }
 
 // Four consecutive stored values as fp32.
@@ -146,10 +160,9 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     constexpr int NQB = DH / 16;  // blocks per head
     constexpr int NHC = DH / 32;  // 32-wide K chunks over the head dim
     constexpr int NCB = NQB > FCH / 16 ? NQB : FCH / 16;  // carried blocks (Q of a head, or a GELU chunk)
-    constexpr int PAD = SEQ_PAD;
-    constexpr int KLD = DH + PAD;             // K rows in LDS
-    constexpr int VLD = SEQ_TOK + PAD;        // V^T rows in LDS
-    // Staged weight tiles, rows padded by PAD halves and sigma32-gathered:
+    constexpr int KCPR = DH / 8;              // chunks per K row (token)
+    constexpr int VCPR = SEQ_TOK / 8;         // chunks per V^T row (feature)
+    // Staged weight tiles, rows sigma32-gathered and chunk-swizzled:
     //   kinds 0-2: Q/K/V rows of one head, DH x D;  3: W_o columns of one head, D x DH;
     //   4: W_1 rows of one chunk, FCH x D;          5: W_2 columns of one chunk, D x FCH.
     constexpr int TBUF = seq_tbuf(D, DH);
@@ -158,10 +171,10 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 
     __shared__ __attribute__((aligned(16))) f16 Wb0[TBUF];
     __shared__ __attribute__((aligned(16))) f16 Wb1[TBUF];
-    __shared__ __attribute__((aligned(16))) f16 Kh[SEQ_TOK * KLD];
-    __shared__ __attribute__((aligned(16))) f16 Kl[SEQ_TOK * KLD];
-    __shared__ __attribute__((aligned(16))) f16 Vt[DH * VLD];
-    static_assert(seq_static_lds(D, DH) == (2 * TBUF + 2 * SEQ_TOK * KLD + DH * VLD) * 2, "LDS accounting");
+    __shared__ __attribute__((aligned(16))) f16 Kh[SEQ_TOK * DH];
+    __shared__ __attribute__((aligned(16))) f16 Kl[SEQ_TOK * DH];
+    __shared__ __attribute__((aligned(16))) f16 Vt[DH * SEQ_TOK];
+    static_assert(seq_static_lds(D, DH) == (2 * TBUF + 3 * SEQ_TOK * DH) * 2, "LDS accounting");
     // Small per-layer vectors, raw I/O-dtype bits, double-buffered by layer
     // parity: b_qkv | b_o | ln1_g | ln1_b | b_1 | b_2 | ln2_g | ln2_b.
     constexpr int P_BQKV = 0, P_BO = 3 * D, P_G1 = 4 * D, P_BE1 = 5 * D, P_B1 = 6 * D;
@@ -254,26 +267,33 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             fn(std::integral_constant<int, D>{}, std::integral_constant<int, FCH>{}, (const WT*)w.w_2 + d.fc * FCH, F);
     };
 
-    // Every 16-byte chunk of the padded, row-gathered LDS image of a tile;
-    // pad chunks re-read the row's first chunk.  Chunk c of the image is
-    // loaded by thread c mod 512 (the DMA destination of a lane is fixed).
+    // Chunk c of a tile's LDS image (row c / CPR, slot c % CPR) is loaded by
+    // thread c mod 512, since an LDS-DMA lane's destination is fixed; the
+    // slot holds source chunk slot ^ swz(row) of gathered source row
+    // gather(row).  512 / CPR rows lie between one thread's loads, a multiple
+    // of 16 (rows of up to 32 chunks), so slot, swz and the gather's low part
+    // are the same for all of them: the source offsets differ by whole rows.
     uint4 stg[DIRECT ? 1 : MAXCH];
     auto tile_fetch = [&](int t, f16* buf) {
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         with_geom(t, [&](auto R, auto C, const WT* base, int rstride) {
-            constexpr int ROWS = decltype(R)::value, CPR = decltype(C)::value / 8, CPP = CPR + PAD / 8;
-            constexpr int N = ROWS * CPP;
+            constexpr int ROWS = decltype(R)::value, CPR = decltype(C)::value / 8, N = ROWS * CPR;
+            constexpr int S = SEQ_THREADS / CPR;  // rows between one thread's loads
+            static_assert(S % 16 == 0, "rows between loads");
+            const int tt = tid & (SEQ_THREADS - 1);
+            const int r0 = tt / CPR, slot = tt % CPR;
+            const int lane_off = (((r0 & ~31) + sigma32(r0 & 31)) * rstride + ((slot ^ swz<CPR>(r0)) << 3)) * (int)sizeof(WT);
 #pragma unroll
             for (int i = 0; i < MAXCH; i++) {
-                const int c = tid + i * SEQ_THREADS;
-                if (i * SEQ_THREADS < N && c < N) {
-                    const int r = c / CPP, k8 = c - r * CPP;
-                    const int gr = (r & ~31) + sigma32(r & 31);
-                    const WT* src = base + (gr * rstride + (k8 < CPR ? k8 : 0) * 8);
+                if (i * SEQ_THREADS < N && tt + i * SEQ_THREADS < N) {
+                    // gathered row of r0 + S i: + S i for S >= 32; for S = 16 the
+                    // odd half-group adds 4 (sigma32 maps +16 to +4)
+                    const int drow = S >= 32 ? S * i : 32 * (i >> 1) + 4 * (i & 1);
+                    const WT* sb = base + (size_t)drow * rstride;
                     if constexpr (DIRECT) {
-                        dma16(src, buf + (i * SEQ_THREADS + wv * 64) * 8);
+                        dma16s(sb, (unsigned)lane_off, buf + (i * SEQ_THREADS + wv * 64) * 8);
                     } else {
-                        stg[i] = *(const uint4*)src;
+                        stg[i] = *(const uint4*)((const char*)sb + lane_off);
                     }
                 }
             }
@@ -282,10 +302,11 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     auto tile_commit = [&](int t, f16* buf) {
         if constexpr (!DIRECT) {
             with_geom(t, [&](auto R, auto C, const WT*, int) {
-                constexpr int N = decltype(R)::value * (decltype(C)::value / 8 + PAD / 8);
+                constexpr int N = decltype(R)::value * (decltype(C)::value / 8);
+                const int tt = tid & (SEQ_THREADS - 1);
 #pragma unroll
                 for (int i = 0; i < MAXCH; i++) {
-                    const int c = tid + i * SEQ_THREADS;
+                    const int c = tt + i * SEQ_THREADS;
                     if (i * SEQ_THREADS < N && c < N) *(f16x8*)&buf[c * 8] = load8_as_f16((const WT*)&stg[i]);
                 }
             });
@@ -353,7 +374,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 
         if (d.kind <= 2) {
             // ---- Q^T, K^T or V^T of head h: [DH x tokens] = W rows . X^T
-            constexpr int ldw = D + PAD;
+            constexpr int CPR = D / 8;
+            const int sw = swz<CPR>(c16);
             f32x4 acc[NQB][TPW];
             const WT* bq = P + P_BQKV + d.kind * D + d.h * DH;
 #pragma unroll
@@ -366,7 +388,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             for (int kk = 0; kk < NKC; kk++)
 #pragma unroll
                 for (int ob = 0; ob < NQB; ob++) {
-                    const f16x8 a = afrag(W, ldw, ob * 16 + c16, kk * 32, g);
+                    const f16x8 a = afrag16<CPR>(W, ob, c16, kk * 4 + g, sw);
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = mfma_16x16x32(a, XB[kk][tb], acc[ob][tb]);
                 }
@@ -389,8 +411,10 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                             hv[e] = (f16)acc[kb][tb][e];
                             lv[e] = (f16)(acc[kb][tb][e] - (float)hv[e]);
                         }
-                        *(f16x4*)&Kh[tok * KLD + feat4(kb, g)] = hv;
-                        if (split) *(f16x4*)&Kl[tok * KLD + feat4(kb, g)] = lv;
+                        // features feat4(kb, g) .. + 3: chunk (kb >> 1) * 4 + g, half kb & 1
+                        const int o = img_off<KCPR>(tok, (kb >> 1) * 4 + g) + 8 * (kb & 1);
+                        *(f16x4*)((char*)Kh + o) = hv;
+                        if (split) *(f16x4*)((char*)Kl + o) = lv;
                     }
                 }
             } else {
@@ -401,13 +425,16 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int vb = 0; vb < NQB; vb++)
 #pragma unroll
                         // feature feat4(vb, g) + e sits in LDS row sigma32_inv of it: vb * 16 + 4g + e
-                        for (int e = 0; e < 4; e++) Vt[(vb * 16 + 4 * g + e) * VLD + tok] = (f16)acc[vb][tb][e];
+                        for (int e = 0; e < 4; e++)
+                            *(f16*)((char*)Vt + img_off<VCPR>(vb * 16 + 4 * g + e, tok >> 3) + 2 * (tok & 7)) =
+                                (f16)acc[vb][tb][e];
                 }
             }
         } else if (d.kind == 3) {
             // ---- attention of head h for this wave's queries
             const int kbase = sq * SEQ_SLOT;
             const int kmax = min(q0 + 16 * TPW, len);
+            const int swk = swz<KCPR>(c16);
             const int nch = (kmax + 31) >> 5;  // 32-key chunks that matter (1 or 2)
             f16x8 qh[NHC][TPW], ql[NHC][TPW];
 #pragma unroll
@@ -443,15 +470,16 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int hb = 0; hb < 2; hb++) {
 #pragma unroll
                         for (int tb = 0; tb < TPW; tb++) s[hb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        const int krow = kbase + cc * 32 + hb * 16 + c16;  // holds key sigma32(hb * 16 + c16)
+                        // LDS row kbase + cc * 32 + hb * 16 + c16 holds key sigma32(hb * 16 + c16)
+                        const int kblk = (kbase + cc * 32) / 16 + hb;
 #pragma unroll
                         for (int kk = 0; kk < NHC; kk++) {
-                            const f16x8 a = afrag(Kh, KLD, krow, kk * 32, g);
+                            const f16x8 a = afrag16<KCPR>(Kh, kblk, c16, kk * 4 + g, swk);
 #pragma unroll
                             for (int tb = 0; tb < TPW; tb++) {
                                 s[hb][tb] = mfma_16x16x32(a, qh[kk][tb], s[hb][tb]);
                                 if (split) {
-                                    s[hb][tb] = mfma_16x16x32(afrag(Kl, KLD, krow, kk * 32, g), qh[kk][tb], s[hb][tb]);
+                                    s[hb][tb] = mfma_16x16x32(afrag16<KCPR>(Kl, kblk, c16, kk * 4 + g, swk), qh[kk][tb], s[hb][tb]);
                                     s[hb][tb] = mfma_16x16x32(a, ql[kk][tb], s[hb][tb]);
                                 }
                             }
@@ -493,8 +521,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     }
 #pragma unroll
                     for (int db = 0; db < NQB; db++) {
-                        const int vrow = db * 16 + c16;  // holds feature (db >> 1) * 32 + sigma32((db & 1) * 16 + c16)
-                        const f16x8 va = afrag(Vt, VLD, vrow, kbase + cc * 32, g);
+                        // LDS row db * 16 + c16 holds feature (db >> 1) * 32 + sigma32((db & 1) * 16 + c16)
+                        const f16x8 va = afrag16<VCPR>(Vt, db, c16, (kbase + cc * 32) / 8 + g, c16);
 #pragma unroll
                         for (int tb = 0; tb < TPW; tb++) o[db][tb] = mfma_16x16x32(va, pack8(s[0][tb], s[1][tb]), o[db][tb]);
                     }
@@ -520,19 +548,19 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
                 }
             }
-            constexpr int ldw = DH + PAD;
+            const int swo = swz<DH / 8>(c16);
 #pragma unroll
             for (int db = 0; db < NDB; db++)
 #pragma unroll
                 for (int kk = 0; kk < NHC; kk++) {
-                    const f16x8 a = afrag(W, ldw, db * 16 + c16, kk * 32, g);
+                    const f16x8 a = afrag16<DH / 8>(W, db, c16, kk * 4 + g, swo);
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] = mfma_16x16x32(a, OB[kk][tb], R[db][tb]);
                 }
             pipeline_order<NDB * NHC, NDB * NHC * TPW, TPW, SEQ_AHEAD>();
         } else if (d.kind == 4) {
             // ---- FFN up-projection chunk + GELU, carried to the next tile
-            constexpr int ldw = D + PAD;
+            const int sw1 = swz<D / 8>(c16);
 #pragma unroll
             for (int ob = 0; ob < FCH / 16; ob++) {
                 const f32x4 bv = load4(P + P_B1 + d.fc * FCH + feat4(ob, g));
@@ -543,7 +571,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             for (int kk = 0; kk < NKC; kk++)
 #pragma unroll
                 for (int ob = 0; ob < FCH / 16; ob++) {
-                    const f16x8 a = afrag(W, ldw, ob * 16 + c16, kk * 32, g);
+                    const f16x8 a = afrag16<D / 8>(W, ob, c16, kk * 4 + g, sw1);
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) carry[ob][tb] = mfma_16x16x32(a, XB[kk][tb], carry[ob][tb]);
                 }
@@ -564,7 +592,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] += bv;
                 }
             }
-            constexpr int ldw = FCH + PAD;
+            const int sw2 = swz<FCH / 8>(c16);
             f16x8 gb[FCH / 32][TPW];
 #pragma unroll
             for (int kk = 0; kk < FCH / 32; kk++)
@@ -574,7 +602,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             for (int db = 0; db < NDB; db++)
 #pragma unroll
                 for (int kk = 0; kk < FCH / 32; kk++) {
-                    const f16x8 a = afrag(W, ldw, db * 16 + c16, kk * 32, g);
+                    const f16x8 a = afrag16<FCH / 8>(W, db, c16, kk * 4 + g, sw2);
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) R[db][tb] = mfma_16x16x32(a, gb[kk][tb], R[db][tb]);
                 }
