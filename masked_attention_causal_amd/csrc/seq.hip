@@ -205,8 +205,6 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     len = len < 1 ? 1 : (len > L ? L : len);
     const int F = p.F;
     const int NF = F / FCH;
-    const int per_layer = 4 * H + 2 * NF;
-    const int ntiles = per_layer * p.n_layers;
     const int PLEN = 9 * D + F;
     const int PLENP = (PLEN + 7) & ~7;          // 16-byte aligned parity buffers
     const int P_B2 = 6 * D + F, P_G2 = 7 * D + F, P_BE2 = 8 * D + F;
@@ -232,28 +230,35 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
         }
     };
 
-    // Tile t of the stream: per layer, for each head h: Q_h, K_h, V_h, W_o(h);
-    // then for each FFN chunk: W_1(chunk), W_2(chunk).
-    auto describe = [&](int t) {
-        TileDesc d;
-        d.layer = t / per_layer;
-        int r = t - d.layer * per_layer;
-        d.h = d.kc = d.fc = 0;
-        if (r < 4 * H) {
-            d.h = r >> 2;
-            d.kind = r & 3;  // 0 Q, 1 K, 2 V, 3 W_o
+    // The tile stream: per layer, for each head h: Q_h, K_h, V_h, W_o(h);
+    // then for each FFN chunk: W_1(chunk), W_2(chunk).  next_of gives the
+    // tile after d (kind -1 past the last one).
+    auto next_of = [&](const TileDesc& d) {
+        TileDesc n = d;
+        if (d.kind <= 2 || d.kind == 4) {
+            n.kind = d.kind + 1;
+        } else if (d.kind == 3) {
+            if (d.h + 1 < H) {
+                n.kind = 0;
+                n.h = d.h + 1;
+            } else {
+                n.kind = 4;
+                n.fc = 0;
+            }
+        } else if (d.fc + 1 < NF) {
+            n.kind = 4;
+            n.fc = d.fc + 1;
+        } else if (d.layer + 1 < p.n_layers) {
+            n = TileDesc{0, d.layer + 1, 0, 0, 0};
         } else {
-            r -= 4 * H;
-            d.fc = r >> 1;
-            d.kind = 4 + (r & 1);  // 4 W_1, 5 W_2
+            n.kind = -1;
         }
-        return d;
+        return n;
     };
     // Geometry of a tile, passed to fn as compile-time rows and columns of the
     // staged image plus the global base and row stride (elements), so the
     // per-lane chunk -> (row, column) split below divides by constants.
-    auto with_geom = [&](int t, auto&& fn) {
-        const TileDesc d = describe(t);
+    auto with_geom = [&](const TileDesc& d, auto&& fn) {
         const LayerPtrs& w = p.lw[d.layer];
         if (d.kind <= 2)
             fn(std::integral_constant<int, DH>{}, std::integral_constant<int, D>{},
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     // of 16 (rows of up to 32 chunks), so slot, swz and the gather's low part
     // are the same for all of them: the source offsets differ by whole rows.
     uint4 stg[DIRECT ? 1 : MAXCH];
-    auto tile_fetch = [&](int t, f16* buf) {
+    auto tile_fetch = [&](const TileDesc& t, f16* buf) {
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         with_geom(t, [&](auto R, auto C, const WT* base, int rstride) {
             constexpr int ROWS = decltype(R)::value, CPR = decltype(C)::value / 8, N = ROWS * CPR;
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             }
         });
     };
-    auto tile_commit = [&](int t, f16* buf) {
+    auto tile_commit = [&](const TileDesc& t, f16* buf) {
         if constexpr (!DIRECT) {
             with_geom(t, [&](auto R, auto C, const WT*, int) {
                 constexpr int N = decltype(R)::value * (decltype(C)::value / 8);
@@ -367,8 +372,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
         }
     };
 
-    auto step = [&](int t, const f16* W) {
-        const TileDesc d = describe(t);
+    auto step = [&](const TileDesc& d, const f16* W) {
         const WT* P = Pm + (d.layer & 1) * PLENP;
         const bool split = d.layer == 0;
 
@@ -614,29 +618,37 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             layer_norm(P + (d.kind == 3 ? P_G1 : P_G2), P + (d.kind == 3 ? P_BE1 : P_BE2));
     };
 
+    // One step: the next tile streams into the other buffer while this one
+    // is multiplied; the first step of a layer also fetches the next layer's
+    // vectors into the other parity buffer.  Step kinds are compile-time at
+    // every call site below, so each kind is inlined once with no dispatch
+    // and the residual stays in the same registers across steps.
+    auto run = [&](const TileDesc d, const f16* W, f16* Wn, bool first_of_layer) {
+        refresh_lane();
+        const TileDesc n = next_of(d);
+        if (n.kind >= 0) tile_fetch(n, Wn);
+        if (first_of_layer && d.layer + 1 < p.n_layers) param_fetch(d.layer + 1);
+        step(d, W);
+        if (n.kind >= 0) tile_commit(n, Wn);
+        __syncthreads();
+    };
     param_fetch(0);
-    tile_fetch(0, Wb0);
-    tile_commit(0, Wb0);
+    tile_fetch(TileDesc{0, 0, 0, 0, 0}, Wb0);
+    tile_commit(TileDesc{0, 0, 0, 0, 0}, Wb0);
     __syncthreads();
-    // The next layer's vectors stream into the other parity buffer during the
-    // first step of a layer and land with that step's tile.
-    auto next_params = [&](int t) { return (t % per_layer) == 0 && t / per_layer + 1 < p.n_layers; };
-    // Two steps per iteration so each step's LDS buffers are fixed at compile
-    // time: tile t is read from one buffer while tile t + 1 streams into the other.
-    for (int t = 0; t < ntiles; t += 2) {
-        refresh_lane();
-        if (t + 1 < ntiles) tile_fetch(t + 1, Wb1);
-        if (next_params(t)) param_fetch(t / per_layer + 1);
-        step(t, Wb0);
-        if (t + 1 < ntiles) tile_commit(t + 1, Wb1);
-        __syncthreads();
-        if (t + 1 >= ntiles) break;
-        refresh_lane();
-        if (t + 2 < ntiles) tile_fetch(t + 2, Wb0);
-        if (next_params(t + 1)) param_fetch((t + 1) / per_layer + 1);
-        step(t + 1, Wb1);
-        if (t + 2 < ntiles) tile_commit(t + 2, Wb0);
-        __syncthreads();
+    // Every group (4 tiles per head, 2 per FFN chunk) has an even length, so
+    // a group's first tile is always in Wb0.
+    for (int l = 0; l < p.n_layers; l++) {
+        for (int h = 0; h < H; h++) {
+            run(TileDesc{0, l, h, 0, 0}, Wb0, Wb1, h == 0);
+            run(TileDesc{1, l, h, 0, 0}, Wb1, Wb0, false);
+            run(TileDesc{2, l, h, 0, 0}, Wb0, Wb1, false);
+            run(TileDesc{3, l, h, 0, 0}, Wb1, Wb0, false);
+        }
+        for (int fc = 0; fc < NF; fc++) {
+            run(TileDesc{4, l, 0, 0, fc}, Wb0, Wb1, false);
+            run(TileDesc{5, l, 0, 0, fc}, Wb1, Wb0, false);
+        }
     }
 
     // ---- output rows
