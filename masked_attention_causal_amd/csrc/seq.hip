@@ -580,12 +580,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     for (int tb = 0; tb < TPW; tb++) carry[ob][tb] = mfma_16x16x32(a, XB[kk][tb], carry[ob][tb]);
                 }
             pipeline_order<FCH / 16 + NKC * FCH / 16, NKC * FCH / 16 * TPW, TPW, SEQ_AHEAD>();
-#pragma unroll
-            for (int ob = 0; ob < FCH / 16; ob++)
-#pragma unroll
-                for (int tb = 0; tb < TPW; tb++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) carry[ob][tb][e] = gelu_erf(carry[ob][tb][e]);
+            static_assert(sizeof(carry) == FCH / 16 * TPW * 4 * sizeof(float), "carry is packed floats");
+            gelu_inplace<FCH / 16 * TPW * 4>((float*)&carry[0][0]);
         } else {
             // ---- FFN down-projection chunk accumulated into the residual
             if (d.fc == 0) {
