@@ -36,8 +36,11 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-# Per-file extra flags (none at present).
-EXTRA: dict = {}
+# Per-file extra flags.  attn.hip: MFMA accumulators in VGPRs (the softmax
+# reads every score, and AGPR operands would cost a move each way), and no
+# NaN honouring, so max over scores needs no quieting pass (the kernels never
+# produce NaN from finite inputs; masks use -inf, which is still honoured).
+EXTRA: dict = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

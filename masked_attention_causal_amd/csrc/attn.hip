@@ -514,14 +514,19 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
     const f16x4 qh = qok ? *(const f16x4*)(Qh + (size_t)myq * DH + 4 * g) : f16x4{};
     const f16x4 ql = (SPLIT && qok) ? *(const f16x4*)(Ql + (size_t)myq * DH + 4 * g) : f16x4{};
 
-    // DMA: thread tid fetches K row tid >> 1 (chunk slot tid & 1) and V^T row
-    // tid >> 4 (chunk slot tid & 15); chunk c of row r sits in slot c ^ (r mod chunks).
-    const int krow = tid >> 1, kchk = (tid & 1) ^ (krow & 1);
+    // DMA: thread tid fetches K chunk slot tid & 1 of LDS row tid >> 1 and V^T
+    // row tid >> 4 (chunk slot tid & 15).  LDS K row 16 kb + i holds the key
+    // that lane i reads for score block kb (key (kb/2)*32 + 8(i/4) + 4(kb%2) +
+    // i%4), so a block's A operand is 16 consecutive 32-byte rows; its two
+    // chunks are swapped in rows 8-15 of the block, which puts each half-wave's
+    // 8-byte reads on 64 distinct banks.  V^T rows: chunk c in slot c ^ (r mod 16).
+    const int krow = tid >> 1, kchk = (tid & 1) ^ ((krow >> 3) & 1);
+    const int kkey = ((krow >> 5) * 32) + (((krow & 15) >> 2) * 8) + (((krow >> 4) & 1) * 4) + (krow & 3);
     const int vrow = tid >> 4, vchk = (tid & 15) ^ (vrow & 15);
     auto issue = [&](int t, int buf) {
         char* base = lds + buf * SB;
         const int k0 = t * KT;
-        const size_t off = (size_t)min(k0 + krow, L - 1) * KROW + 16 * kchk;   // rows past L: copies
+        const size_t off = (size_t)min(k0 + kkey, L - 1) * KROW + 16 * kchk;   // keys past L: copies
         dma16(Khg + off, base + wave * 64 * 16);
         if constexpr (SPLIT) dma16(Klg + off, base + KB + wave * 64 * 16);
         dma16(Vg + ((size_t)vrow * Lp + k0) * 2 + 16 * vchk, base + KB * (SPLIT ? 2 : 1) + wave * 64 * 16);
@@ -551,17 +556,29 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
         const char* vs = ks + KB * (SPLIT ? 2 : 1);
         // key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
         f32x4 sc[8];
+        f16x4 ka[8], kl[8];
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
-            const int r = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
-            const int off = r * KROW + (((g >> 1) ^ (r & 1)) * 16) + (g & 1) * 8;
-            const f16x4 a = *(const f16x4*)(ks + off);
-            sc[kb] = mfma_16x16x16(a, qh, f32x4{0.f, 0.f, 0.f, 0.f});
+            const int off = (kb * 16 + c16) * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
+            ka[kb] = *(const f16x4*)(ks + off);
+            if constexpr (SPLIT) kl[kb] = *(const f16x4*)(kls + off);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++) {
+            sc[kb] = mfma_16x16x16(ka[kb], qh, f32x4{0.f, 0.f, 0.f, 0.f});
             if constexpr (SPLIT) {
-                sc[kb] = mfma_16x16x16(*(const f16x4*)(kls + off), qh, sc[kb]);
-                sc[kb] = mfma_16x16x16(a, ql, sc[kb]);
+                sc[kb] = mfma_16x16x16(kl[kb], qh, sc[kb]);
+                sc[kb] = mfma_16x16x16(ka[kb], ql, sc[kb]);
             }
         }
+        // all K fragments of the tile are read before the first product
+#pragma unroll
+        for (int i = 0; i < (SPLIT ? 8 : 4); i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT ? 24 : 8, 0);
+        // scores in the exp2 domain: the product with the scale also makes the
+        // values canonical, so the max below needs no NaN-quieting pass
+#pragma unroll
+        for (int kb = 0; kb < 8; kb++) sc[kb] *= sl2;
         const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
         if (need_mask) {
 #pragma unroll
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
             mx = fmaxf(fmaxf(mx, fmaxf(sc[kb][0], sc[kb][1])), fmaxf(sc[kb][2], sc[kb][3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float m_new = fmaxf(m_run, mx * sl2);
+        const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_use);
         m_run = m_new;
@@ -589,8 +606,8 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
             f16x8 pb;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                pb[e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc][e], sl2, -m_use));
-                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc + 1][e], sl2, -m_use));
+                pb[e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc][e] - m_use);
+                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc + 1][e] - m_use);
             }
             const int r = c16;
             const f16x8 va = *(const f16x8*)(vs + r * VROW + (((cc * 4 + g) ^ (r & 15)) * 16));
