@@ -480,8 +480,12 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
 // barrier (32 scores per lane), the scale folded into one FMA feeding the
 // hardware exp2, and the softmax row sums taken on the MFMA by a ones row
 // appended to V^T (the sum of the same fp16 weights that multiply V).
+// Queries per workgroup of the head-dim-16 kernel: 8 waves of 16, so each
+// staged K/V tile serves 128 queries (the first four waves load it).
+constexpr int ATT16_WAVES = 8, ATT16_BQ = 16 * ATT16_WAVES;
+
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
+__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs p) {
     constexpr int DH = 16, KT = 128, ST = 3;
     constexpr int KROW = DH * 2;                     // 32-byte K rows: two 16-byte chunks
     constexpr int KB = KT * KROW;                    // 4 KB per K plane tile
@@ -499,8 +503,8 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
     const int L = p.L, Lp = p.Lp;
     int len = p.lens[b];
     len = len < 1 ? 1 : (len > L ? L : len);
-    const int q0 = qt * ATT_BQ, qw0 = q0 + 16 * wave;
-    const int kend = min(q0 + ATT_BQ, len);
+    const int q0 = qt * ATT16_BQ, qw0 = q0 + 16 * wave;
+    const int kend = min(q0 + ATT16_BQ, len);
     const int ntiles = (kend + KT - 1) / KT;
     const size_t bh = (size_t)b * p.H + h;
     const f16* Qh = (const f16*)p.Q + bh * L * DH;
@@ -539,16 +543,19 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
     float m_run = -INFINITY;
     const float sl2 = p.scale_log2;
 
+    // waves 0-3 load the tiles (one chunk per thread per plane); the others
+    // issue no loads, so their waits below return at once
+    const bool loader = wave < 4;
 #pragma unroll
     for (int s = 0; s < ST - 1; s++)
-        if (s < ntiles) issue(s, s);
+        if (loader && s < ntiles) issue(s, s);
     for (int t = 0; t < ntiles; t++) {
         if (t + ST - 2 < ntiles)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST - 2) * NDMA) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
+        if (loader && t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
         const int k0 = t * KT;
         if (k0 > qw0 + 15) continue;
         const char* ks = lds + (t % ST) * SB;
@@ -575,10 +582,6 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
 #pragma unroll
         for (int i = 0; i < (SPLIT ? 8 : 4); i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, SPLIT ? 24 : 8, 0);
-        // scores in the exp2 domain: the product with the scale also makes the
-        // values canonical, so the max below needs no NaN-quieting pass
-#pragma unroll
-        for (int kb = 0; kb < 8; kb++) sc[kb] *= sl2;
         const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
         if (need_mask) {
 #pragma unroll
@@ -595,7 +598,9 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
             mx = fmaxf(fmaxf(mx, fmaxf(sc[kb][0], sc[kb][1])), fmaxf(sc[kb][2], sc[kb][3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float m_new = fmaxf(m_run, mx);
+        // the max over raw scores scales with the (positive) exp2-domain factor;
+        // the scale then folds into one fma per score before the exponential
+        const float m_new = fmaxf(m_run, mx * sl2);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_use);
         m_run = m_new;
@@ -606,8 +611,8 @@ __global__ __launch_bounds__(256) void attn_ring16_kernel(AttnArgs p) {
             f16x8 pb;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                pb[e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc][e] - m_use);
-                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc + 1][e] - m_use);
+                pb[e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc][e], sl2, -m_use));
+                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc + 1][e], sl2, -m_use));
             }
             const int r = c16;
             const f16x8 va = *(const f16x8*)(vs + r * VROW + (((cc * 4 + g) ^ (r & 15)) * 16));
@@ -656,11 +661,11 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
         return hipGetLastError();
     }
     if (dh == 16) {   // the plan pads V^T rows to whole 128-key tiles
-        dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
+        dim3 grid((a.L + ATT16_BQ - 1) / ATT16_BQ, a.H, a.B);
         if (split_qk)
-            hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
         else
-            hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
         return hipGetLastError();
     }
     return attn_mode<f16>(dh, split_qk, a, s);

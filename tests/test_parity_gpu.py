@@ -29,6 +29,7 @@ SMALL = [
     W("s_f32_dh16", 2, 64, 4, 96, 3, 150, "f32", 1, 150, 1.0),
     W("s_f32_dh64", 2, 128, 2, 256, 2, 200, "f32", 1, 200, 1.0),
     W("s_f16_dh16", 2, 64, 4, 128, 3, 130, "f16", 1, 130, 1.0),
+    W("s_bf16_dh16_l600", 2, 64, 4, 128, 2, 600, "bf16", 200, 600, 1.0),  # several 128-query blocks and key tiles
     W("s_f16_dh32", 2, 96, 3, 160, 2, 70, "f16", 1, 70, 1.0),
     W("s_f16_dh64", 2, 256, 4, 512, 5, 64, "f16", 8, 64, 1.0),
     W("s_bf16_dh64", 3, 128, 2, 256, 2, 190, "bf16", 1, 190, 1.0),
