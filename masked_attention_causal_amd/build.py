@@ -37,10 +37,12 @@ def _hipcc() -> str:
 
 
 # Per-file extra flags.  attn.hip: MFMA accumulators in VGPRs (the softmax
-# reads every score, and AGPR operands would cost a move each way), and no
-# NaN honouring, so max over scores needs no quieting pass (the kernels never
-# produce NaN from finite inputs; masks use -inf, which is still honoured).
-EXTRA: dict = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+# reads every score, and AGPR operands would cost a move each way).  attn.hip
+# and seq.hip: no NaN honouring, so a max over scores needs no quieting pass
+# (the kernels never produce NaN from finite inputs; masks use -inf, which is
+# still honoured).
+EXTRA: dict = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+               "seq.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -489,6 +489,10 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                             }
                         }
                     }
+                    // keys of this chunk can be masked only if it reaches past the
+                    // wave's first query or past the sequence end (wave-uniform)
+                    const bool need_mask =
+                        __builtin_amdgcn_readfirstlane((cc * 32 + 31 > q0) || (cc * 32 + 31 >= len) ? 1 : 0) != 0;
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) {
                         const int pos = q0 + tb * 16 + c16;
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                             for (int e = 0; e < 4; e++) {
                                 const int key = cc * 32 + 8 * g + 4 * hb + e;
                                 float v = s[hb][tb][e] * p.scale_log2;
-                                if (key > pos || key >= len) v = -INFINITY;
+                                if (need_mask && (key > pos || key >= len)) v = -INFINITY;
                                 s[hb][tb][e] = v;
                                 mx = fmaxf(mx, v);
                             }
@@ -507,14 +511,14 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                         mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
                         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
                         const float mnew = fmaxf(mrun[tb], mx);  // finite: key 0 is in chunk 0
-                        const float alpha = exp2f(mrun[tb] - mnew);
+                        const float alpha = __builtin_amdgcn_exp2f(mrun[tb] - mnew);
                         mrun[tb] = mnew;
                         float ls = 0.f;
 #pragma unroll
                         for (int hb = 0; hb < 2; hb++) {
 #pragma unroll
                             for (int e = 0; e < 4; e++) {
-                                const float pv = exp2f(s[hb][tb][e] - mnew);
+                                const float pv = __builtin_amdgcn_exp2f(s[hb][tb][e] - mnew);
                                 s[hb][tb][e] = pv;
                                 ls += pv;
                             }
