@@ -39,6 +39,8 @@
 
 namespace tfl {
 
+typedef __attribute__((address_space(3))) char lds_char;
+
 template <class OpT, int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     constexpr bool F32 = sizeof(OpT) == 4;
@@ -564,11 +566,20 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
         // key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
         f32x4 sc[8];
         f16x4 ka[8], kl[8];
+        const int koff = c16 * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
-            const int off = (kb * 16 + c16) * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
-            ka[kb] = *(const f16x4*)(ks + off);
-            if constexpr (SPLIT) kl[kb] = *(const f16x4*)(kls + off);
+            // each block's base goes through an opaque scalar, which keeps the
+            // reads separate: merged into one two-address instruction, blocks
+            // 512 bytes apart would meet on the same banks
+            unsigned kbase = (unsigned)(size_t)(lds_char*)(ks + kb * 16 * KROW);
+            asm volatile("" : "+s"(kbase));
+            ka[kb] = *(const __attribute__((address_space(3))) f16x4*)((const lds_char*)(size_t)kbase + koff);
+            if constexpr (SPLIT) {
+                unsigned lbase = (unsigned)(size_t)(lds_char*)(kls + kb * 16 * KROW);
+                asm volatile("" : "+s"(lbase));
+                kl[kb] = *(const __attribute__((address_space(3))) f16x4*)((const lds_char*)(size_t)lbase + koff);
+            }
         }
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
