@@ -105,6 +105,20 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Lane exchanges inside a row of 16 lanes by DPP (a register move with a
+// lane pattern; no LDS round trip): partner lane i ^ 1, i ^ 2 within each
+// quad, and 7 - i within each group of 8.  After dpp_xor1 and dpp_xor2 sums a
+// quad holds its total; dpp_mirror8 then pairs the two quads of an 8-group.
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror8(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float gelu_erf(float h) { return 0.5f * h * (1.0f + erff(h * 0.7071067811865475f)); }
 
 // erf on |x| <= 1 as x * P(x^2), P of degree 5 (coefficients from

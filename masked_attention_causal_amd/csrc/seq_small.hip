@@ -8,7 +8,11 @@
 // keeps every value in fp32 with no operand rounding at all: projections on
 // fp32 MFMA (16 x 16 output blocks spread over the four waves), attention
 // one thread per (head, query) with the exact two-pass softmax, LayerNorm
-// one wave per row.
+// one wave per row.  When every layer's weights fit in LDS beside the
+// activations (WL), they are copied there once at the start, as fp32 rows
+// padded to 4 floats past a multiple of 32 (the 16 rows of an MFMA operand
+// then fall on distinct banks); each phase then waits on LDS, not on a
+// global-memory round trip per dependent product.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,13 +25,28 @@ constexpr int SS_THREADS = 256;
 template <class T>
 __device__ __forceinline__ float ld(const T* p, int i) { return to_f32(p[i]); }
 
+// Four consecutive stored values (16-, 8- or 8-byte aligned) as fp32.
+__device__ __forceinline__ f32x4 load4v(const float* q) { return *(const f32x4*)q; }
+template <class T>
+__device__ __forceinline__ f32x4 load4v(const T* q) {
+    const uint2 r = *(const uint2*)q;
+    const T* h = (const T*)&r;
+    return f32x4{to_f32(h[0]), to_f32(h[1]), to_f32(h[2]), to_f32(h[3])};
+}
+
 }  // namespace
 
 // LDS (rows padded to a multiple of 16 with zeros):
 // X [L][D] (layer input / LayerNorm output), B1 [L][max(3D, F)] (QKV, then
 // the out-projection sum, then the GELU hidden rows), B2 [L][D] (attention
 // output, then the FFN sum).
-template <class WT, int DH>
+// Floats of one layer's weights in LDS: W_qkv, W_o, W_1 rows of D + 4, W_2 rows
+// of F + 4, then b_qkv | b_o | ln1_g | ln1_b | b_1 | b_2 | ln2_g | ln2_b.
+__host__ __device__ inline int ss_layer_floats(int D, int F) {
+    return ((3 * D + D + F) * (D + 4) + D * (F + 4) + 9 * D + F + 3) & ~3;
+}
+
+template <class WT, int DH, bool WL>
 __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D) {
     extern __shared__ __attribute__((aligned(16))) float ss_lds[];
     const int H = D / DH;
@@ -49,57 +68,124 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
     for (int i = tid; i < LR * (2 * PX + P1); i += SS_THREADS) ss_lds[i] = 0.f;
     __syncthreads();
     for (int i = tid; i < L * D; i += SS_THREADS) X[(i / D) * PX + i % D] = ld(x, i);
+    float* const WLb = B2 + LR * PX;  // weights of every layer (WL only)
+    const int LF = ss_layer_floats(D, F);
+    if constexpr (WL) {
+        // four values per load (cols and n are multiples of 16), loads issued
+        // in batches of 8 before their stores
+        auto copy_rows = [&](const WT* src, int rows, int cols, float* dst) {
+            const int n4 = rows * cols / 4, c4 = cols / 4;
+            for (int i0 = 0; i0 < n4; i0 += 8 * SS_THREADS) {
+                f32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int i = i0 + u * SS_THREADS + tid;
+                    if (i < n4) v[u] = load4v(src + 4 * (size_t)i);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int i = i0 + u * SS_THREADS + tid;
+                    if (i < n4) {
+                        const int r = i / c4;
+                        *(f32x4*)(dst + r * (cols + 4) + 4 * (i - r * c4)) = v[u];
+                    }
+                }
+            }
+        };
+        auto copy_vec = [&](const WT* src, int n, float* dst) {
+            for (int i = tid; i < n / 4; i += SS_THREADS) *(f32x4*)(dst + 4 * i) = load4v(src + 4 * (size_t)i);
+        };
+        for (int l = 0; l < p.n_layers; l++) {
+            const LayerPtrs& w = p.lw[l];
+            float* o = WLb + (size_t)l * LF;
+            copy_rows((const WT*)w.w_qkv, 3 * D, D, o);
+            o += 3 * D * (D + 4);
+            copy_rows((const WT*)w.w_o, D, D, o);
+            o += D * (D + 4);
+            copy_rows((const WT*)w.w_1, F, D, o);
+            o += F * (D + 4);
+            copy_rows((const WT*)w.w_2, D, F, o);
+            o += D * (F + 4);
+            copy_vec((const WT*)w.b_qkv, 3 * D, o);
+            copy_vec((const WT*)w.b_o, D, o + 3 * D);
+            copy_vec((const WT*)w.ln1_g, D, o + 4 * D);
+            copy_vec((const WT*)w.ln1_b, D, o + 5 * D);
+            copy_vec((const WT*)w.b_1, F, o + 6 * D);
+            copy_vec((const WT*)w.b_2, D, o + 6 * D + F);
+            copy_vec((const WT*)w.ln2_g, D, o + 7 * D + F);
+            copy_vec((const WT*)w.ln2_b, D, o + 8 * D + F);
+        }
+    }
     __syncthreads();
     const float scale = rsqrtf((float)DH);
 
     // out[r][n] = bias[n] + sum_k in[r][k] W[n][k] (+ res[r][n]) on fp32 MFMA
     // (16x16x4: exact fp32 products, fp32 accumulation); one 16 x 16 output
-    // block per wave at a time, weights straight from global memory.
-    auto linear = [&](const float* in, int pin, int K, const WT* W, const WT* bias, int N, float* out, int pout,
+    // block per wave at a time; W rows pw elements apart (global memory in
+    // the stored dtype, or the fp32 LDS copy).
+    auto linear = [&](const float* in, int pin, int K, auto W, int pw, auto bias, int N, float* out, int pout,
                       const float* res, bool gelu) {
         const int nb16 = N / 16, nblk = (LR / 16) * nb16;
         for (int blk = wave; blk < nblk; blk += SS_THREADS / 64) {
             const int rb = blk / nb16, nb = blk - rb * nb16;
             const float* a = in + (rb * 16 + c16) * pin + g;
-            const WT* w = W + (size_t)(nb * 16 + c16) * K + g;
+            const auto w = W + (size_t)(nb * 16 + c16) * pw + g;
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
             for (int k = 0; k < K; k += 4) acc = mfma_16x16x4(a[k], ld(w, k), acc);
             // result: rows rb*16 + 4g + e, feature nb*16 + c16
             const int n = nb * 16 + c16;
             const float bn = ld(bias, n);
+            float vb[4] = {acc[0] + bn, acc[1] + bn, acc[2] + bn, acc[3] + bn};
+            if (gelu) gelu_inplace<4>(vb);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = rb * 16 + 4 * g + e;
                 if (r >= L) continue;
-                float v = acc[e] + bn;
-                if (gelu) v = gelu_erf(v);
+                float v = vb[e];
                 if (res) v += res[r * PX + n];
                 out[r * pout + n] = v;
             }
         }
     };
-    // rows of Z [L][D] (pitch PZ) -> LayerNorm -> X (two-pass, fp32, biased variance)
-    auto layernorm = [&](const float* Z, int PZ, const WT* gam, const WT* bet) {
-        for (int r = wave; r < L; r += SS_THREADS / 64) {
+    // rows of Z [L][D] (pitch PZ) -> LayerNorm -> X (two-pass, fp32, biased
+    // variance).  Eight lanes share a row (lane i of the 8 takes columns
+    // i, i + 8, ...), so a wave normalises 8 rows at once and the row sums
+    // reduce over the 8 lanes with DPP moves.
+    auto sum8 = [](float v) {
+        v += dpp_xor1(v);
+        v += dpp_xor2(v);
+        return v + dpp_mirror8(v);
+    };
+    auto layernorm = [&](const float* Z, int PZ, auto gam, auto bet) {
+        const int j8 = lane & 7;
+        for (int r = wave * 8 + (lane >> 3); r - (lane >> 3) < L; r += SS_THREADS / 8) {
+            const bool live = r < L;
+            const int rr = live ? r : 0;
             float s = 0.f;
-            for (int n = lane; n < D; n += 64) s += Z[r * PZ + n];
-            s = wave_sum<64>(s);
+            for (int n = j8; n < D; n += 8) s += Z[rr * PZ + n];
+            s = sum8(s);
             const float mean = s / (float)D;
             float q = 0.f;
-            for (int n = lane; n < D; n += 64) {
-                const float c = Z[r * PZ + n] - mean;
+            for (int n = j8; n < D; n += 8) {
+                const float c = Z[rr * PZ + n] - mean;
                 q += c * c;
             }
-            q = wave_sum<64>(q);
+            q = sum8(q);
             const float rstd = 1.0f / sqrtf(q / (float)D + p.eps);
-            for (int n = lane; n < D; n += 64) X[r * PX + n] = (Z[r * PZ + n] - mean) * rstd * ld(gam, n) + ld(bet, n);
+            if (live)
+                for (int n = j8; n < D; n += 8) X[r * PX + n] = (Z[r * PZ + n] - mean) * rstd * ld(gam, n) + ld(bet, n);
         }
     };
 
     for (int l = 0; l < p.n_layers; l++) {
         const LayerPtrs& w = p.lw[l];
-        linear(X, PX, D, (const WT*)w.w_qkv, (const WT*)w.b_qkv, 3 * D, B1, P1, nullptr, false);
+        const float* wl = WLb + (size_t)l * LF;
+        const float* wv = wl + (3 * D + D + F) * (D + 4) + D * (F + 4);  // vectors of layer l
+        if constexpr (WL)
+            linear(X, PX, D, wl, D + 4, wv, 3 * D, B1, P1, nullptr, false);
+        else
+            linear(X, PX, D, (const WT*)w.w_qkv, D, (const WT*)w.b_qkv, 3 * D, B1, P1, nullptr, false);
         __syncthreads();
         // attention: four lanes per (head, query), lane s taking keys j = s mod 4
         // of j <= min(i, len - 1); exact two-pass softmax, partials combined
@@ -127,16 +213,27 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
                 }
                 return sc * scale;
             };
+            // this lane's keys j = s4 + 4c (c < 16 covers L <= 64): scores
+            // kept from the max pass for the exponential pass
+            float sc[16];
             float m = -INFINITY;
-            for (int j = s4; j <= nk; j += 4) m = fmaxf(m, score(j));
-            m = fmaxf(m, __shfl_xor(m, 1, WAVE));
-            m = fmaxf(m, __shfl_xor(m, 2, WAVE));
+#pragma unroll
+            for (int c = 0; c < 16; c++) {
+                const int j = s4 + 4 * c;
+                sc[c] = j <= nk ? score(j) : -INFINITY;
+                m = fmaxf(m, sc[c]);
+            }
+            m = fmaxf(m, dpp_xor1(m));
+            m = fmaxf(m, dpp_xor2(m));
             float o[DH];
 #pragma unroll
             for (int t = 0; t < DH; t++) o[t] = 0.f;
             float den = 0.f;
-            for (int j = s4; j <= nk; j += 4) {
-                const float e = expf(score(j) - m);
+#pragma unroll
+            for (int c = 0; c < 16; c++) {
+                const int j = s4 + 4 * c;
+                if (j > nk) break;
+                const float e = expf(sc[c] - m);
                 den += e;
                 const float* v = B1 + j * P1 + 2 * D + h * DH;
 #pragma unroll
@@ -148,12 +245,12 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
                     o[t + 3] = fmaf(e, v4.w, o[t + 3]);
                 }
             }
-            den += __shfl_xor(den, 1, WAVE);
-            den += __shfl_xor(den, 2, WAVE);
+            den += dpp_xor1(den);
+            den += dpp_xor2(den);
 #pragma unroll
             for (int t = 0; t < DH; t++) {
-                o[t] += __shfl_xor(o[t], 1, WAVE);
-                o[t] += __shfl_xor(o[t], 2, WAVE);
+                o[t] += dpp_xor1(o[t]);
+                o[t] += dpp_xor2(o[t]);
             }
             if (s4 == 0) {
                 const float inv = 1.0f / den;
@@ -163,16 +260,31 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
         }
         __syncthreads();
         // z = X + O Wo^T + b_o  (into B1), LayerNorm -> X
-        linear(B2, PX, D, (const WT*)w.w_o, (const WT*)w.b_o, D, B1, P1, X, false);
+        if constexpr (WL)
+            linear(B2, PX, D, wl + 3 * D * (D + 4), D + 4, wv + 3 * D, D, B1, P1, X, false);
+        else
+            linear(B2, PX, D, (const WT*)w.w_o, D, (const WT*)w.b_o, D, B1, P1, X, false);
         __syncthreads();
-        layernorm(B1, P1, (const WT*)w.ln1_g, (const WT*)w.ln1_b);
+        if constexpr (WL)
+            layernorm(B1, P1, wv + 4 * D, wv + 5 * D);
+        else
+            layernorm(B1, P1, (const WT*)w.ln1_g, (const WT*)w.ln1_b);
         __syncthreads();
         // g = GELU(X W1^T + b1) (into B1), z2 = X + g W2^T + b2 (into B2), LayerNorm -> X
-        linear(X, PX, D, (const WT*)w.w_1, (const WT*)w.b_1, F, B1, P1, nullptr, true);
+        if constexpr (WL)
+            linear(X, PX, D, wl + 4 * D * (D + 4), D + 4, wv + 6 * D, F, B1, P1, nullptr, true);
+        else
+            linear(X, PX, D, (const WT*)w.w_1, D, (const WT*)w.b_1, F, B1, P1, nullptr, true);
         __syncthreads();
-        linear(B1, P1, F, (const WT*)w.w_2, (const WT*)w.b_2, D, B2, PX, X, false);
+        if constexpr (WL)
+            linear(B1, P1, F, wl + (4 * D + F) * (D + 4), F + 4, wv + 6 * D + F, D, B2, PX, X, false);
+        else
+            linear(B1, P1, F, (const WT*)w.w_2, F, (const WT*)w.b_2, D, B2, PX, X, false);
         __syncthreads();
-        layernorm(B2, PX, (const WT*)w.ln2_g, (const WT*)w.ln2_b);
+        if constexpr (WL)
+            layernorm(B2, PX, wv + 7 * D + F, wv + 8 * D + F);
+        else
+            layernorm(B2, PX, (const WT*)w.ln2_g, (const WT*)w.ln2_b);
         __syncthreads();
     }
     WT* y = (WT*)p.y + (size_t)b * L * D;
@@ -190,17 +302,34 @@ bool seq_small_supported(int d, int dh, int f, int L, int n_layers) {
            n_layers <= SEQ_MAX_LAYERS && seq_small_lds(d, f, L) <= 64 * 1024;
 }
 
+// Dynamic LDS with every layer's weights copied in (bytes).
+static size_t seq_small_lds_wl(int d, int f, int L, int n_layers) {
+    return seq_small_lds(d, f, L) + (size_t)n_layers * ss_layer_floats(d, f) * sizeof(float);
+}
+
+template <class WT, int DH, bool WL>
+static hipError_t small_launch(const SeqArgs& a, int d, size_t lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        // above 64 KB of dynamic LDS the kernel must be allowed it explicitly
+        static const hipError_t set = hipFuncSetAttribute((const void*)seq_small_kernel<WT, DH, WL>,
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (set != hipSuccess) return set;
+    }
+    hipLaunchKernelGGL((seq_small_kernel<WT, DH, WL>), dim3(a.B), dim3(SS_THREADS), lds, s, a, d);
+    return hipGetLastError();
+}
+
 template <class WT>
 static hipError_t small_mode(int d, int dh, const SeqArgs& a, hipStream_t s) {
-    const size_t lds = seq_small_lds(d, a.F, a.L);
-    dim3 grid(a.B);
+    const size_t lds_wl = seq_small_lds_wl(d, a.F, a.L, a.n_layers);
+    const bool wl = lds_wl <= 160 * 1024;
+    const size_t lds = wl ? lds_wl : seq_small_lds(d, a.F, a.L);
     switch (dh) {
-        case 16: hipLaunchKernelGGL((seq_small_kernel<WT, 16>), grid, dim3(SS_THREADS), lds, s, a, d); break;
-        case 32: hipLaunchKernelGGL((seq_small_kernel<WT, 32>), grid, dim3(SS_THREADS), lds, s, a, d); break;
-        case 64: hipLaunchKernelGGL((seq_small_kernel<WT, 64>), grid, dim3(SS_THREADS), lds, s, a, d); break;
-        default: return hipErrorInvalidValue;
+        case 16: return wl ? small_launch<WT, 16, true>(a, d, lds, s) : small_launch<WT, 16, false>(a, d, lds, s);
+        case 32: return wl ? small_launch<WT, 32, true>(a, d, lds, s) : small_launch<WT, 32, false>(a, d, lds, s);
+        case 64: return wl ? small_launch<WT, 64, true>(a, d, lds, s) : small_launch<WT, 64, false>(a, d, lds, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_seq_small(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s) {
