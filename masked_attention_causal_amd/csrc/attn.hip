@@ -41,6 +41,13 @@ namespace tfl {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
+// max(a, b, c) in one instruction (NaN handling as the file's no-NaN build).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 template <class OpT, int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     constexpr bool F32 = sizeof(OpT) == 4;
@@ -603,10 +610,14 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
                     if (key > myq || key >= len) sc[kb][e] = -INFINITY;
                 }
         }
+        // running max as a chain of three-input maxima (two new values each;
+        // left to itself the compiler spends three instructions per four)
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 8; kb++)
-            mx = fmaxf(fmaxf(mx, fmaxf(sc[kb][0], sc[kb][1])), fmaxf(sc[kb][2], sc[kb][3]));
+        for (int kb = 0; kb < 8; kb++) {
+            mx = max3f(mx, sc[kb][0], sc[kb][1]);
+            mx = max3f(mx, sc[kb][2], sc[kb][3]);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
         // the max over raw scores scales with the (positive) exp2-domain factor;
