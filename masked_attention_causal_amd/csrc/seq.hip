@@ -181,10 +181,12 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint16_t seq_dyn_lds[];
     WT* const Pm = (WT*)seq_dyn_lds;  // 2 * PLENP elements
 
-    // Lane coordinates are re-derived from an opaque copy of the thread id
-    // at every step (refresh_lane below), so per-lane addresses are
-    // recomputed where they are used instead of being hoisted out of the
-    // tile loop and pinned in registers for the whole kernel.
+    // Lane coordinates.  With fp16 weights the compiler may keep per-lane
+    // addresses derived from them in registers across the tile loop (there is
+    // room below the register ceiling); with bf16 weights the staging
+    // registers of the tile loads leave none, so there the coordinates are
+    // re-derived from an opaque copy of the thread id at every step and the
+    // addresses recomputed where they are used.
     int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int c16 = lane & 15, g = lane >> 4;
     const int wave0 = threadIdx.x >> 6;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
     const int b = blockIdx.x * SEQ_SEQS + sq;
     auto refresh_lane = [&]() {
         int t = threadIdx.x;
-        asm volatile("" : "+v"(t));
+        if constexpr (!std::is_same<WT, f16>::value) asm volatile("" : "+v"(t));
         tid = t;
         lane = t & 63;
         wave = t >> 6;
