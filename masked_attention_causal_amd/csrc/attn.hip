@@ -505,7 +505,9 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     static_assert(KT * 2 == 256 && DH * 16 == 256, "one DMA chunk per thread per plane");
     __shared__ __attribute__((aligned(16))) char lds[ST * SB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is made wave-uniform, so the tile skip and mask tests
+    // below are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
     const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
@@ -558,35 +560,46 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 #pragma unroll
     for (int s = 0; s < ST - 1; s++)
         if (loader && s < ntiles) issue(s, s);
-    for (int t = 0; t < ntiles; t++) {
+    // Per-lane LDS byte addresses, fixed for the kernel: this lane's K
+    // fragment in each score block and its V^T chunk for each 32-key group, in
+    // ring buffer 0.  The tile loop below is unrolled over the ST ring buffers,
+    // so a buffer's offset is an immediate of the read.  Each K address goes
+    // through an opaque copy once: the compiler then keeps the eight reads
+    // separate (merged into a two-address read, blocks 512 bytes apart meet on
+    // the same banks) without recomputing their addresses at every tile.
+    const unsigned lds0 = (unsigned)(size_t)(lds_char*)lds;
+    const int koff = c16 * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
+    unsigned kad[8], vad[4];
+#pragma unroll
+    for (int kb = 0; kb < 8; kb++) {
+        kad[kb] = lds0 + kb * 16 * KROW + koff;
+        asm volatile("" : "+v"(kad[kb]));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) vad[cc] = lds0 + KB * (SPLIT ? 2 : 1) + c16 * VROW + (((cc * 4 + g) ^ c16) * 16);
+    // lanes l ^ 16 and l ^ 32 (byte indices for ds_bpermute)
+    const int ix16 = (lane ^ 16) << 2, ix32 = (lane ^ 32) << 2;
+    typedef const __attribute__((address_space(3))) f16x4 lds_f16x4;
+    typedef const __attribute__((address_space(3))) f16x8 lds_f16x8;
+
+    auto tile = [&](const int t, auto bufc) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr unsigned BO = BUF * SB;
         if (t + ST - 2 < ntiles)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"((ST - 2) * NDMA) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (loader && t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
+        if (loader && t + ST - 1 < ntiles) issue(t + ST - 1, (BUF + ST - 1) % ST);
         const int k0 = t * KT;
-        if (k0 > qw0 + 15) continue;
-        const char* ks = lds + (t % ST) * SB;
-        const char* kls = ks + KB;
-        const char* vs = ks + KB * (SPLIT ? 2 : 1);
+        if (k0 > qw0 + 15) return;
         // key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
         f32x4 sc[8];
         f16x4 ka[8], kl[8];
-        const int koff = c16 * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
-            // each block's base goes through an opaque scalar, which keeps the
-            // reads separate: merged into one two-address instruction, blocks
-            // 512 bytes apart would meet on the same banks
-            unsigned kbase = (unsigned)(size_t)(lds_char*)(ks + kb * 16 * KROW);
-            asm volatile("" : "+s"(kbase));
-            ka[kb] = *(const __attribute__((address_space(3))) f16x4*)((const lds_char*)(size_t)kbase + koff);
-            if constexpr (SPLIT) {
-                unsigned lbase = (unsigned)(size_t)(lds_char*)(kls + kb * 16 * KROW);
-                asm volatile("" : "+s"(lbase));
-                kl[kb] = *(const __attribute__((address_space(3))) f16x4*)((const lds_char*)(size_t)lbase + koff);
-            }
+            ka[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO);
+            if constexpr (SPLIT) kl[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO + KB);
         }
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
@@ -618,13 +631,13 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
             mx = max3f(mx, sc[kb][0], sc[kb][1]);
             mx = max3f(mx, sc[kb][2], sc[kb][3]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
         // the max over raw scores scales with the (positive) exp2-domain factor;
         // the scale then folds into one fma per score before the exponential
         const float m_new = fmaxf(m_run, mx * sl2);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
         m_run = m_new;
         o *= alpha;
         lsum *= alpha;
@@ -636,12 +649,17 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
                 pb[e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc][e], sl2, -m_use));
                 pb[4 + e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc + 1][e], sl2, -m_use));
             }
-            const int r = c16;
-            const f16x8 va = *(const f16x8*)(vs + r * VROW + (((cc * 4 + g) ^ (r & 15)) * 16));
+            const f16x8 va = *(lds_f16x8*)(size_t)(vad[cc] + BO);
             o = mfma_16x16x32(va, pb, o);
             lsum = mfma_16x16x32(ones, pb, lsum);
         }
+    };
+    for (int t = 0; t < ntiles; t += ST) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < ntiles) tile(t + 2, std::integral_constant<int, 2>{});
     }
+    static_assert(ST == 3, "the tile loop is unrolled over three ring buffers");
 
     // lsum row 0 (lanes 0..15, element 0) holds the weight sum of query c16
     const float l = __shfl(lsum[0], c16, WAVE);
