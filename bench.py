@@ -29,6 +29,10 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+# Transcendental issue: 256 CUs x 4 SIMDs x 32 fp32 lanes per clock (the
+# 157.3 TFLOP/s fp32 vector peak over 2 FLOPs per FMA at 2.4 GHz), with
+# v_exp_f32 at a quarter of the FMA rate: 1.966e13 exponentials per second.
+PEAK_EXP_TPS = 256 * 4 * 32 / 4 * 2.4e9 / 1e12
 
 
 def allowed_pairs(lens, L):
@@ -139,6 +143,17 @@ def roofline(w, stage, lens, avg_ms, plan):
     t_mfma = flops / (peak * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     sec = avg_ms / 1e3
+    # attention also needs one exponential per allowed (query, key) pair and
+    # head; at small head dims that, not the products, is the bound
+    exps = w.H * allowed_pairs(lens, w.L) if stage == "attn" else 0
+    t_exp = exps / (PEAK_EXP_TPS * 1e12)
+    if t_exp > max(t_mfma, t_hbm):
+        ach = exps / sec / 1e12
+        return {"bound": "alu", "achieved": round(ach, 3), "peak": round(PEAK_EXP_TPS, 3), "unit": "Texp/s",
+                "frac": round(ach / PEAK_EXP_TPS, 4), "traffic": None, "kernel_stage": stage,
+                "avg_launch_us": round(avg_ms * 1e3, 2), "algorithmic_exps_per_launch": exps,
+                "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                "mfma_frac": round(flops / sec / 1e12 / peak, 4)}
     if t_mfma >= t_hbm:
         ach = flops / sec / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",

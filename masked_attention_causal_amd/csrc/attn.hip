@@ -569,11 +569,18 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     // the same banks) without recomputing their addresses at every tile.
     const unsigned lds0 = (unsigned)(size_t)(lds_char*)lds;
     const int koff = c16 * KROW + (((g >> 1) ^ (c16 >> 3)) * 16) + (g & 1) * 8;
-    unsigned kad[8], vad[4];
+    // The lo plane's reads get addresses of their own (opaque as well): from
+    // the hi addresses plus 4 KB the compiler forms two-address reads of a hi
+    // and a lo fragment, which meet on the same banks.
+    unsigned kad[8], kadl[SPLIT ? 8 : 1], vad[4];
 #pragma unroll
     for (int kb = 0; kb < 8; kb++) {
         kad[kb] = lds0 + kb * 16 * KROW + koff;
         asm volatile("" : "+v"(kad[kb]));
+        if constexpr (SPLIT) {
+            kadl[kb] = lds0 + KB + kb * 16 * KROW + koff;
+            asm volatile("" : "+v"(kadl[kb]));
+        }
     }
 #pragma unroll
     for (int cc = 0; cc < 4; cc++) vad[cc] = lds0 + KB * (SPLIT ? 2 : 1) + c16 * VROW + (((cc * 4 + g) ^ c16) * 16);
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
             ka[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO);
-            if constexpr (SPLIT) kl[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO + KB);
+            if constexpr (SPLIT) kl[kb] = *(lds_f16x4*)(size_t)(kadl[kb] + BO);
         }
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
