@@ -486,8 +486,11 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
 // With 16-dim heads the products are a small part of the work and the
 // softmax arithmetic dominates ("KernelForge", "Challenges": the 100k-token
 // shape), so this variant trims VALU work per score: 128-key tiles per
-// barrier (32 scores per lane), the scale folded into one FMA feeding the
-// hardware exp2, and the softmax row sums taken on the MFMA by a ones row
+// barrier (32 scores per lane); keys written by the QKV projection already
+// multiplied by log2(e)/sqrt(dh) and score products accumulated onto the
+// negated row reference, so each score goes straight into the hardware exp2;
+// the reference raised only when a tile passes it by a margin (no per-tile
+// rescaling); and the softmax row sums taken on the MFMA by a ones row
 // appended to V^T (the sum of the same fp16 weights that multiply V).
 // Queries per workgroup of the head-dim-16 kernel: 8 waves of 16, so each
 // staged K/V tile serves 128 queries (the first four waves load it).
@@ -551,8 +554,15 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     f32x4 lsum = f32x4{0.f, 0.f, 0.f, 0.f};          // row 0 of (ones . P^T): the weight sums
     const f16 one = (f16)(c16 == 0 ? 1.0f : 0.0f);
     const f16x8 ones = {one, one, one, one, one, one, one, one};
-    float m_run = -INFINITY;
-    const float sl2 = p.scale_log2;
+    // Keys arrive multiplied by log2(e)/sqrt(dh), and each score product starts
+    // from -m_ref, so the MFMA leaves the exponent of exp2 itself.  m_ref (per
+    // query) is the exact row max of the first key tile (every wave computes
+    // tile 0, and key 0 is visible to every query); later it is raised only
+    // when a tile's max passes it by more than RESCALE, so the row's largest
+    // weight stays in [1, 2^RESCALE]: the online softmax is exact for any such
+    // reference, and no weight underflows that the running max would keep.
+    constexpr float RESCALE = 8.f;
+    float m_ref = 0.f;
 
     // waves 0-3 load the tiles (one chunk per thread per plane); the others
     // issue no loads, so their waits below return at once
@@ -608,9 +618,10 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
             ka[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO);
             if constexpr (SPLIT) kl[kb] = *(lds_f16x4*)(size_t)(kadl[kb] + BO);
         }
+        const f32x4 c0 = f32x4{-m_ref, -m_ref, -m_ref, -m_ref};
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
-            sc[kb] = mfma_16x16x16(ka[kb], qh, f32x4{0.f, 0.f, 0.f, 0.f});
+            sc[kb] = mfma_16x16x16(ka[kb], qh, c0);
             if constexpr (SPLIT) {
                 sc[kb] = mfma_16x16x16(kl[kb], qh, sc[kb]);
                 sc[kb] = mfma_16x16x16(ka[kb], ql, sc[kb]);
@@ -640,21 +651,27 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
         }
         mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
         mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
-        // the max over raw scores scales with the (positive) exp2-domain factor;
-        // the scale then folds into one fma per score before the exponential
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
-        m_run = m_new;
-        o *= alpha;
-        lsum *= alpha;
+        // mx: the tile's largest exponent of this lane's query (-inf if none)
+        if (t == 0) {
+            m_ref = mx;
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++) sc[kb] -= mx;
+        } else if (__ballot(mx > RESCALE) != 0) {
+            const float dl = fmaxf(mx, 0.f);
+            m_ref += dl;
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++) sc[kb] -= dl;
+            const float alpha = __builtin_amdgcn_exp2f(-dl);
+            o *= alpha;
+            lsum *= alpha;
+        }
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) {
             f16x8 pb;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                pb[e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc][e], sl2, -m_use));
-                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(fmaf(sc[2 * cc + 1][e], sl2, -m_use));
+                pb[e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc][e]);
+                pb[4 + e] = (f16)__builtin_amdgcn_exp2f(sc[2 * cc + 1][e]);
             }
             const f16x8 va = *(lds_f16x8*)(size_t)(vad[cc] + BO);
             o = mfma_16x16x32(va, pb, o);

@@ -170,9 +170,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
                         (which == 0 ? p.Q : p.Kd)[o] = v;
                     } else {
                         f16* dst = (f16*)(which == 0 ? p.Q : p.Kd);
-                        const f16 hv = (f16)v;
+                        const float vs = (which == 1 && p.kscale != 0.f) ? v * p.kscale : v;
+                        const f16 hv = (f16)vs;
                         dst[o] = hv;
-                        if (p.split) dst[(size_t)M * p.d + o] = (f16)(v - (float)hv);
+                        if (p.split) dst[(size_t)M * p.d + o] = (f16)(vs - (float)hv);
                     }
                 } else if constexpr (EPI == EPI_GELU) {
                     ((OpT*)p.out)[(size_t)m * N + n] = from_f32<OpT>(gelu_erf(v));

@@ -182,11 +182,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe_kernel(GemmArgs p) {
                 const size_t bh = (size_t)b * p.H + h;
                 if (which < 2) {
                     f16* dst = (f16*)(which == 0 ? p.Q : p.Kd) + (bh * p.L + pos) * p.dh + t;
+                    const float ks = (which == 1 && p.kscale != 0.f) ? p.kscale : 1.f;
                     f16x4 hv, lv;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        hv[e] = (f16)v[e];
-                        lv[e] = (f16)(v[e] - (float)hv[e]);
+                        const float vs = v[e] * ks;
+                        hv[e] = (f16)vs;
+                        lv[e] = (f16)(vs - (float)hv[e]);
                     }
                     *(f16x4*)dst = hv;
                     if (p.split) *(f16x4*)(dst + (size_t)M * p.d) = lv;

@@ -29,6 +29,10 @@ struct GemmArgs {
     void* Vt;
     int L, Lp, H, dh, d;
     int split;
+    // EPI_QKV: K is written multiplied by kscale (0 means 1).  The head-dim-16
+    // attention kernel takes keys pre-multiplied by log2(e)/sqrt(dh), so its
+    // score products come out in the exp2 domain.
+    float kscale;
     // EPI_GELU: out [M, N] operand dtype
     void* out;
     // EPI_RES: Z = acc + bias + R, [M, N] fp32
@@ -45,7 +49,7 @@ struct AttnArgs {
     void* O;           // [B*L, d] operand dtype, head h at columns h*dh
     const int32_t* lens;
     int B, H, L, Lp, d;
-    float scale_log2;  // log2(e) / sqrt(dh)
+    float scale_log2;  // log2(e) / sqrt(dh); the head-dim-16 kernel reads K already multiplied by it
 };
 
 // Weight pointers of one layer (same fields as tfl_layer).

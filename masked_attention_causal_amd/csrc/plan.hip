@@ -209,6 +209,8 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         // Scores of the first layer see the raw input (up to 1e3 in scale):
         // fp32-accurate there; LayerNorm bounds every later layer's input.
         g.split = l == 0;
+        // the head-dim-16 attention kernel (16-bit modes) reads K pre-scaled
+        if (P.mode != MODE_F32 && P.dh == 16) g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
         {
             Timed tm(T, TFL_STAGE_QKV, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_QKV, g, s))) != hipSuccess) return e;
