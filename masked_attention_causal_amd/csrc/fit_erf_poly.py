@@ -1,6 +1,8 @@
-"""Coefficients of the short-range erf polynomial in common.h (erf_small).
+"""Coefficients of the short-range GELU polynomial in common.h (gelu_poly).
 
-erf(x) = x * P(x^2) on |x| <= 1, P of degree 5.  The coefficients come from
+erf(x) = x * P(x^2) on |x| <= 1, P of degree 5; the kernel evaluates
+GELU(h) = h/2 + u R(u), u = h^2, R(u) = P(u/2) / (2 sqrt(2)), so it prints
+both P and R (coefficient k of R is that of P times 2^-k / (2 sqrt(2))).  The coefficients come from
 an iteratively reweighted least-squares fit of erf(x)/x against x^2 on 400
 Chebyshev nodes that drives down the largest relative error (about 4e-8 in
 exact arithmetic); evaluated by Horner's rule in fp32 the result stays within
@@ -41,5 +43,7 @@ def fp32_ulp_error(c):
 
 if __name__ == "__main__":
     c, rel = fit()
-    print("coefficients:", ", ".join(f"{float(np.float32(v))!r}f" for v in c))
+    print("erf coefficients P (degree 0..5):", ", ".join(f"{float(np.float32(v))!r}f" for v in c))
+    r = [v / (2 * math.sqrt(2) * 2 ** k) for k, v in enumerate(c)]
+    print("GELU coefficients R (degree 0..5):", ", ".join(f"{np.float32(v)}f" for v in r))
     print(f"max relative error (exact arithmetic) {rel:.3g}; fp32 Horner {fp32_ulp_error(c):.2f} ulp")
