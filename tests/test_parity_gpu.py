@@ -50,6 +50,32 @@ def test_small_shapes(w, scale):
         assert_gate(y, oracle_forward(inp), f"{w.name} seed {seed} scale {scale}")
 
 
+# ---------------------------------------------------------------- head-dim-16 softmax reference
+
+RAMP = W("ramp_dh16_l640", 2, 64, 4, 128, 2, 640, "f16", 1, 640, 1.0)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("direction", ["up", "down"])
+def test_attention_reference_rescaling(dtype, direction):
+    """Rows of x scaled by a monotone ramp along the sequence: in the first
+    layer a query's largest score then grows (or shrinks) from one 128-key
+    tile to the next by tens of exp2 units, so the head-dim-16 kernel's row
+    reference is raised at most tiles (or never after the first), and late
+    keys carry weights far below the row's largest."""
+    from dataclasses import replace
+    w = replace(RAMP, dtype=dtype)
+    ramp = np.linspace(0.05, 1.0, w.L)
+    if direction == "down":
+        ramp = ramp[::-1].copy()
+    for seed, top in ((0, 60.0), (1, 120.0)):
+        inp = _case(w, seed, 1.0)
+        inp.x = synth.round_to(synth.to_f64(inp.x, dtype) * (top * ramp)[None, :, None], dtype)
+        inp.lens[:] = [w.L, w.L - 77]
+        say(f"[ramp] {dtype} {direction} seed={seed} top={top} lens={inp.lens.tolist()}")
+        assert_gate(gpu_forward(inp, force_path="tiled"), oracle_forward(inp), f"ramp {dtype} {direction} top {top}")
+
+
 # ---------------------------------------------------------------- the five workloads at full size
 
 TINY = synth.WORKLOADS["tiny_d32_b4_l32"]
