@@ -326,7 +326,8 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     static_assert(4 * 16 == ATT_BQ, "planner and kernel disagree on the query tile");
     __shared__ __attribute__((aligned(16))) char lds[ST * SB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave-uniform wave index: the tile skip and mask tests are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
     const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // heaviest query tiles first
     const int h = blockIdx.y, b = blockIdx.z;
@@ -387,6 +388,7 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale_log2;
+    const int ix16 = (lane ^ 16) << 2, ix32 = (lane ^ 32) << 2;  // ds_bpermute byte indices
 
 #pragma unroll
     for (int s = 0; s < ST - 1; s++)
@@ -421,33 +423,37 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
                 }
             }
         }
-        // running max on raw scores (scale > 0), then one FMA per score into exp2
+        // running max on raw scores (scale > 0), then one FMA per score into
+        // the hardware exp2 (its flushing of results below 2^-126 is far
+        // below the fp16 rounding of the weights and next to a row sum >= 1)
         const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
+                    if (key > myq || key >= len) sc[kb][e] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float v = sc[kb][e];
-                if (need_mask) {
-                    const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
-                    if (key > myq || key >= len) v = -INFINITY;
-                }
-                sc[kb][e] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        for (int kb = 0; kb < 4; kb++) {
+            mx = max3f(mx, sc[kb][0], sc[kb][1]);
+            mx = max3f(mx, sc[kb][2], sc[kb][3]);
+        }
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
         const float m_new = fmaxf(m_run, mx * sl2);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
         m_run = m_new;
         float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float pv = exp2f(fmaf(sc[kb][e], sl2, -m_use));
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], sl2, -m_use));
                 sc[kb][e] = pv;
                 ls += pv;
             }
