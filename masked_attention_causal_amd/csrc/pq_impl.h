@@ -518,14 +518,16 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                 mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
                 const float m_new = fmaxf(m_run, mx);
                 const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = exp2f(m_run - m_use);
+                // hardware exp2: its flushing below 2^-126 is far below the fp16
+                // rounding of the weights and next to a row sum >= 1
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
                 m_run = m_new;
                 float ls = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const float pv = exp2f(sc[kb][e] - m_use);
+                        const float pv = __builtin_amdgcn_exp2f(sc[kb][e] - m_use);
                         sc[kb][e] = pv;
                         ls += pv;
                     }
@@ -586,7 +588,7 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
             for (int s = 0; s < ns; s++) {
                 const float2 ml = p.ML[(slot0 + s) * PQ_RT + r];
                 if (ml.x == -INFINITY) continue;
-                const float w = exp2f(ml.x - M);
+                const float w = __builtin_amdgcn_exp2f(ml.x - M);
                 lsum += w * ml.y;
                 const float* op = p.Op + ((slot0 + s) * PQ_RT + r) * DH + qd;
 #pragma unroll
