@@ -698,18 +698,28 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
 #pragma unroll
             for (int rb = 0; rb < 4; rb++) ga[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         mm_rows<2, D>(ga, (const WT*)w.w_1, D, f0, 0, act, TL::ALD, c16, g);
+        // bias, then GELU on all 32 values of the lane at once: the
+        // short-range polynomial when the whole wave is in its range
 #pragma unroll
         for (int nb = 0; nb < 2; nb++) {
             float bv[4];
             load4_f32((const WT*)w.b_1 + f0 + 16 * nb + 4 * g, bv);
 #pragma unroll
+            for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) ga[nb][rb][e] += bv[e];
+        }
+        static_assert(sizeof(ga) == 32 * sizeof(float), "ga is 32 packed floats");
+        gelu_inplace<32>((float*)&ga[0][0]);
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++)
+#pragma unroll
             for (int rb = 0; rb < 4; rb++) {
                 f16x4 hv;
 #pragma unroll
-                for (int e = 0; e < 4; e++) hv[e] = (f16)gelu_erf(ga[nb][rb][e] + bv[e]);
+                for (int e = 0; e < 4; e++) hv[e] = (f16)ga[nb][rb][e];
                 *(f16x4*)(gb + (16 * rb + c16) * TL::GLD + wave * (PQ_FC / 4) + 16 * nb + 4 * g) = hv;
             }
-        }
         __syncthreads();
         if constexpr (NB == 1) {
             mm_rows<1, PQ_FC>(y2, (const WT*)w.w_2, p.F, n0, c * PQ_FC, gb, TL::GLD, c16, g);
