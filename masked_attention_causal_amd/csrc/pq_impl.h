@@ -136,6 +136,32 @@ __device__ __forceinline__ void mm_rows(f32x4 (&acc)[NBW][4], const WT* W, int l
     }
 }
 
+// mm_rows split in two, for products whose weights are fetched ahead: the
+// weight fragments of KS 32-wide K slices (rows n0 + 16 nb + c16, columns
+// k0 + 32 ks + 8 g), and the products of such fragments with the tile rows.
+template <int NBW, int KS, class WT>
+__device__ __forceinline__ void frags_load(f16x8 (&a)[KS][NBW], const WT* W, int ldw, int n0, int k0, int c16, int g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++)
+            a[ks][nb] = load8_as_f16(W + (size_t)(n0 + 16 * nb + c16) * ldw + k0 + ks * 32 + 8 * g);
+}
+template <int NBW, int KS>
+__device__ __forceinline__ void frags_mma(f32x4 (&acc)[NBW][4], const f16x8 (&a)[KS][NBW], const f16* act, int ald,
+                                          int c16, int g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        f16x8 bf[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) bf[rb] = *(const f16x8*)(act + (16 * rb + c16) * ald + ks * 32 + 8 * g);
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) acc[nb][rb] = mfma_16x16x32(a[ks][nb], bf[rb], acc[nb][rb]);
+    }
+}
+
 // Three-pass version for fp32 weights and a hi/lo activation pair:
 // main += Wh*Ah, lo += Wl*Ah + Wh*Al (lo parts carry a 2^11 scale).
 template <int NBW, int K>
@@ -688,10 +714,21 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) y2[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nch = p.F / PQ_FC;
+    // Up to d = 128 the W2 fragments of a chunk are fetched before its W1
+    // products and GELU, so that round trip overlaps them instead of
+    // following the barrier (at d = 256 the registers they need would spill).
+    constexpr bool PRE = NB <= 2;
+    constexpr int NBW2 = NB == 1 ? 1 : 2, NH = NB == 1 ? 1 : NB / 2;
+    f16x8 a2[PRE ? NH : 1][PQ_FC / 32][NBW2];
 #pragma unroll 1
     for (int c = 0; c < nch; c++) {
         f16* gb = gs + (c & 1) * PQ_RT * TL::GLD;
         const int f0 = c * PQ_FC + wave * (PQ_FC / 4);
+        if constexpr (PRE) {
+#pragma unroll
+            for (int hh = 0; hh < NH; hh++)
+                frags_load<NBW2, PQ_FC / 32>(a2[hh], (const WT*)w.w_2, p.F, n0 + 32 * hh, c * PQ_FC, c16, g);
+        }
         f32x4 ga[2][4];
 #pragma unroll
         for (int nb = 0; nb < 2; nb++)
@@ -722,12 +759,15 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
             }
         __syncthreads();
         if constexpr (NB == 1) {
-            mm_rows<1, PQ_FC>(y2, (const WT*)w.w_2, p.F, n0, c * PQ_FC, gb, TL::GLD, c16, g);
+            frags_mma<1, PQ_FC / 32>(y2, a2[0], gb, TL::GLD, c16, g);
+        } else if constexpr (PRE) {
+            f32x4 (&yy)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&y2[0]);
+            frags_mma<2, PQ_FC / 32>(yy, a2[0], gb, TL::GLD, c16, g);
         } else {
 #pragma unroll
-            for (int half = 0; half < NB / 2; half++) {
-                f32x4 (&yy)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&y2[2 * half]);
-                mm_rows<2, PQ_FC>(yy, (const WT*)w.w_2, p.F, n0 + 32 * half, c * PQ_FC, gb, TL::GLD, c16, g);
+            for (int hh = 0; hh < NB / 2; hh++) {
+                f32x4 (&yy)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&y2[2 * hh]);
+                mm_rows<2, PQ_FC>(yy, (const WT*)w.w_2, p.F, n0 + 32 * hh, c * PQ_FC, gb, TL::GLD, c16, g);
             }
         }
     }
