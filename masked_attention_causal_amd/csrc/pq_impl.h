@@ -653,6 +653,12 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     const int n0 = wave * (D / 4);          // this wave's output features
     const bool last = l == p.n_layers - 1;
 
+    // Up to d = 128 the out-projection's weight fragments are fetched before
+    // the merge of the attention partials, so the two memory waits overlap.
+    constexpr bool PRE = NB <= 2;
+    constexpr int NBWO = NB == 1 ? 1 : 2;
+    f16x8 ao[PRE ? D / 32 : 1][NBWO];
+    if constexpr (PRE) frags_load<NBWO, D / 32>(ao, (const WT*)w.w_o, D, n0, 0, c16, g);
     merge_att<WT, D, DH>(p, b, t, act, tid);
     __syncthreads();
 
@@ -662,7 +668,10 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) z[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NB == 1) {
+    if constexpr (PRE) {
+        f32x4 (&zz)[NBWO][4] = *reinterpret_cast<f32x4(*)[NBWO][4]>(&z[0]);
+        frags_mma<NBWO, D / 32>(zz, ao, act, TL::ALD, c16, g);
+    } else if constexpr (NB == 1) {
         mm_rows<1, D>(z, (const WT*)w.w_o, D, n0, 0, act, TL::ALD, c16, g);
     } else {
 #pragma unroll
@@ -717,7 +726,6 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     // Up to d = 128 the W2 fragments of a chunk are fetched before its W1
     // products and GELU, so that round trip overlaps them instead of
     // following the barrier (at d = 256 the registers they need would spill).
-    constexpr bool PRE = NB <= 2;
     constexpr int NBW2 = NB == 1 ? 1 : 2, NH = NB == 1 ? 1 : NB / 2;
     f16x8 a2[PRE ? NH : 1][PQ_FC / 32][NBW2];
 #pragma unroll 1
