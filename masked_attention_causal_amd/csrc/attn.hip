@@ -655,14 +655,21 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
             mx = max3f(mx, sc[kb][0], sc[kb][1]);
             mx = max3f(mx, sc[kb][2], sc[kb][3]);
         }
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
-        // mx: the tile's largest exponent of this lane's query (-inf if none)
+        // mx: the largest exponent among this lane's 32 scores.  The four
+        // lanes of a query share its reference (their weights meet in one
+        // MFMA), so the row max over them is formed only where the reference
+        // is set or raised; the common path needs just this lane's test.
+        auto row_max = [&](float v) __attribute__((always_inline)) {
+            v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(v))));
+            return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(v))));
+        };
         if (t == 0) {
+            mx = row_max(mx);
             m_ref = mx;
 #pragma unroll
             for (int kb = 0; kb < 8; kb++) sc[kb] -= mx;
         } else if (__ballot(mx > RESCALE) != 0) {
+            mx = row_max(mx);
             const float dl = fmaxf(mx, 0.f);
             m_ref += dl;
 #pragma unroll
