@@ -247,6 +247,54 @@ def test_gpu_batch_independence_and_determinism():
         assert np.array_equal(gpu_forward(sub)[0], y[b])
 
 
+# ---------------------------------------------------------------- graph capture
+
+GRAPH = W("graph_d128_dh64", 2, 128, 2, 256, 2, 64, "f16", 1, 64, 1.0)
+
+
+@pytest.mark.parametrize("path", ["seq", "pq", "tiled"])
+def test_graph_capture_replays(path):
+    """The forward issues only kernels on the caller's stream (no host sync,
+    no memset), so it can be captured into a HIP graph: every replay, with
+    new inputs copied into the captured buffers and eager forwards on other
+    buffers in between, equals the eager forward on the same inputs."""
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    w = GRAPH
+    inps = [_case(w, seed) for seed in (0, 1, 2)]
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inps[0].layers]
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=path)
+    assert enc.plan_path == path, enc.plan_name
+    xs = [tfl.to_device(i.x, w.dtype) for i in inps]
+    ls = [torch.from_numpy(i.lens).cuda() for i in inps]
+    eager = [enc.forward(x, l).clone() for x, l in zip(xs, ls)]
+    torch.cuda.synchronize()
+
+    x, lens, y = xs[0].clone(), ls[0].clone(), torch.empty_like(xs[0])
+    ws = torch.empty(max(enc.handle.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        enc.forward(x, lens, y, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        enc.forward(x, lens, y, ws)
+    other = torch.empty_like(y)
+    for r, k in enumerate((1, 0, 2, 1)):
+        x.copy_(xs[k])
+        lens.copy_(ls[k])
+        y.zero_()
+        graph.replay()
+        enc.forward(xs[(k + 1) % 3], ls[(k + 1) % 3], other)   # eager work on other buffers
+        torch.cuda.synchronize()
+        say(f"[graph] {path} replay {r} inputs {k}")
+        assert torch.equal(y, eager[k]), f"{path} replay {r}"
+        assert torch.equal(other, eager[(k + 1) % 3])
+
+
 # ---------------------------------------------------------------- error statuses through the ABI
 
 
