@@ -14,6 +14,41 @@
 
 namespace tfl {
 
+namespace {
+
+// Four consecutive stored values as fp32 (one 8- or 16-byte load).
+__device__ __forceinline__ void ld4(const float* p, float (&v)[4]) {
+    const float4 t = *(const float4*)p;
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void ld4(const f16* p, float (&v)[4]) {
+    const f16x4 t = *(const f16x4*)p;
+#pragma unroll
+    for (int e = 0; e < 4; e++) v[e] = (float)t[e];
+}
+__device__ __forceinline__ void ld4(const bf16* p, float (&v)[4]) {
+    const uint2 t = *(const uint2*)p;
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+}
+// Four values stored in T, round to nearest even (one 8- or 16-byte store).
+template <class T>
+__device__ __forceinline__ void st4(T* p, const float (&v)[4]) {
+    if constexpr (sizeof(T) == 4) {
+        *(float4*)p = float4{v[0], v[1], v[2], v[3]};
+    } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const T t = from_f32<T>(v[e]);
+            h[e] = *(const uint16_t*)&t;
+        }
+        *(uint2*)p = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    }
+}
+
+}  // namespace
+
 bool ln_shape(int d, int* lanes_per_row, int* chunks) {
     if (d <= 0 || d % 4 != 0) return false;
     const int q = d / 4;
@@ -57,18 +92,14 @@ __global__ __launch_bounds__(256) void ln_kernel(const float* __restrict__ Z, co
 #pragma unroll
     for (int c = 0; c < NC; c++) {
         const int col = (c * LPR + sub) * 4;
-        float o[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+        float o[4] = {v[c].x, v[c].y, v[c].z, v[c].w}, ga[4], be[4];
+        ld4(gamma + col, ga);
+        ld4(beta + col, be);
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = o[e] * rstd * to_f32(gamma[col + e]) + to_f32(beta[col + e]);
+        for (int e = 0; e < 4; e++) o[e] = o[e] * rstd * ga[e] + be[e];
         if (Xo) *(float4*)(Xo + row * d + col) = float4{o[0], o[1], o[2], o[3]};
-        if (Ao) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) Ao[row * d + col + e] = from_f32<OpT>(o[e]);
-        }
-        if (Y) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) Y[row * d + col + e] = from_f32<PT>(o[e]);
-        }
+        if (Ao) st4(Ao + row * d + col, o);
+        if (Y) st4(Y + row * d + col, o);
     }
 }
 
