@@ -167,6 +167,18 @@ def roofline(w, stage, lens, avg_ms, plan):
             "algorithmic_bytes_per_launch": nbytes}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, target_s=15.0):
     """The fp64 oracle, as it is, on a bounded sample of the same inputs."""
     import numpy as np
@@ -182,7 +194,7 @@ def cpu_baseline(w, inp, target_s=15.0):
         oracle.forward(inp.x64(), inp.lens, inp.layers64(), w.H)
         dt = time.perf_counter() - t0
         return {"value": round(1.0 / dt, 4), "unit": "sequences/s", "cores": threads, "kind": "oracle",
-                "sample": f"the whole batch-1 workload once ({dt:.2f} s)"}
+                "cpu": cpu_model(), "sample": f"the whole batch-1 workload once ({dt:.2f} s)"}
     n0 = min(w.B, 16)
     sub = synth.subset(inp, np.arange(n0))
     t0 = time.perf_counter()
@@ -195,7 +207,7 @@ def cpu_baseline(w, inp, target_s=15.0):
     oracle.forward(x64, sub.lens, l64, w.H)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "sequences/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {w.B} sequences of the same seeded batch, {dt:.1f} s"}
+            "cpu": cpu_model(), "sample": f"first {n} of {w.B} sequences of the same seeded batch, {dt:.1f} s"}
 
 
 def main():
@@ -275,6 +287,19 @@ def main():
     roof["launches_timed"] = dom_n
     roof["traffic"] = measured_traffic(dom, name, enc.plan_name, w)
 
+    # per-forward distribution, in a pass of its own after the timed region
+    # (one event pair per forward; the timed region above has none of these)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        enc.forward(x, lens, y, ws)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+    pick = lambda q: round(per_us[min(len(per_us) - 1, int(q * len(per_us)))], 2)
+    dist = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "forwards": len(per_us)}
+
     # whole-forward roofline figure for context
     tot_flops = 0.0
     for st in (("fused",) if enc.plan_path in ("seq", "pq") else ("qkv", "attn", "out", "ffn1", "ffn2")):
@@ -303,6 +328,7 @@ def main():
         "roofline": roof,
         "forward_tflops": round(fwd_tflops, 2),
         "stage_ms_per_forward": {k: round(v, 4) for k, v in survey.items()},
+        "us_per_forward_dist": dist,
         "cold_first_call_ms": round(cold_ms, 2),
         "cpu_baseline": cpu,
     }
