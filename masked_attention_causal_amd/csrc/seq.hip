@@ -390,15 +390,24 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 #pragma unroll
                 for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = bv;
             }
+            // Fragments of the next 32-wide K slice are read before this
+            // slice's products, in their own registers (left to the scheduler
+            // alone, this step's reads were each waited on before their
+            // product).
+            f16x8 fa[2][NQB];
 #pragma unroll
-            for (int kk = 0; kk < NKC; kk++)
+            for (int ob = 0; ob < NQB; ob++) fa[0][ob] = afrag16<CPR>(W, ob, c16, g, sw);
 #pragma unroll
-                for (int ob = 0; ob < NQB; ob++) {
-                    const f16x8 a = afrag16<CPR>(W, ob, c16, kk * 4 + g, sw);
+            for (int kk = 0; kk < NKC; kk++) {
+                if (kk + 1 < NKC) {
 #pragma unroll
-                    for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = mfma_16x16x32(a, XB[kk][tb], acc[ob][tb]);
+                    for (int ob = 0; ob < NQB; ob++) fa[(kk + 1) & 1][ob] = afrag16<CPR>(W, ob, c16, (kk + 1) * 4 + g, sw);
                 }
-            pipeline_order<NQB + NKC * NQB, NKC * NQB * TPW, TPW, SEQ_AHEAD>();
+#pragma unroll
+                for (int ob = 0; ob < NQB; ob++)
+#pragma unroll
+                    for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = mfma_16x16x32(fa[kk & 1][ob], XB[kk][tb], acc[ob][tb]);
+            }
             if (d.kind == 0) {
 #pragma unroll
                 for (int ob = 0; ob < NQB; ob++)
