@@ -391,7 +391,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                 for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = bv;
             }
             // Fragments of the next 32-wide K slice are read before this
-            // slice's products, in their own registers (left to the scheduler
+            // slice's products, in their own registers, and the issue order
+            // below keeps a few more reads in flight (left to the scheduler
             // alone, this step's reads were each waited on before their
             // product).
             f16x8 fa[2][NQB];
@@ -408,6 +409,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) acc[ob][tb] = mfma_16x16x32(fa[kk & 1][ob], XB[kk][tb], acc[ob][tb]);
             }
+            pipeline_order<NQB + NKC * NQB, NKC * NQB * TPW, TPW, NQB + 4>();
             if (d.kind == 0) {
 #pragma unroll
                 for (int ob = 0; ob < NQB; ob++)
