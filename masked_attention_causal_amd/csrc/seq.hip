@@ -468,25 +468,19 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                         ql[kk][tb][4 + e] = (f16)(c - (float)ch);
                     }
                 }
-            // Two 32-key chunks, online softmax across them (running max and sum
-            // per query, live in the 4 lanes that share the query).
-            f32x4 o[NQB][TPW];
-            float mrun[TPW], lrun[TPW];
-#pragma unroll
-            for (int tb = 0; tb < TPW; tb++) {
-                mrun[tb] = -INFINITY;
-                lrun[tb] = 0.f;
-#pragma unroll
-                for (int db = 0; db < NQB; db++) o[db][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            // At most two 32-key chunks: the scores of both are formed first,
+            // then one row max, the weights and the P V products -- a plain
+            // softmax over the row, with one cross-lane reduction and no
+            // rescaling in the dependent chain.
+            f32x4 o[NQB][TPW], s[2][2][TPW];
+            float lrun[TPW];
 #pragma unroll
             for (int cc = 0; cc < 2; cc++) {
                 if (cc < nch) {
-                    f32x4 s[2][TPW];
 #pragma unroll
                     for (int hb = 0; hb < 2; hb++) {
 #pragma unroll
-                        for (int tb = 0; tb < TPW; tb++) s[hb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int tb = 0; tb < TPW; tb++) s[cc][hb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
                         // LDS row kbase + cc * 32 + hb * 16 + c16 holds key sigma32(hb * 16 + c16)
                         const int kblk = (kbase + cc * 32) / 16 + hb;
 #pragma unroll
@@ -494,10 +488,10 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                             const f16x8 a = afrag16<KCPR>(Kh, kblk, c16, kk * 4 + g, swk);
 #pragma unroll
                             for (int tb = 0; tb < TPW; tb++) {
-                                s[hb][tb] = mfma_16x16x32(a, qh[kk][tb], s[hb][tb]);
+                                s[cc][hb][tb] = mfma_16x16x32(a, qh[kk][tb], s[cc][hb][tb]);
                                 if (split) {
-                                    s[hb][tb] = mfma_16x16x32(afrag16<KCPR>(Kl, kblk, c16, kk * 4 + g, swk), qh[kk][tb], s[hb][tb]);
-                                    s[hb][tb] = mfma_16x16x32(a, ql[kk][tb], s[hb][tb]);
+                                    s[cc][hb][tb] = mfma_16x16x32(afrag16<KCPR>(Kl, kblk, c16, kk * 4 + g, swk), qh[kk][tb], s[cc][hb][tb]);
+                                    s[cc][hb][tb] = mfma_16x16x32(a, ql[kk][tb], s[cc][hb][tb]);
                                 }
                             }
                         }
@@ -509,46 +503,60 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) {
                         const int pos = q0 + tb * 16 + c16;
-                        float mx = -INFINITY;
 #pragma unroll
-                        for (int hb = 0; hb < 2; hb++) {
+                        for (int hb = 0; hb < 2; hb++)
 #pragma unroll
                             for (int e = 0; e < 4; e++) {
                                 const int key = cc * 32 + 8 * g + 4 * hb + e;
-                                float v = s[hb][tb][e] * p.scale_log2;
+                                float v = s[cc][hb][tb][e] * p.scale_log2;
                                 if (need_mask && (key > pos || key >= len)) v = -INFINITY;
-                                s[hb][tb][e] = v;
-                                mx = fmaxf(mx, v);
+                                s[cc][hb][tb][e] = v;
                             }
-                        }
-                        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                        const float mnew = fmaxf(mrun[tb], mx);  // finite: key 0 is in chunk 0
-                        const float alpha = __builtin_amdgcn_exp2f(mrun[tb] - mnew);
-                        mrun[tb] = mnew;
-                        float ls = 0.f;
+                    }
+                }
+            }
 #pragma unroll
-                        for (int hb = 0; hb < 2; hb++) {
+            for (int tb = 0; tb < TPW; tb++) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int cc = 0; cc < 2; cc++)
+                    if (cc < nch) {
+#pragma unroll
+                        for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+                            for (int e = 0; e < 4; e++) mx = fmaxf(mx, s[cc][hb][tb][e]);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));  // finite: key 0 is in chunk 0
+                float ls = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < 2; cc++)
+                    if (cc < nch) {
+#pragma unroll
+                        for (int hb = 0; hb < 2; hb++)
 #pragma unroll
                             for (int e = 0; e < 4; e++) {
-                                const float pv = __builtin_amdgcn_exp2f(s[hb][tb][e] - mnew);
-                                s[hb][tb][e] = pv;
+                                const float pv = __builtin_amdgcn_exp2f(s[cc][hb][tb][e] - mx);
+                                s[cc][hb][tb][e] = pv;
                                 ls += pv;
                             }
-                        }
-                        lrun[tb] = lrun[tb] * alpha + ls;
-#pragma unroll
-                        for (int db = 0; db < NQB; db++) o[db][tb] *= alpha;
                     }
+                lrun[tb] = ls;
+#pragma unroll
+                for (int db = 0; db < NQB; db++) o[db][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; cc++)
+                if (cc < nch) {
 #pragma unroll
                     for (int db = 0; db < NQB; db++) {
                         // LDS row db * 16 + c16 holds feature (db >> 1) * 32 + sigma32((db & 1) * 16 + c16)
                         const f16x8 va = afrag16<VCPR>(Vt, db, c16, (kbase + cc * 32) / 8 + g, c16);
 #pragma unroll
-                        for (int tb = 0; tb < TPW; tb++) o[db][tb] = mfma_16x16x32(va, pack8(s[0][tb], s[1][tb]), o[db][tb]);
+                        for (int tb = 0; tb < TPW; tb++)
+                            o[db][tb] = mfma_16x16x32(va, pack8(s[cc][0][tb], s[cc][1][tb]), o[db][tb]);
                     }
                 }
-            }
             f16x8 OB[NHC][TPW];
 #pragma unroll
             for (int tb = 0; tb < TPW; tb++) {
