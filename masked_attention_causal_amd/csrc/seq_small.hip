@@ -34,6 +34,24 @@ __device__ __forceinline__ f32x4 load4v(const T* q) {
     return f32x4{to_f32(h[0]), to_f32(h[1]), to_f32(h[2]), to_f32(h[3])};
 }
 
+// Four consecutive stored values read through a pointer known to be in
+// global memory (a generic pointer would be read with a flat load, which the
+// compiler orders with LDS work), kept as raw bits until widened, so a batch
+// of reads can be in flight before the first conversion.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <class T>
+using raw4 = typename std::conditional<sizeof(T) == 4, f32x4, u32x2>::type;
+template <class T>
+__device__ __forceinline__ raw4<T> load4g(const T* q) {
+    return *(const __attribute__((address_space(1))) raw4<T>*)q;
+}
+__device__ __forceinline__ f32x4 widen4(const float*, f32x4 r) { return r; }
+template <class T>
+__device__ __forceinline__ f32x4 widen4(const T*, u32x2 r) {
+    const T* h = (const T*)&r;
+    return f32x4{to_f32(h[0]), to_f32(h[1]), to_f32(h[2]), to_f32(h[3])};
+}
+
 }  // namespace
 
 // LDS (rows padded to a multiple of 16 with zeros):
@@ -65,55 +83,98 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
     int len = p.lens[b];
     len = len < 1 ? 1 : (len > L ? L : len);
     const WT* x = (const WT*)p.x + (size_t)b * L * D;
+    // The input rows, as 16-byte units (D is a multiple of 16), are loaded
+    // before the LDS is cleared and stored after: one memory round trip.
+    constexpr int XB = 4;  // units per thread per batch (L * D / 4 <= 1024)
+    const int D4 = D / 4, F4 = F / 4;
+    f32x4 xv[XB];
+#pragma unroll
+    for (int k = 0; k < XB; k++) {
+        const int u = k * SS_THREADS + tid;
+        if (u < L * D4) xv[k] = load4v(x + 4 * (size_t)u);
+    }
     for (int i = tid; i < LR * (2 * PX + P1); i += SS_THREADS) ss_lds[i] = 0.f;
     __syncthreads();
-    for (int i = tid; i < L * D; i += SS_THREADS) X[(i / D) * PX + i % D] = ld(x, i);
+#pragma unroll
+    for (int k = 0; k < XB; k++) {
+        const int u = k * SS_THREADS + tid;
+        if (u < L * D4) {
+            const int r = u / D4;
+            *(f32x4*)(X + r * PX + 4 * (u - r * D4)) = xv[k];
+        }
+    }
     float* const WLb = B2 + LR * PX;  // weights of every layer (WL only)
     const int LF = ss_layer_floats(D, F);
     if constexpr (WL) {
-        // four values per load (cols and n are multiples of 16), loads issued
-        // in batches of 8 before their stores
-        auto copy_rows = [&](const WT* src, int rows, int cols, float* dst) {
-            const int n4 = rows * cols / 4, c4 = cols / 4;
-            for (int i0 = 0; i0 < n4; i0 += 8 * SS_THREADS) {
-                f32x4 v[8];
-#pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const int i = i0 + u * SS_THREADS + tid;
-                    if (i < n4) v[u] = load4v(src + 4 * (size_t)i);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; u++) {
-                    const int i = i0 + u * SS_THREADS + tid;
-                    if (i < n4) {
-                        const int r = i / c4;
-                        *(f32x4*)(dst + r * (cols + 4) + 4 * (i - r * c4)) = v[u];
-                    }
-                }
-            }
-        };
-        auto copy_vec = [&](const WT* src, int n, float* dst) {
-            for (int i = tid; i < n / 4; i += SS_THREADS) *(f32x4*)(dst + 4 * i) = load4v(src + 4 * (size_t)i);
-        };
+        // One layer's weights and vectors as 16-byte units, in three
+        // regions: the rows of W_qkv, W_o and W_1 (D columns each, stored as
+        // consecutive LDS rows of D + 4), the rows of W_2 (F columns, rows of
+        // F + 4), then the eight vectors.  In the two row regions a thread
+        // keeps one column and steps over rows (256 / columns rows a pass),
+        // so which region an iteration is in is the same for the whole wave.
+        // A thread loads all its units of a batch before storing any: a layer
+        // costs one memory round trip (a few at d = 64), not one per matrix
+        // or vector.  (F / 4 < 256 since the activations fit 64 KB of LDS.)
+        constexpr int WB = 16;  // units per thread per batch
+        const int PA = SS_THREADS / D4, PB = SS_THREADS / F4;  // rows per pass
+        const int rA = tid / D4, cA = 4 * (tid - rA * D4);
+        const int rB = tid / F4, cB = 4 * (tid - rB * F4);
+        const int RA = 4 * D + F;
+        const int nA = (RA + PA - 1) / PA, nB = (D + PB - 1) / PB, nV = ((9 * D + F) / 4 + SS_THREADS - 1) / SS_THREADS;
+        const int V0 = RA * (D + 4) + D * (F + 4);  // first vector float
         for (int l = 0; l < p.n_layers; l++) {
-            const LayerPtrs& w = p.lw[l];
-            float* o = WLb + (size_t)l * LF;
-            copy_rows((const WT*)w.w_qkv, 3 * D, D, o);
-            o += 3 * D * (D + 4);
-            copy_rows((const WT*)w.w_o, D, D, o);
-            o += D * (D + 4);
-            copy_rows((const WT*)w.w_1, F, D, o);
-            o += F * (D + 4);
-            copy_rows((const WT*)w.w_2, D, F, o);
-            o += D * (F + 4);
-            copy_vec((const WT*)w.b_qkv, 3 * D, o);
-            copy_vec((const WT*)w.b_o, D, o + 3 * D);
-            copy_vec((const WT*)w.ln1_g, D, o + 4 * D);
-            copy_vec((const WT*)w.ln1_b, D, o + 5 * D);
-            copy_vec((const WT*)w.b_1, F, o + 6 * D);
-            copy_vec((const WT*)w.b_2, D, o + 6 * D + F);
-            copy_vec((const WT*)w.ln2_g, D, o + 7 * D + F);
-            copy_vec((const WT*)w.ln2_b, D, o + 8 * D + F);
+            // The layer's pointers, taken into scalar registers first: a
+            // per-lane choice among them must select values, not load a
+            // pointer per lane from the argument block.
+            const WT* wp[12] = {(const WT*)p.lw[l].w_qkv, (const WT*)p.lw[l].w_o,   (const WT*)p.lw[l].w_1,
+                                (const WT*)p.lw[l].w_2,   (const WT*)p.lw[l].b_qkv, (const WT*)p.lw[l].b_o,
+                                (const WT*)p.lw[l].ln1_g, (const WT*)p.lw[l].ln1_b, (const WT*)p.lw[l].b_1,
+                                (const WT*)p.lw[l].b_2,   (const WT*)p.lw[l].ln2_g, (const WT*)p.lw[l].ln2_b};
+#pragma unroll
+            for (int i = 0; i < 12; i++) asm volatile("" : "+s"(wp[i]));
+            float* const o = WLb + (size_t)l * LF;
+            for (int k0 = 0; k0 < nA + nB + nV; k0 += WB) {
+                raw4<WT> v[WB];
+                int dst[WB];
+#pragma unroll
+                for (int k = 0; k < WB; k++) {
+                    const int it = k0 + k;
+                    dst[k] = -1;
+                    const WT* src = nullptr;
+                    if (it < nA) {
+                        const int r = it * PA + rA;
+                        if (rA < PA && r < RA) {
+                            src = r < 3 * D   ? wp[0] + r * D + cA
+                                  : r < 4 * D ? wp[1] + (r - 3 * D) * D + cA
+                                              : wp[2] + (r - 4 * D) * D + cA;
+                            dst[k] = r * (D + 4) + cA;
+                        }
+                    } else if (it < nA + nB) {
+                        const int r = (it - nA) * PB + rB;
+                        if (rB < PB && r < D) {
+                            src = wp[3] + r * F + cB;
+                            dst[k] = RA * (D + 4) + r * (F + 4) + cB;
+                        }
+                    } else if (it < nA + nB + nV) {
+                        int j = 4 * ((it - nA - nB) * SS_THREADS + tid);  // float of b_qkv | b_o | ln1 | b_1 | b_2 | ln2
+                        if (j < 9 * D + F) {
+                            dst[k] = V0 + j;
+                            if (j < 3 * D) src = wp[4] + j;
+                            else if ((j -= 3 * D) < D) src = wp[5] + j;
+                            else if ((j -= D) < D) src = wp[6] + j;
+                            else if ((j -= D) < D) src = wp[7] + j;
+                            else if ((j -= D) < F) src = wp[8] + j;
+                            else if ((j -= F) < D) src = wp[9] + j;
+                            else if ((j -= D) < D) src = wp[10] + j;
+                            else src = wp[11] + (j - D);
+                        }
+                    }
+                    if (dst[k] >= 0) v[k] = load4g(src);
+                }
+#pragma unroll
+                for (int k = 0; k < WB; k++)
+                    if (dst[k] >= 0) *(f32x4*)(o + dst[k]) = widen4((const WT*)nullptr, v[k]);
+            }
         }
     }
     __syncthreads();
@@ -298,7 +359,7 @@ size_t seq_small_lds(int d, int f, int L) {
 }
 
 bool seq_small_supported(int d, int dh, int f, int L, int n_layers) {
-    return d <= 64 && (dh == 16 || dh == 32 || dh == 64) && L <= 64 && f % 16 == 0 &&
+    return d <= 64 && (dh == 16 || dh == 32 || dh == 64) && L <= 64 && f % 16 == 0 && f < 4 * SS_THREADS &&
            n_layers <= SEQ_MAX_LAYERS && seq_small_lds(d, f, L) <= 64 * 1024;
 }
 
