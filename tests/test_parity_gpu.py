@@ -156,6 +156,10 @@ SMALL_SEQ = [
     W("t_f32_d64_dh64", 2, 64, 1, 128, 2, 32, "f32", 1, 32, 1.0),
     W("t_bf16_d32_dh32", 3, 32, 1, 64, 3, 50, "bf16", 1, 50, 1.0),
     W("t_f16_d32_dh16", 1, 32, 2, 96, 6, 64, "f16", 1, 64, 1.0),
+    # FFN widths whose rows of 16-byte units do not divide the 256 threads
+    # of the weight copy (24 and 40 units a row)
+    W("t_bf16_d64_dh32_f96", 2, 64, 2, 96, 3, 48, "bf16", 1, 48, 1.0),
+    W("t_f32_d32_dh16_f160", 2, 32, 2, 160, 3, 40, "f32", 1, 40, 1.0),
 ]
 
 
