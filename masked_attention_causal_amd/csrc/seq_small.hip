@@ -6,9 +6,10 @@
 //
 // At these sizes a forward is a few million multiply-adds, so the kernel
 // keeps every value in fp32 with no operand rounding at all: projections on
-// fp32 MFMA (16 x 16 output blocks spread over the four waves), attention
-// one thread per (head, query) with the exact two-pass softmax, LayerNorm
-// one wave per row.  When every layer's weights fit in LDS beside the
+// fp32 MFMA (16 x 16 output blocks spread over eight waves, two per SIMD so
+// one hides the other's latency), attention eight lanes per (head, query)
+// with the exact two-pass softmax, LayerNorm eight lanes per row.  When
+// every layer's weights fit in LDS beside the
 // activations (WL), they are copied there once at the start, as fp32 rows
 // padded to 4 floats past a multiple of 32 (the 16 rows of an MFMA operand
 // then fall on distinct banks); each phase then waits on LDS, not on a
@@ -20,7 +21,7 @@ namespace tfl {
 
 namespace {
 
-constexpr int SS_THREADS = 256;
+constexpr int SS_THREADS = 512;  // 8 waves, two per SIMD
 
 template <class T>
 __device__ __forceinline__ float ld(const T* p, int i) { return to_f32(p[i]); }
@@ -248,11 +249,11 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
         else
             linear(X, PX, D, (const WT*)w.w_qkv, D, (const WT*)w.b_qkv, 3 * D, B1, P1, nullptr, false);
         __syncthreads();
-        // attention: four lanes per (head, query), lane s taking keys j = s mod 4
-        // of j <= min(i, len - 1); exact two-pass softmax, partials combined
-        // across the four lanes
-        for (int u = tid >> 2; u < H * L; u += SS_THREADS / 4) {
-            const int s4 = tid & 3;
+        // attention: eight lanes per (head, query), lane s taking keys
+        // j = s mod 8 of j <= min(i, len - 1); exact two-pass softmax,
+        // partials combined across the eight lanes
+        for (int u = tid >> 3; u < H * L; u += SS_THREADS / 8) {
+            const int s8 = tid & 7;
             const int h = u / L, i = u - h * L;
             const int nk = min(i, len - 1);
             float q[DH];
@@ -274,25 +275,26 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
                 }
                 return sc * scale;
             };
-            // this lane's keys j = s4 + 4c (c < 16 covers L <= 64): scores
+            // this lane's keys j = s8 + 8c (c < 8 covers L <= 64): scores
             // kept from the max pass for the exponential pass
-            float sc[16];
+            float sc[8];
             float m = -INFINITY;
 #pragma unroll
-            for (int c = 0; c < 16; c++) {
-                const int j = s4 + 4 * c;
+            for (int c = 0; c < 8; c++) {
+                const int j = s8 + 8 * c;
                 sc[c] = j <= nk ? score(j) : -INFINITY;
                 m = fmaxf(m, sc[c]);
             }
             m = fmaxf(m, dpp_xor1(m));
             m = fmaxf(m, dpp_xor2(m));
+            m = fmaxf(m, dpp_mirror8(m));
             float o[DH];
 #pragma unroll
             for (int t = 0; t < DH; t++) o[t] = 0.f;
             float den = 0.f;
 #pragma unroll
-            for (int c = 0; c < 16; c++) {
-                const int j = s4 + 4 * c;
+            for (int c = 0; c < 8; c++) {
+                const int j = s8 + 8 * c;
                 if (j > nk) break;
                 const float e = expf(sc[c] - m);
                 den += e;
@@ -308,12 +310,14 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
             }
             den += dpp_xor1(den);
             den += dpp_xor2(den);
+            den += dpp_mirror8(den);
 #pragma unroll
             for (int t = 0; t < DH; t++) {
                 o[t] += dpp_xor1(o[t]);
                 o[t] += dpp_xor2(o[t]);
+                o[t] += dpp_mirror8(o[t]);
             }
-            if (s4 == 0) {
+            if (s8 == 0) {
                 const float inv = 1.0f / den;
 #pragma unroll
                 for (int t = 0; t < DH; t++) B2[i * PX + h * DH + t] = o[t] * inv;
