@@ -6,10 +6,10 @@
 //
 // At these sizes a forward is a few million multiply-adds, so the kernel
 // keeps every value in fp32 with no operand rounding at all: projections on
-// fp32 MFMA (16 x 16 output blocks spread over eight waves, two per SIMD so
-// one hides the other's latency), attention eight lanes per (head, query)
-// with the exact two-pass softmax, LayerNorm eight lanes per row.  When
-// every layer's weights fit in LDS beside the
+// fp32 MFMA (16 x 16 output blocks spread over 8 or 16 waves, two or four
+// per SIMD so they hide one another's latency), attention eight lanes per
+// (head, query) with the exact two-pass softmax, LayerNorm eight lanes per
+// row.  When every layer's weights fit in LDS beside the
 // activations (WL), they are copied there once at the start, as fp32 rows
 // padded to 4 floats past a multiple of 32 (the 16 rows of an MFMA operand
 // then fall on distinct banks); each phase then waits on LDS, not on a
@@ -21,7 +21,10 @@ namespace tfl {
 
 namespace {
 
-constexpr int SS_THREADS = 512;  // 8 waves, two per SIMD
+// Threads per workgroup: 16 waves (four per SIMD) where the kernel fits the
+// 128 registers that allows (head dim 16), else 8 waves.
+constexpr int ss_threads(int dh) { return dh == 16 ? 1024 : 512; }
+constexpr int SS_MIN_THREADS = 512;
 
 template <class T>
 __device__ __forceinline__ float ld(const T* p, int i) { return to_f32(p[i]); }
@@ -66,7 +69,8 @@ __host__ __device__ inline int ss_layer_floats(int D, int F) {
 }
 
 template <class WT, int DH, bool WL>
-__global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D) {
+__global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, int D) {
+    constexpr int SS_THREADS = ss_threads(DH);
     extern __shared__ __attribute__((aligned(16))) float ss_lds[];
     const int H = D / DH;
     const int L = p.L, F = p.F;
@@ -249,11 +253,23 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
         else
             linear(X, PX, D, (const WT*)w.w_qkv, D, (const WT*)w.b_qkv, 3 * D, B1, P1, nullptr, false);
         __syncthreads();
-        // attention: eight lanes per (head, query), lane s taking keys
+        // attention: ALN = 8 lanes per (head, query), lane s taking keys
         // j = s mod 8 of j <= min(i, len - 1); exact two-pass softmax,
-        // partials combined across the eight lanes
-        for (int u = tid >> 3; u < H * L; u += SS_THREADS / 8) {
-            const int s8 = tid & 7;
+        // partials combined across the eight lanes by DPP (16 lanes per
+        // query with 16 waves measured slower)
+        constexpr int ALN = 8, NKL = 64 / ALN;
+        auto lanes_max = [](float v) {
+            v = fmaxf(v, dpp_xor1(v));
+            v = fmaxf(v, dpp_xor2(v));
+            return fmaxf(v, dpp_mirror8(v));
+        };
+        auto lanes_sum = [](float v) {
+            v += dpp_xor1(v);
+            v += dpp_xor2(v);
+            return v + dpp_mirror8(v);
+        };
+        for (int u = tid / ALN; u < H * L; u += SS_THREADS / ALN) {
+            const int s8 = tid & (ALN - 1);
             const int h = u / L, i = u - h * L;
             const int nk = min(i, len - 1);
             float q[DH];
@@ -275,26 +291,24 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
                 }
                 return sc * scale;
             };
-            // this lane's keys j = s8 + 8c (c < 8 covers L <= 64): scores
+            // this lane's keys j = s8 + ALN c (c < NKL covers L <= 64): scores
             // kept from the max pass for the exponential pass
-            float sc[8];
+            float sc[NKL];
             float m = -INFINITY;
 #pragma unroll
-            for (int c = 0; c < 8; c++) {
-                const int j = s8 + 8 * c;
+            for (int c = 0; c < NKL; c++) {
+                const int j = s8 + ALN * c;
                 sc[c] = j <= nk ? score(j) : -INFINITY;
                 m = fmaxf(m, sc[c]);
             }
-            m = fmaxf(m, dpp_xor1(m));
-            m = fmaxf(m, dpp_xor2(m));
-            m = fmaxf(m, dpp_mirror8(m));
+            m = lanes_max(m);
             float o[DH];
 #pragma unroll
             for (int t = 0; t < DH; t++) o[t] = 0.f;
             float den = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; c++) {
-                const int j = s8 + 8 * c;
+            for (int c = 0; c < NKL; c++) {
+                const int j = s8 + ALN * c;
                 if (j > nk) break;
                 const float e = expf(sc[c] - m);
                 den += e;
@@ -308,15 +322,9 @@ __global__ __launch_bounds__(SS_THREADS) void seq_small_kernel(SeqArgs p, int D)
                     o[t + 3] = fmaf(e, v4.w, o[t + 3]);
                 }
             }
-            den += dpp_xor1(den);
-            den += dpp_xor2(den);
-            den += dpp_mirror8(den);
+            den = lanes_sum(den);
 #pragma unroll
-            for (int t = 0; t < DH; t++) {
-                o[t] += dpp_xor1(o[t]);
-                o[t] += dpp_xor2(o[t]);
-                o[t] += dpp_mirror8(o[t]);
-            }
+            for (int t = 0; t < DH; t++) o[t] = lanes_sum(o[t]);
             if (s8 == 0) {
                 const float inv = 1.0f / den;
 #pragma unroll
@@ -363,7 +371,7 @@ size_t seq_small_lds(int d, int f, int L) {
 }
 
 bool seq_small_supported(int d, int dh, int f, int L, int n_layers) {
-    return d <= 64 && (dh == 16 || dh == 32 || dh == 64) && L <= 64 && f % 16 == 0 && f < 4 * SS_THREADS &&
+    return d <= 64 && (dh == 16 || dh == 32 || dh == 64) && L <= 64 && f % 16 == 0 && f < 4 * SS_MIN_THREADS &&
            n_layers <= SEQ_MAX_LAYERS && seq_small_lds(d, f, L) <= 64 * 1024;
 }
 
@@ -380,7 +388,7 @@ static hipError_t small_launch(const SeqArgs& a, int d, size_t lds, hipStream_t 
                                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (set != hipSuccess) return set;
     }
-    hipLaunchKernelGGL((seq_small_kernel<WT, DH, WL>), dim3(a.B), dim3(SS_THREADS), lds, s, a, d);
+    hipLaunchKernelGGL((seq_small_kernel<WT, DH, WL>), dim3(a.B), dim3(ss_threads(DH)), lds, s, a, d);
     return hipGetLastError();
 }
 
