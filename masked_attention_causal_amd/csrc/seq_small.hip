@@ -196,9 +196,18 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
             const int rb = blk / nb16, nb = blk - rb * nb16;
             const float* a = in + (rb * 16 + c16) * pin + g;
             const auto w = W + (size_t)(nb * 16 + c16) * pw + g;
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int k = 0; k < K; k += 4) acc = mfma_16x16x4(a[k], ld(w, k), acc);
+            // four accumulators over interleaved K slices (K is a multiple of
+            // 32), so four product chains overlap instead of one running K / 4
+            // dependent products
+            f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+#pragma unroll 2
+            for (int k = 0; k < K; k += 16) {
+                acc0 = mfma_16x16x4(a[k], ld(w, k), acc0);
+                acc1 = mfma_16x16x4(a[k + 4], ld(w, k + 4), acc1);
+                acc2 = mfma_16x16x4(a[k + 8], ld(w, k + 8), acc2);
+                acc3 = mfma_16x16x4(a[k + 12], ld(w, k + 12), acc3);
+            }
+            const f32x4 acc = (acc0 + acc1) + (acc2 + acc3);
             // result: rows rb*16 + 4g + e, feature nb*16 + c16
             const int n = nb * 16 + c16;
             const float bn = ld(bias, n);
