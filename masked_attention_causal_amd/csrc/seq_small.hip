@@ -88,99 +88,111 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
     int len = p.lens[b];
     len = len < 1 ? 1 : (len > L ? L : len);
     const WT* x = (const WT*)p.x + (size_t)b * L * D;
-    // The input rows, as 16-byte units (D is a multiple of 16), are loaded
-    // before the LDS is cleared and stored after: one memory round trip.
-    constexpr int XB = 4;  // units per thread per batch (L * D / 4 <= 1024)
+    // The input rows and (WL) every layer's weights are read as 16-byte
+    // units (D is a multiple of 16).  All the loads of a batch are issued
+    // before any LDS store, and the first batch's before the LDS is
+    // cleared, so the whole prologue costs one memory round trip (a few at
+    // d = 64), hidden in part under the clearing.
+    constexpr int XB = (1024 + SS_THREADS - 1) / SS_THREADS;  // units per thread (L * D / 4 <= 1024)
     const int D4 = D / 4, F4 = F / 4;
-    f32x4 xv[XB];
+    raw4<WT> xv[XB];
 #pragma unroll
     for (int k = 0; k < XB; k++) {
         const int u = k * SS_THREADS + tid;
-        if (u < L * D4) xv[k] = load4v(x + 4 * (size_t)u);
+        xv[k] = load4g(x + 4 * (size_t)(u < L * D4 ? u : 0));  // unconditional: no branch to wait in
     }
-    for (int i = tid; i < LR * (2 * PX + P1); i += SS_THREADS) ss_lds[i] = 0.f;
-    __syncthreads();
+    auto clear_and_store_x = [&]() {
+        for (int i = tid; i < LR * (2 * PX + P1); i += SS_THREADS) ss_lds[i] = 0.f;
+        __syncthreads();
 #pragma unroll
-    for (int k = 0; k < XB; k++) {
-        const int u = k * SS_THREADS + tid;
-        if (u < L * D4) {
-            const int r = u / D4;
-            *(f32x4*)(X + r * PX + 4 * (u - r * D4)) = xv[k];
+        for (int k = 0; k < XB; k++) {
+            const int u = k * SS_THREADS + tid;
+            if (u < L * D4) {
+                const int r = u / D4;
+                asm volatile("" : "+v"(xv[k]));  // widened here, after the wait, not at the load
+                *(f32x4*)(X + r * PX + 4 * (u - r * D4)) = widen4((const WT*)nullptr, xv[k]);
+            }
         }
-    }
+    };
     float* const WLb = B2 + LR * PX;  // weights of every layer (WL only)
     const int LF = ss_layer_floats(D, F);
     if constexpr (WL) {
-        // One layer's weights and vectors as 16-byte units, in three
+        // Each layer's weights and vectors as 16-byte units, in three
         // regions: the rows of W_qkv, W_o and W_1 (D columns each, stored as
         // consecutive LDS rows of D + 4), the rows of W_2 (F columns, rows of
         // F + 4), then the eight vectors.  In the two row regions a thread
-        // keeps one column and steps over rows (256 / columns rows a pass),
-        // so which region an iteration is in is the same for the whole wave.
-        // A thread loads all its units of a batch before storing any: a layer
-        // costs one memory round trip (a few at d = 64), not one per matrix
-        // or vector.  (F / 4 < 256 since the activations fit 64 KB of LDS.)
+        // keeps one column and steps over rows (threads / columns rows a
+        // pass), so the layer and region of an iteration are the same for
+        // the whole wave.  (F / 4 < 256 since the activations fit 64 KB of
+        // LDS.)
         constexpr int WB = 16;  // units per thread per batch
         const int PA = SS_THREADS / D4, PB = SS_THREADS / F4;  // rows per pass
         const int rA = tid / D4, cA = 4 * (tid - rA * D4);
         const int rB = tid / F4, cB = 4 * (tid - rB * F4);
         const int RA = 4 * D + F;
         const int nA = (RA + PA - 1) / PA, nB = (D + PB - 1) / PB, nV = ((9 * D + F) / 4 + SS_THREADS - 1) / SS_THREADS;
+        const int nI = nA + nB + nV, NIT = p.n_layers * nI;  // iterations per layer, in all
         const int V0 = RA * (D + 4) + D * (F + 4);  // first vector float
-        for (int l = 0; l < p.n_layers; l++) {
-            // The layer's pointers, taken into scalar registers first: a
-            // per-lane choice among them must select values, not load a
-            // pointer per lane from the argument block.
-            const WT* wp[12] = {(const WT*)p.lw[l].w_qkv, (const WT*)p.lw[l].w_o,   (const WT*)p.lw[l].w_1,
-                                (const WT*)p.lw[l].w_2,   (const WT*)p.lw[l].b_qkv, (const WT*)p.lw[l].b_o,
-                                (const WT*)p.lw[l].ln1_g, (const WT*)p.lw[l].ln1_b, (const WT*)p.lw[l].b_1,
-                                (const WT*)p.lw[l].b_2,   (const WT*)p.lw[l].ln2_g, (const WT*)p.lw[l].ln2_b};
+        for (int k0 = 0; k0 < NIT; k0 += WB) {
+            raw4<WT> v[WB];
+            int dst[WB];
 #pragma unroll
-            for (int i = 0; i < 12; i++) asm volatile("" : "+s"(wp[i]));
-            float* const o = WLb + (size_t)l * LF;
-            for (int k0 = 0; k0 < nA + nB + nV; k0 += WB) {
-                raw4<WT> v[WB];
-                int dst[WB];
-#pragma unroll
-                for (int k = 0; k < WB; k++) {
-                    const int it = k0 + k;
-                    dst[k] = -1;
-                    const WT* src = nullptr;
+            for (int k = 0; k < WB; k++) {
+                dst[k] = -1;
+                const WT* src = nullptr;
+                const int l = (k0 + k) / nI, it = k0 + k - l * nI;  // wave-uniform
+                if (l < p.n_layers) {
+                    // The layer's pointers, in scalar registers first: a
+                    // per-lane choice among them must select values, not
+                    // load a pointer per lane from the argument block.
+                    const LayerPtrs& w = p.lw[l];
                     if (it < nA) {
+                        const WT *q0 = (const WT*)w.w_qkv, *q1 = (const WT*)w.w_o, *q2 = (const WT*)w.w_1;
+                        asm volatile("" : "+s"(q0), "+s"(q1), "+s"(q2));
                         const int r = it * PA + rA;
                         if (rA < PA && r < RA) {
-                            src = r < 3 * D   ? wp[0] + r * D + cA
-                                  : r < 4 * D ? wp[1] + (r - 3 * D) * D + cA
-                                              : wp[2] + (r - 4 * D) * D + cA;
+                            src = r < 3 * D   ? q0 + r * D + cA
+                                  : r < 4 * D ? q1 + (r - 3 * D) * D + cA
+                                              : q2 + (r - 4 * D) * D + cA;
                             dst[k] = r * (D + 4) + cA;
                         }
                     } else if (it < nA + nB) {
                         const int r = (it - nA) * PB + rB;
                         if (rB < PB && r < D) {
-                            src = wp[3] + r * F + cB;
+                            src = (const WT*)w.w_2 + r * F + cB;
                             dst[k] = RA * (D + 4) + r * (F + 4) + cB;
                         }
-                    } else if (it < nA + nB + nV) {
+                    } else {
                         int j = 4 * ((it - nA - nB) * SS_THREADS + tid);  // float of b_qkv | b_o | ln1 | b_1 | b_2 | ln2
                         if (j < 9 * D + F) {
+                            const WT* q[8] = {(const WT*)w.b_qkv, (const WT*)w.b_o, (const WT*)w.ln1_g, (const WT*)w.ln1_b,
+                                              (const WT*)w.b_1,   (const WT*)w.b_2, (const WT*)w.ln2_g, (const WT*)w.ln2_b};
+#pragma unroll
+                            for (int e = 0; e < 8; e++) asm volatile("" : "+s"(q[e]));
                             dst[k] = V0 + j;
-                            if (j < 3 * D) src = wp[4] + j;
-                            else if ((j -= 3 * D) < D) src = wp[5] + j;
-                            else if ((j -= D) < D) src = wp[6] + j;
-                            else if ((j -= D) < D) src = wp[7] + j;
-                            else if ((j -= D) < F) src = wp[8] + j;
-                            else if ((j -= F) < D) src = wp[9] + j;
-                            else if ((j -= D) < D) src = wp[10] + j;
-                            else src = wp[11] + (j - D);
+                            if (j < 3 * D) src = q[0] + j;
+                            else if ((j -= 3 * D) < D) src = q[1] + j;
+                            else if ((j -= D) < D) src = q[2] + j;
+                            else if ((j -= D) < D) src = q[3] + j;
+                            else if ((j -= D) < F) src = q[4] + j;
+                            else if ((j -= F) < D) src = q[5] + j;
+                            else if ((j -= D) < D) src = q[6] + j;
+                            else src = q[7] + (j - D);
                         }
                     }
-                    if (dst[k] >= 0) v[k] = load4g(src);
+                    if (dst[k] >= 0) {
+                        v[k] = load4g(src);
+                        dst[k] += l * LF;
+                    }
                 }
-#pragma unroll
-                for (int k = 0; k < WB; k++)
-                    if (dst[k] >= 0) *(f32x4*)(o + dst[k]) = widen4((const WT*)nullptr, v[k]);
             }
+            if (k0 == 0) clear_and_store_x();
+#pragma unroll
+            for (int k = 0; k < WB; k++)
+                if (dst[k] >= 0) *(f32x4*)(WLb + dst[k]) = widen4((const WT*)nullptr, v[k]);
         }
+    } else {
+        clear_and_store_x();
     }
     __syncthreads();
     const float scale = rsqrtf((float)DH);
