@@ -195,7 +195,9 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
         clear_and_store_x();
     }
     __syncthreads();
-    const float scale = rsqrtf((float)DH);
+    // scores in base 2 (scaled by log2 e / sqrt(dh)): the softmax weights are
+    // then 2^(s - max) on the hardware exp2, the same values as e^ in base e
+    const float scale = rsqrtf((float)DH) * 1.4426950408889634f;
 
     // out[r][n] = bias[n] + sum_k in[r][k] W[n][k] (+ res[r][n]) on fp32 MFMA
     // (16x16x4: exact fp32 products, fp32 accumulation); one 16 x 16 output
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
             for (int c = 0; c < NKL; c++) {
                 const int j = s8 + ALN * c;
                 if (j > nk) break;
-                const float e = expf(sc[c] - m);
+                const float e = __builtin_amdgcn_exp2f(sc[c] - m);
                 den += e;
                 const float* v = B1 + j * P1 + 2 * D + h * DH;
 #pragma unroll
