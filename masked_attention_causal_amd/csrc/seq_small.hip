@@ -247,23 +247,43 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
         return v + dpp_mirror8(v);
     };
     auto layernorm = [&](const float* Z, int PZ, auto gam, auto bet) {
+        // A lane's values (at most 8: D <= 64), gamma and beta are read once
+        // into registers, all reads issued before the first sum; column
+        // j8 + 8e is below D for every lane or for none (D is a multiple of 32).
         const int j8 = lane & 7;
         for (int r = wave * 8 + (lane >> 3); r - (lane >> 3) < L; r += SS_THREADS / 8) {
             const bool live = r < L;
             const int rr = live ? r : 0;
+            float zv[8], gv[8], bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                zv[e] = gv[e] = bv[e] = 0.f;
+                if (8 * e < D) {
+                    const int n = j8 + 8 * e;
+                    zv[e] = Z[rr * PZ + n];
+                    gv[e] = ld(gam, n);
+                    bv[e] = ld(bet, n);
+                }
+            }
             float s = 0.f;
-            for (int n = j8; n < D; n += 8) s += Z[rr * PZ + n];
+#pragma unroll
+            for (int e = 0; e < 8; e++) s += zv[e];
             s = sum8(s);
             const float mean = s / (float)D;
             float q = 0.f;
-            for (int n = j8; n < D; n += 8) {
-                const float c = Z[rr * PZ + n] - mean;
-                q += c * c;
-            }
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if (8 * e < D) {
+                    const float c = zv[e] - mean;
+                    q += c * c;
+                }
             q = sum8(q);
             const float rstd = 1.0f / sqrtf(q / (float)D + p.eps);
-            if (live)
-                for (int n = j8; n < D; n += 8) X[r * PX + n] = (Z[r * PZ + n] - mean) * rstd * ld(gam, n) + ld(bet, n);
+            if (live) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    if (8 * e < D) X[r * PX + j8 + 8 * e] = (zv[e] - mean) * rstd * gv[e] + bv[e];
+            }
         }
     };
 
