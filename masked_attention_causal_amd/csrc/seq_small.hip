@@ -210,6 +210,15 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
             const int rb = blk / nb16, nb = blk - rb * nb16;
             const float* a = in + (rb * 16 + c16) * pin + g;
             const auto w = W + (size_t)(nb * 16 + c16) * pw + g;
+            // result: rows rb*16 + 4g + e, feature nb*16 + c16; its bias and
+            // residual (rows below LR, in LDS) are read before the products
+            const int n = nb * 16 + c16;
+            const float bn = ld(bias, n);
+            float rv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (res) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) rv[e] = res[(rb * 16 + 4 * g + e) * PX + n];
+            }
             // four accumulators over interleaved K slices (K is a multiple of
             // 32), so four product chains overlap instead of one running K / 4
             // dependent products
@@ -222,18 +231,13 @@ __global__ __launch_bounds__(ss_threads(DH)) void seq_small_kernel(SeqArgs p, in
                 acc3 = mfma_16x16x4(a[k + 12], ld(w, k + 12), acc3);
             }
             const f32x4 acc = (acc0 + acc1) + (acc2 + acc3);
-            // result: rows rb*16 + 4g + e, feature nb*16 + c16
-            const int n = nb * 16 + c16;
-            const float bn = ld(bias, n);
             float vb[4] = {acc[0] + bn, acc[1] + bn, acc[2] + bn, acc[3] + bn};
             if (gelu) gelu_inplace<4>(vb);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int r = rb * 16 + 4 * g + e;
                 if (r >= L) continue;
-                float v = vb[e];
-                if (res) v += res[r * PX + n];
-                out[r * pout + n] = v;
+                out[r * pout + n] = vb[e] + rv[e];
             }
         }
     };
