@@ -19,8 +19,8 @@
  *  - "KernelForge", "What it does": one frozen plan per (GPU, dtype, shape),
  *    looked up at run time with no autotuning.
  *  - "Hyper-optimized megakernel-hybrid transformer inference", "Problem
- *    decomposition": sequence-resident, persistent task-queue and tiled
- *    families chosen by shape; "Sample prompts": one callable handles all
+ *    decomposition": sequence-resident, task-graph and tiled families
+ *    chosen by shape; "Sample prompts": one callable handles all
  *    cases.
  *  - "Implement a GPU Kernel for a Transformer Layer", "What it does": a
  *    shape-aware adapter that routes on sequence length, width and dtype.
@@ -60,12 +60,18 @@ typedef enum {
     TFL_E_INTERNAL = 5
 } tfl_status;
 
-/* Execution paths the dispatcher chooses among. */
+/* Execution paths the dispatcher chooses among ("Hyper-optimized
+ * megakernel-hybrid transformer inference", "Problem decomposition": a
+ * sequence-resident family, a task-graph family and a tiled family). */
 typedef enum {
     TFL_PATH_AUTO = 0,
     TFL_PATH_SEQ = 1,   /* one workgroup owns whole sequences, whole stack in one launch */
-    TFL_PATH_PQ = 2,    /* persistent workgroups pop tasks from a dependency-ordered queue */
-    TFL_PATH_TILED = 3  /* per-stage kernels: QKV GEMM, attention, GEMM+residual, LayerNorm, FFN */
+    TFL_PATH_PQ = 2,    /* task list over 64-row tiles (split-K attention tasks, fused row
+                           tasks), one launch per stage of the list */
+    TFL_PATH_TILED = 3, /* per-stage kernels: QKV GEMM, attention, GEMM+residual, LayerNorm, FFN */
+    TFL_PATH_PQ_SINGLE = 4 /* the PQ tasks in one persistent launch fed by a device queue:
+                              disabled, tfl_create returns TFL_E_UNSUPPORTED (its one GPU
+                              run did not finish and no cause has been shown) */
 } tfl_path;
 
 typedef struct {
@@ -95,14 +101,27 @@ typedef struct {
 
 /* Validates cfg and the layer pointers, freezes the plan for this shape and
  * returns a handle.  No device call is made.  layers points to n_layers
- * entries, copied into the handle (the weights themselves are borrowed). */
+ * entries, copied into the handle (the weights themselves are borrowed).
+ * The plan is a fixed rule over the shape and dtype, evaluated once here
+ * ("KernelForge", "What it does": a frozen per-shape table consulted at run
+ * time, no autotuning).  Errors: TFL_E_INVALID for null or misaligned
+ * pointers and sizes < 1; TFL_E_UNSUPPORTED for shapes outside the supported
+ * set or a forced path that cannot run the shape. */
 tfl_status tfl_create(const tfl_config *cfg, const tfl_layer *layers, tfl_handle **out);
 
-/* Device workspace one tfl_forward needs, in bytes (0 is possible). */
+/* Device workspace one tfl_forward needs, in bytes (0 is possible: the SEQ
+ * path keeps everything between x and y on chip).  The caller allocates it;
+ * the library never does ("KernelForge", "What it does": memory planned per
+ * shape). */
 tfl_status tfl_workspace_bytes(const tfl_handle *h, size_t *bytes);
 
 /* Enqueues the forward pass on hip_stream (a hipStream_t; NULL = default
- * stream).  Asynchronous: no host synchronisation, no allocation.
+ * stream).  Asynchronous: no host synchronisation, no allocation.  Computes
+ * the operation stated at the top of this file: the encoder layers of
+ * "Hyper-optimized megakernel-hybrid transformer inference", "Problem
+ * decomposition", with the causal and key-padding masks applied together
+ * ("KernelForge", "What we built") and the exact-erf GELU ("KernelForge",
+ * "How the LLM is used").
  *   x          [batch, seq_len, d_model] I/O dtype, 16-byte aligned
  *   valid_len  [batch] int32 in device memory, each in [1, seq_len]; the
  *              kernels clamp values outside that range (results are those
@@ -111,15 +130,22 @@ tfl_status tfl_workspace_bytes(const tfl_handle *h, size_t *bytes);
  *              stream) and out-of-range values return TFL_E_INVALID
  *   y          [batch, seq_len, d_model] I/O dtype, 16-byte aligned, must
  *              not overlap x or the workspace
- *   workspace  at least tfl_workspace_bytes() bytes, 256-byte aligned
- * Inputs must be finite; for bf16, |x| must stay below 65504. */
+ *   workspace  at least tfl_workspace_bytes() bytes, 256-byte aligned, must
+ *              not overlap x
+ * Errors: TFL_E_INVALID (null or misaligned pointer, overlap, bad length
+ * with TFL_CHECK=1), TFL_E_WORKSPACE (too small), TFL_E_HIP (launch failed).
+ * Inputs must be finite.  The first layer's products take x rounded to fp16
+ * operands on the fp16-operand paths (bf16 I/O on every path, fp32 I/O on
+ * the PQ path); there |x| must stay below 65504. */
 tfl_status tfl_forward(tfl_handle *h, const void *x, const int32_t *valid_len, void *y,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* Frees the handle (host memory only).  NULL is accepted. */
+/* Frees the handle (host memory only; the borrowed weights stay the
+ * caller's).  NULL is accepted. */
 tfl_status tfl_destroy(tfl_handle *h);
 
-/* Name of the frozen plan ("TILED", "SEQ", "PQ" plus a tile tag). */
+/* Name of the frozen plan ("TILED", "SEQ", "PQ" plus a tile tag); the
+ * string is owned by the handle.  "(null handle)" for NULL. */
 const char *tfl_plan_name(const tfl_handle *h);
 
 /* Path of the frozen plan (a tfl_path value), or -1 for a NULL handle. */

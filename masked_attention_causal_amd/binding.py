@@ -11,6 +11,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtfl.so")
+AUDIT_LIB_PATH = os.path.join(PKG, "libtfl_audit.so")   # test build (include/tfl_audit.h)
 
 LAYER_KEYS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
               "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
@@ -19,7 +20,7 @@ SYMBOLS = ("tfl_create", "tfl_workspace_bytes", "tfl_forward", "tfl_destroy",
 STAGES = {"prep": 1, "qkv": 2, "attn": 3, "out": 4, "ln": 5, "ffn1": 6, "ffn2": 7, "fused": 8}
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
-PATHS = {"auto": 0, "seq": 1, "pq": 2, "tiled": 3}
+PATHS = {"auto": 0, "seq": 1, "pq": 2, "tiled": 3, "pq_single": 4}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 STATUS = {0: "TFL_OK", 1: "TFL_E_INVALID", 2: "TFL_E_UNSUPPORTED", 3: "TFL_E_WORKSPACE",
           4: "TFL_E_HIP", 5: "TFL_E_INTERNAL"}
@@ -41,14 +42,13 @@ class TflError(RuntimeError):
         self.status = status
 
 
-_lib = None
+_libs: dict = {}
 
 
 def load_library(path: str = LIB_PATH):
-    """Load libtfl.so; raises when it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """Load libtfl.so (or another build of it); raises when it has not been built."""
+    if path in _libs:
+        return _libs[path]
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is not built; run "
                            "`python -m masked_attention_causal_amd.build` (or __graft_entry__.build())")
@@ -77,13 +77,16 @@ def load_library(path: str = LIB_PATH):
     L.tfl_timer_read.restype = ctypes.c_int
     L.tfl_last_error.argtypes = []
     L.tfl_last_error.restype = ctypes.c_char_p
-    _lib = L
+    if hasattr(L, "tfl_audit_attach"):
+        L.tfl_audit_attach.argtypes = [vp]
+        L.tfl_audit_attach.restype = ctypes.c_int
+    _libs[path] = L
     return L
 
 
-def _check(st: int) -> None:
+def _check(st: int, L=None) -> None:
     if st != 0:
-        raise TflError(st, load_library().tfl_last_error().decode())
+        raise TflError(st, (L or load_library()).tfl_last_error().decode())
 
 
 def make_config(n_layers, d_model, n_heads, d_ffn, batch, seq_len, dtype, ln_eps=0.0, force_path="auto"):
@@ -95,47 +98,47 @@ def make_config(n_layers, d_model, n_heads, d_ffn, batch, seq_len, dtype, ln_eps
 class Handle:
     """A frozen plan over borrowed weight pointers (raw addresses)."""
 
-    def __init__(self, cfg: TflConfig, layer_ptrs: list):
-        L = load_library()
+    def __init__(self, cfg: TflConfig, layer_ptrs: list, lib_path: str = LIB_PATH):
+        self._L = L = load_library(lib_path)
         arr = (TflLayer * max(1, len(layer_ptrs)))()
         for i, lp in enumerate(layer_ptrs):
             for k in LAYER_KEYS:
                 setattr(arr[i], k, lp[k])
         h = ctypes.c_void_p()
-        _check(L.tfl_create(ctypes.byref(cfg), arr, ctypes.byref(h)))
+        _check(L.tfl_create(ctypes.byref(cfg), arr, ctypes.byref(h)), L)
         self._h = h
         self.cfg = cfg
 
     @property
     def workspace_bytes(self) -> int:
         n = ctypes.c_size_t()
-        _check(load_library().tfl_workspace_bytes(self._h, ctypes.byref(n)))
+        _check(self._L.tfl_workspace_bytes(self._h, ctypes.byref(n)), self._L)
         return n.value
 
     @property
     def plan_name(self) -> str:
-        return load_library().tfl_plan_name(self._h).decode()
+        return self._L.tfl_plan_name(self._h).decode()
 
     @property
     def plan_path(self) -> str:
-        return PATH_NAMES.get(load_library().tfl_plan_path(self._h), "?")
+        return PATH_NAMES.get(self._L.tfl_plan_path(self._h), "?")
 
     def forward_raw(self, x: int, lens: int, y: int, ws: int, ws_bytes: int, stream: int) -> None:
-        _check(load_library().tfl_forward(self._h, x, lens, y, ws, ws_bytes, stream))
+        _check(self._L.tfl_forward(self._h, x, lens, y, ws, ws_bytes, stream), self._L)
 
     def timer_arm(self, stage: str, max_launches: int) -> None:
-        _check(load_library().tfl_timer_arm(self._h, STAGES[stage], int(max_launches)))
+        _check(self._L.tfl_timer_arm(self._h, STAGES[stage], int(max_launches)), self._L)
 
     def timer_read(self):
         """(summed kernel ms, launches) of the armed stage since arming."""
         ms = ctypes.c_float()
         n = ctypes.c_int32()
-        _check(load_library().tfl_timer_read(self._h, ctypes.byref(ms), ctypes.byref(n)))
+        _check(self._L.tfl_timer_read(self._h, ctypes.byref(ms), ctypes.byref(n)), self._L)
         return ms.value, n.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
-            load_library().tfl_destroy(self._h)
+            self._L.tfl_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -162,7 +165,7 @@ class Encoder:
     torch tensors on the device, in the I/O dtype, nn.Linear layout."""
 
     def __init__(self, n_layers, d_model, n_heads, d_ffn, batch, seq_len, dtype, layers,
-                 ln_eps=0.0, force_path="auto"):
+                 ln_eps=0.0, force_path="auto", lib_path: str = LIB_PATH):
         import torch
         self.torch_dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
         self.dtype = dtype
@@ -174,7 +177,7 @@ class Encoder:
                     raise ValueError(f"layer tensor {k} must be a {dtype} device tensor")
         ptrs = [{k: lw[k].data_ptr() for k in LAYER_KEYS} for lw in self._layers]
         cfg = make_config(n_layers, d_model, n_heads, d_ffn, batch, seq_len, dtype, ln_eps, force_path)
-        self.handle = Handle(cfg, ptrs)
+        self.handle = Handle(cfg, ptrs, lib_path)
         self._ws = None
 
     @property

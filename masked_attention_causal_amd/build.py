@@ -1,9 +1,13 @@
-"""Build libtfl.so (HIP, gfx950) in-tree with hipcc.
+"""Build libtfl.so (HIP, gfx950) in-tree with hipcc, and its audit copy.
 
     python -m masked_attention_causal_amd.build
 
 Every translation unit is compiled for gfx950 only.  Packed fp32 VALU
 instructions are disabled for device code.
+
+libtfl_audit.so is the same sources built with TFL_AUDIT=1 (attention masks
+on every key tile and tile counters; include/tfl_audit.h).  Only the tests
+load it.
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtfl.so")
+AUDIT_LIB = os.path.join(PKG, "libtfl_audit.so")
 
 SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "gemm_pipe.hip", "attn.hip", "ln.hip", "seq.hip", "seq_small.hip",
            "pq.hip", "pq_f32.hip", "pq_f16.hip", "pq_bf16.hip"]
@@ -45,30 +50,43 @@ EXTRA: dict = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans
                "seq.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, objdir, defs = job
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *FLAGS, *defs, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, audit: bool = True) -> str:
+    """Compiles libtfl.so (and, with audit, libtfl_audit.so) from scratch."""
+    variants = [(LIB, os.path.join(BUILD, "product"), [])]
+    if audit:
+        variants.append((AUDIT_LIB, os.path.join(BUILD, "audit"), ["-DTFL_AUDIT=1"]))
+    jobs = []
+    for _, objdir, defs in variants:
+        os.makedirs(objdir, exist_ok=True)
+        jobs += [(src, objdir, defs) for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, jobs))
+    for i, (out, _, _) in enumerate(variants):
+        _link(objs[i * len(SOURCES):(i + 1) * len(SOURCES)], out)
+        if verbose:
+            print(f"built {out}")
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, audit="--no-audit" not in sys.argv)
     sys.exit(0)

@@ -185,6 +185,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale_log2;
 
+    int n_vis = 0;                               // tiles scored by this wave (audit build)
     gload(0);
     sstore(0);
     __syncthreads();
@@ -194,6 +195,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
         if (t + 1 < ntiles) gload(k0 + KT);
         // A wave whose queries all precede this tile has nothing to add.
         if (k0 <= qw0 + BQW - 1) {
+            if constexpr (MASK_ALL) n_vis++;
             const LT* ks = Ks[buf];
             const LT* vs = Vs[buf];
             f32x4 s[4];
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
                 }
             }
             // ---- scale, mask (boundary tiles only), online softmax
-            const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+            const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) {
@@ -297,6 +299,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
     // ---- normalise and write O [B*L, d] at this head's columns
     l_run += __shfl_xor(l_run, 16, WAVE);
     l_run += __shfl_xor(l_run, 32, WAVE);
+    if constexpr (MASK_ALL) {
+        if (lane == 0) audit_add(p.audit, AUD_TILED_WAVE, n_vis);
+        if (tid == 0) audit_add(p.audit, AUD_TILED_WG, ntiles);
+    }
     if (!qok) return;
     const float inv = 1.0f / l_run;
     OpT* out = (OpT*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
@@ -390,6 +396,7 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     const float sl2 = p.scale_log2;
     const int ix16 = (lane ^ 16) << 2, ix32 = (lane ^ 32) << 2;  // ds_bpermute byte indices
 
+    int n_vis = 0;  // tiles scored by this wave (audit build)
 #pragma unroll
     for (int s = 0; s < ST - 1; s++)
         if (s < ntiles) issue(s, s);
@@ -402,6 +409,7 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
         if (t + ST - 1 < ntiles) issue(t + ST - 1, (t + ST - 1) % ST);
         const int k0 = t * KT;
         if (k0 > qw0 + 15) continue;  // this wave's queries all precede the tile
+        if constexpr (MASK_ALL) n_vis++;
         const char* ks = lds + (t % ST) * SB;
         const char* kls = ks + KB;
         const char* vs = ks + KB * (SPLIT ? 2 : 1);
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
         // running max on raw scores (scale > 0), then one FMA per score into
         // the hardware exp2 (its flushing of results below 2^-126 is far
         // below the fp16 rounding of the weights and next to a row sum >= 1)
-        const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+        const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 4; kb++)
@@ -479,6 +487,10 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
 
     l_run += __shfl_xor(l_run, 16, WAVE);
     l_run += __shfl_xor(l_run, 32, WAVE);
+    if constexpr (MASK_ALL) {
+        if (lane == 0) audit_add(p.audit, AUD_TILED_WAVE, n_vis);
+        if (tid == 0) audit_add(p.audit, AUD_TILED_WG, ntiles);
+    }
     if (!qok) return;
     const float inv = 1.0f / l_run;
     f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
@@ -569,6 +581,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     // reference, and no weight underflows that the running max would keep.
     constexpr float RESCALE = 8.f;
     float m_ref = 0.f;
+    int n_vis = 0;  // tiles scored by this wave (audit build)
 
     // waves 0-3 load the tiles (one chunk per thread per plane); the others
     // issue no loads, so their waits below return at once
@@ -616,6 +629,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
         if (loader && t + ST - 1 < ntiles) issue(t + ST - 1, (BUF + ST - 1) % ST);
         const int k0 = t * KT;
         if (k0 > qw0 + 15) return;
+        if constexpr (MASK_ALL) n_vis++;
         // key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
         f32x4 sc[8];
         f16x4 ka[8], kl[8];
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 #pragma unroll
         for (int i = 0; i < (SPLIT ? 8 : 4); i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, SPLIT ? 24 : 8, 0);
-        const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+        const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 8; kb++)
@@ -700,6 +714,10 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 
     // lsum row 0 (lanes 0..15, element 0) holds the weight sum of query c16
     const float l = __shfl(lsum[0], c16, WAVE);
+    if constexpr (MASK_ALL) {
+        if (lane == 0) audit_add(p.audit, AUD_TILED_WAVE, n_vis);
+        if (tid == 0) audit_add(p.audit, AUD_TILED_WG, ntiles);
+    }
     if (!qok) return;
     const float inv = 1.0f / l;
     f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;

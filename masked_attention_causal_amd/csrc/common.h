@@ -20,6 +20,36 @@ struct bf16 {
 
 static constexpr int WAVE = 64;
 
+// ---------------------------------------------------------------- audit build
+// A second copy of the library, built with TFL_AUDIT=1 for the tests only,
+// checks two claims of "KernelForge", "Challenges" about the attention loop:
+// (1) evaluating the mask only on key tiles that reach past the diagonal or
+// the padding boundary gives bit-identical results to evaluating it on every
+// tile, and (2) the tiles visited are exactly those holding an allowed key,
+// M(M+1)/2 of M^2 at full length.  In that build every attention kernel masks
+// every tile it visits (MASK_ALL) and adds the tiles it visits to counters in
+// device memory (audit_add).  In the product build both compile to nothing.
+#ifndef TFL_AUDIT
+#define TFL_AUDIT 0
+#endif
+constexpr bool MASK_ALL = TFL_AUDIT != 0;
+// Counter slots (uint64 each).
+enum AuditSlot {
+    AUD_TILED_WG = 0,    // layer-wise attention: key tiles staged per workgroup
+    AUD_TILED_WAVE = 1,  // layer-wise attention: key tiles scored per 16-query wave
+    AUD_SEQ_WAVE = 2,    // fused SEQ kernel: 32-key chunks scored per 16-query wave
+    AUD_PQ_WG = 3,       // PQ attention tasks: key tiles staged per task
+    AUD_PQ_WAVE = 4,     // PQ attention tasks: key tiles scored per 16-query wave
+    AUD_SLOTS = 8
+};
+__device__ __forceinline__ void audit_add(unsigned long long* ctr, int slot, unsigned long long v) {
+#if TFL_AUDIT
+    if (ctr) atomicAdd(ctr + slot, v);
+#else
+    (void)ctr, (void)slot, (void)v;
+#endif
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float to_f32(float v) { return v; }

@@ -50,6 +50,7 @@ struct AttnArgs {
     const int32_t* lens;
     int B, H, L, Lp, d;
     float scale_log2;  // log2(e) / sqrt(dh); the head-dim-16 kernel reads K already multiplied by it
+    unsigned long long* audit;  // tile counters of the audit build (null otherwise)
 };
 
 // Weight pointers of one layer (same fields as tfl_layer).
@@ -67,15 +68,13 @@ struct SeqArgs {
     int B, L, F, n_layers;
     float eps;
     float scale_log2;
+    unsigned long long* audit;  // tile counters of the audit build (null otherwise)
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
-// Persistent task-queue path: whole stack in one launch, tasks popped from an
-// atomic queue in dependency order.  Counter block layout (int32):
-//   [0] queue head, [1] watchdog flag, [PQ_CTR_HDR ..) ready[n_layers][B*NT],
-//   then done[n_layers][B*NT].
-constexpr int PQ_CTR_HDR = 64;
-
+// PQ path: the stack as a task list over 64-row tiles (layer-0 QKV
+// projection, split-K attention, fused row tasks), run as one launch per
+// stage of the list.
 struct PqArgs {
     const void* x;   // [B, L, d] I/O dtype
     void* y;         // [B, L, d] I/O dtype
@@ -83,10 +82,8 @@ struct PqArgs {
     int B, L, Lp, NT, F, n_layers;
     int KS;          // key tiles per attention split
     int Ctot;        // (tile, split) pairs per (sequence, head)
-    int n_tasks;
     float eps;
     float scale_log2;
-    int* ctr;        // counter block (zeroed by the launcher each forward)
     float* X;        // [B*L, d] fp32 residual stream between layers
     _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 (hi part for layer 0)
     _Float16* Kh;
@@ -95,6 +92,7 @@ struct PqArgs {
     _Float16* Vt;    // [n_layers][B, H, dh, Lp] fp16
     float* Op;       // [B*H*Ctot][64][dh] fp32 partial attention outputs
     float2* ML;      // [B*H*Ctot][64] (running max in log2 units, sum)
+    unsigned long long* audit;  // tile counters of the audit build (null otherwise)
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
@@ -119,9 +117,8 @@ hipError_t launch_seq(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
 bool seq_small_supported(int d, int dh, int f, int L, int n_layers);
 hipError_t launch_seq_small(Mode m, int d, int dh, const SeqArgs& a, hipStream_t s);
 bool pq_supported(Mode m, int d, int dh, int f, int n_layers);
-// single_launch: one persistent launch that resolves dependencies with
-// counters; otherwise one launch per stage (QKV0, then ATT and ROW per layer).
-hipError_t launch_pq(Mode m, int d, int dh, const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s);
+// One launch per stage of the task list: QKV0, then ATT and ROW per layer.
+hipError_t launch_pq(Mode m, int d, int dh, const PqArgs& a, hipStream_t s);
 bool seq_supported(Mode m, int d, int dh, int f, int L, int n_layers);
 
 // Row layout of the LayerNorm kernel: lanes per row and float4 chunks per lane.

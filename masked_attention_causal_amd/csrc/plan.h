@@ -20,11 +20,10 @@ struct Plan {
     size_t op;      // operand element size (4 in F32 mode, 2 otherwise)
     // workspace offsets in bytes (TILED)
     size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G;
-    // persistent task-queue path: key tiles per split, (tile, split) pairs per
-    // (sequence, head), tasks, counters, and workspace offsets
-    int pq_ks, pq_ctot, pq_tasks, pq_nctr;
-    bool pq_single;   // one persistent launch (true) or one launch per stage
-    size_t off_ctr, off_pX, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML;
+    // PQ path: key tiles per split, (tile, split) pairs per (sequence, head),
+    // tasks, and workspace offsets
+    int pq_ks, pq_ctot, pq_tasks;
+    size_t off_pX, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML;
     size_t ws_bytes;
 };
 
@@ -38,6 +37,10 @@ struct StageTimer {
 };
 
 size_t dtype_size(int dtype);
+
+// Device counters the attention kernels add their visited tiles to in the
+// audit build (set through tfl_audit_attach); null in the product build.
+extern unsigned long long* audit_counters;
 
 // The dispatcher's rule for a valid configuration (tfl_path, never AUTO).
 int choose_path(const tfl_config& cfg);

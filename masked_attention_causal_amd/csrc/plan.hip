@@ -17,6 +17,8 @@ namespace tfl {
 
 size_t dtype_size(int dtype) { return dtype == TFL_F32 ? 4 : 2; }
 
+unsigned long long* audit_counters = nullptr;
+
 static Mode mode_of(int dtype) { return dtype == TFL_F32 ? MODE_F32 : (dtype == TFL_F16 ? MODE_F16 : MODE_BF16); }
 
 // Compute units of the target part (MI355X); the rule below compares the
@@ -33,7 +35,7 @@ int choose_path(const tfl_config& c) {
     if (seq_small_supported(c.d_model, dh, c.d_ffn, c.seq_len, c.n_layers)) return TFL_PATH_SEQ;
     // Few long sequences: fewer (sequence, head, 64-query tile) units than
     // compute units, so per-stage launches leave most of the chip idle; one
-    // persistent launch with split-K attention tasks fills it instead.
+    // task list with split-K attention tasks over 64-row tiles fills it instead.
     const long units = (long)c.batch * c.n_heads * ((c.seq_len + 63) / 64);
     if (units < PQ_CU_COUNT && pq_supported(m, c.d_model, dh, c.d_ffn, c.n_layers)) return TFL_PATH_PQ;
     return TFL_PATH_TILED;
@@ -54,9 +56,14 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         *why = "unknown dtype";
         return TFL_E_INVALID;
     }
-    if (c.force_path < TFL_PATH_AUTO || c.force_path > TFL_PATH_TILED) {
+    if (c.force_path < TFL_PATH_AUTO || c.force_path > TFL_PATH_PQ_SINGLE) {
         *why = "unknown force_path";
         return TFL_E_INVALID;
+    }
+    if (c.force_path == TFL_PATH_PQ_SINGLE) {
+        *why = "the single persistent launch of the PQ tasks is disabled: its one GPU run did not finish and "
+               "no cause has been shown; TFL_PATH_PQ runs the same tasks as one launch per stage";
+        return TFL_E_UNSUPPORTED;
     }
     const int dh = c.d_model / c.n_heads;
     if (dh != 16 && dh != 32 && dh != 64) {
@@ -118,17 +125,12 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         const long n_att = (long)q.B * q.H * q.pq_ctot;
         const long n_tasks = BNT + (long)q.n_layers * (n_att + BNT);
         if (n_tasks > INT_MAX / 2) {
-            *why = "too many tasks for the persistent path";
+            *why = "too many tasks for the PQ path";
             return TFL_E_UNSUPPORTED;
         }
         q.pq_tasks = (int)n_tasks;
-        // The single persistent launch stays off: one GPU run of it did not
-        // finish, with no cause found yet.  Stage launches run the same tasks.
-        q.pq_single = false;
-        q.pq_nctr = PQ_CTR_HDR + 2 * q.n_layers * BNT;
         const size_t slots = (size_t)n_att;
         size_t o = 0;
-        q.off_ctr = o; o += up256((size_t)q.pq_nctr * 4);
         q.off_pX = o;  o += up256(Td * 4);
         q.off_Qh = o;  o += up256(Td * 2 * q.n_layers);
         q.off_Kh = o;  o += up256(Td * 2 * q.n_layers);
@@ -138,7 +140,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         q.off_Op = o;  o += up256(slots * 64 * q.dh * 4);
         q.off_ML = o;  o += up256(slots * 64 * 8);
         q.ws_bytes = o;
-        std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d/%s/%s", q.pq_ks, q.pq_single ? "queue" : "staged", q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
+        std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d/staged/%s", q.pq_ks, q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
         *p = q;
         return TFL_OK;
     }
@@ -223,6 +225,7 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         a.Kl = (const f16*)K + (size_t)P.T * P.d;
         a.B = P.B; a.H = P.H; a.L = P.L; a.Lp = P.Lp; a.d = P.d;
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+        a.audit = audit_counters;
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
             if ((e = tm.done(launch_attn(P.mode, P.dh, l == 0, a, s))) != hipSuccess) return e;
@@ -276,6 +279,7 @@ static hipError_t run_seq(const Plan& P, const tfl_layer* layers, const void* x,
     a.n_layers = P.n_layers;
     a.eps = P.eps;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+    a.audit = audit_counters;
     for (int l = 0; l < P.n_layers; l++) {
         const tfl_layer& w = layers[l];
         a.lw[l] = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b,
@@ -300,10 +304,8 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
     a.n_layers = P.n_layers;
     a.KS = P.pq_ks;
     a.Ctot = P.pq_ctot;
-    a.n_tasks = P.pq_tasks;
     a.eps = P.eps;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
-    a.ctr = (int*)(ws + P.off_ctr);
     a.X = (float*)(ws + P.off_pX);
     a.Qh = (_Float16*)(ws + P.off_Qh);
     a.Kh = (_Float16*)(ws + P.off_Kh);
@@ -312,13 +314,14 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
     a.Vt = (_Float16*)(ws + P.off_pVt);
     a.Op = (float*)(ws + P.off_Op);
     a.ML = (float2*)(ws + P.off_ML);
+    a.audit = audit_counters;
     for (int l = 0; l < P.n_layers; l++) {
         const tfl_layer& w = layers[l];
         a.lw[l] = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b,
                             w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
     }
     Timed tm(T, TFL_STAGE_FUSED, s);
-    return tm.done(launch_pq(P.mode, P.d, P.dh, a, P.pq_nctr, P.pq_single, s));
+    return tm.done(launch_pq(P.mode, P.d, P.dh, a, s));
 }
 
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,

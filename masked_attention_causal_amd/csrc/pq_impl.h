@@ -1,32 +1,28 @@
-// Persistent task-queue path (PQ): the whole encoder stack in one launch for
-// few, long sequences.  Every workgroup of a resident grid repeatedly takes
-// the next task id from an atomic queue head, waits on the dependency
-// counters of that task, runs it and releases its own counter; there is no
-// device-wide barrier.  This is the persistent, DAG-scheduled family of
-// "Hyper-optimized megakernel-hybrid transformer inference" ("Problem
-// decomposition" and "Performance optimization": a task graph fixed per
-// shape ahead of time, workgroups pop tasks until none are left, no grid
-// synchronisation).
+// PQ path for few, long sequences: the whole encoder stack as a fixed task
+// list over 64-row tiles, so that a batch-1 sequence of a few thousand tokens
+// still spreads over hundreds of workgroups.  It follows the task-graph
+// family of "Hyper-optimized megakernel-hybrid transformer inference",
+// "Problem decomposition" (a graph of tasks fixed per shape ahead of time;
+// tasks sized so that every compute unit has work).
 //
-// Task graph (64-row tiles of one sequence; t = tile, s = key split):
-//   QKV0(b,t)           layer-0 projection of x rows      -> ready[0][b,t]
+// Task list (64-row tiles of one sequence; t = tile, s = key split):
+//   QKV0(b,t)           layer-0 projection of x rows
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
-//                       needs ready[l][b,t'] for its key tiles and t
-//                                                          -> done[l][b,t]
 //   ROW(l,b,t)          merge of the partials, out-projection + residual +
 //                       LayerNorm, FFN (exact-erf GELU) + residual +
 //                       LayerNorm, then the next layer's QKV projection of
 //                       the same rows (or y after the last layer)
-//                       needs done[l][b,t] == H * nsplit(t)
-//                                                          -> ready[l+1][b,t]
-// Ids are handed out in a topological order (QKV0, then per layer all ATT,
-// then all ROW), so a task only ever waits on tasks that were taken before
-// it by running workgroups: the grid cannot deadlock whatever its size.
+// The list runs as one launch per stage (QKV0, then ATT and ROW of every
+// layer), workgroup i of a stage running its task i; each stage depends only
+// on earlier launches on the stream.  The pages' single persistent launch
+// (workgroups popping task ids from a device queue and waiting on dependency
+// counters) is not offered: its one run on the GPU did not finish, and no
+// cause has been shown.
 //
 // Splitting one query tile's keys over several tasks and combining the
 // partial softmax states (m, l, O) exactly is the split-K attention of
-// "KernelForge" ("Challenges": balancing causal work by construction).
+// "KernelForge", "What's next" (balancing causal work by construction).
 // Key split boundaries depend on seq_len only, so the task list is fixed
 // per plan; splits past a sequence's valid length do no work.
 //
@@ -50,11 +46,6 @@ namespace tfl {
 constexpr int PQ_THREADS = 256;
 constexpr int PQ_RT = 64;     // rows per tile (one tile = one attention query tile)
 constexpr int PQ_FC = 128;    // FFN features per chunk
-constexpr int PQ_GRID_CUS = 256;   // MI355X compute units
-// A dependency wait longer than this (in ticks of the 100 MHz constant clock
-// read by wall_clock64) is treated as a broken schedule: 0.5 s, far beyond the
-// run time of any forward this path is chosen for.
-constexpr uint64_t PQ_WAIT_TICKS = 50000000ull;
 
 // Index helpers of the task list (host and device).
 __host__ __device__ inline int pq_nsplit(int t, int ks) { return t / ks + 1; }
@@ -496,6 +487,10 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale_log2;
 
+    if constexpr (MASK_ALL) {
+        if (tid == 0 && ntl > 0) audit_add(p.audit, AUD_PQ_WG, ntl);
+    }
+    int n_vis = 0;  // tiles scored by this wave (audit build)
     if (ntl > 0) {
         gload(kt0 * KT);
         sstore(0);
@@ -506,6 +501,7 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
             const int k0 = (kt0 + it) * KT;
             if (it + 1 < ntl) gload(k0 + KT);
             if (k0 <= qw0 + 15) {
+                if constexpr (MASK_ALL) n_vis++;
                 const f16* ks = Ks + buf * KT * KLD;
                 const f16* kls = Kls + buf * KT * KLD;
                 const f16* vs = Vs + buf * DH * VLD;
@@ -526,7 +522,7 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                         }
                     }
                 }
-                const bool need_mask = (k0 + KT - 1 > qw0) || (k0 + KT > len);
+                const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
                 float mx = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
@@ -581,6 +577,9 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     }
     l_run += __shfl_xor(l_run, 16, WAVE);
     l_run += __shfl_xor(l_run, 32, WAVE);
+    if constexpr (MASK_ALL) {
+        if (lane == 0) audit_add(p.audit, AUD_PQ_WAVE, n_vis);
+    }
     // partial state of (b, h, t, s): unnormalised O, running max (log2 units), sum
     const size_t slot = ((size_t)b * H + h) * p.Ctot + pq_pairs_before(t, p.KS) + s;
     const int qr = 16 * wave + c16;
@@ -817,37 +816,7 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     qkv_rows<WT, D, DH>(p, l + 1, b, t, smem, tid);
 }
 
-// ------------------------------------------------------------------ scheduler
-
-// Waits until every counter ctr[i], i in [first, first + count), and ctr[extra]
-// reaches `need`.  Wave 0 polls; on a wait far beyond any legal run time the
-// watchdog flag is raised and the wait abandoned, so every wave still exits.
-__device__ __forceinline__ void pq_wait(int* flags, int first, int count, int extra, int need, int* err, int tid) {
-    if (tid < 64) {
-        const int lane = tid;
-        const bool mine = lane < count || lane == 63;
-        int* f = flags + (lane == 63 ? extra : first + lane);
-        const uint64_t t0 = wall_clock64();
-        for (;;) {
-            bool ok = true;
-            if (mine) ok = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
-            if (__all(ok)) break;
-            if (wall_clock64() - t0 > PQ_WAIT_TICKS) {
-                if (lane == 0) __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-__device__ __forceinline__ void pq_release(int* flag, int tid) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
+// ------------------------------------------------------------------ task list
 
 // Task id -> (kind, layer, sequence, head, tile, split).  kind: 0 QKV0, 1 ATT, 2 ROW.
 struct PqTask {
@@ -902,10 +871,10 @@ __device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* s
         task_row<WT, D, DH>(p, k.l, k.b, k.t, smem, tid);
 }
 
-// Stage-ordered execution of the same task list: one launch per stage
-// (QKV0, then ATT and ROW of every layer), workgroup i running task
-// begin + i.  Every dependency of a stage was completed by an earlier launch
-// on the stream, so no workgroup ever waits on another.
+// One launch per stage of the task list (QKV0, then ATT and ROW of every
+// layer), workgroup i running task begin + i.  Every dependency of a stage
+// was completed by an earlier launch on the stream, so no workgroup ever
+// waits on another.
 template <class WT, int D, int DH>
 __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int begin) {
     typedef PqTile<WT, D, DH> TL;
@@ -915,89 +884,35 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int b
 }
 
 template <class WT, int D, int DH>
-__global__ __launch_bounds__(PQ_THREADS, 2) void pq_kernel(PqArgs p) {
-    typedef PqTile<WT, D, DH> TL;
-    constexpr int H = D / DH;
-    __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
-    __shared__ int s_task;
-    const int tid = threadIdx.x;
-    const int BNT = p.B * p.NT;
-    int* ready = p.ctr + PQ_CTR_HDR;
-    int* done = ready + p.n_layers * BNT;
-#pragma unroll 1
-    for (;;) {
-        if (tid == 0) s_task = __hip_atomic_fetch_add(p.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const int task = s_task;
-        __syncthreads();
-        if (task >= p.n_tasks) break;
-        const PqTask k = pq_decode<H>(p, task);
-        if (k.kind == 0) {
-            pq_run<WT, D, DH>(p, k, smem, tid);
-            pq_release(ready + k.b * p.NT + k.t, tid);
-        } else if (k.kind == 1) {
-            const int kt0 = k.s * p.KS, kt1 = min(kt0 + p.KS, k.t + 1);
-            pq_wait(ready + k.l * BNT + k.b * p.NT, kt0, kt1 - kt0, k.t, 1, p.ctr + 1, tid);
-            pq_run<WT, D, DH>(p, k, smem, tid);
-            pq_release(done + k.l * BNT + k.b * p.NT + k.t, tid);
-        } else {
-            const int idx = k.l * BNT + k.b * p.NT + k.t;
-            pq_wait(done, idx, 1, idx, H * pq_nsplit(k.t, p.KS), p.ctr + 1, tid);
-            pq_run<WT, D, DH>(p, k, smem, tid);
-            if (k.l + 1 < p.n_layers)
-                pq_release(ready + (k.l + 1) * BNT + k.b * p.NT + k.t, tid);
-            else
-                __syncthreads();
-        }
-    }
-}
-
-static __global__ void pq_zero_kernel(int* p, int n) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
-
-template <class WT, int D, int DH>
-hipError_t pq_launch_t(const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s) {
+hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     typedef PqTile<WT, D, DH> TL;
     static_assert(TL::SMEM <= 160 * 1024, "LDS budget");
-    // Resident grid: the part's compute units times the workgroups one of
-    // them holds (LDS-limited; registers are bounded to two waves per SIMD).
-    // The queue makes progress with any grid size, so this only sets how
-    // many tasks run at once.
-    constexpr int PER_CU = TL::SMEM <= 80 * 1024 ? 2 : 1;
+    const int BNT = a.B * a.NT, n_att = a.B * (D / DH) * a.Ctot;
+    int begin = 0;
+    auto stage = [&](int n) {
+        hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, begin);
+        begin += n;
+        return hipGetLastError();
+    };
     hipError_t e;
-    if (!single_launch) {
-        const int BNT = a.B * a.NT, n_att = a.B * (D / DH) * a.Ctot;
-        int begin = 0;
-        auto stage = [&](int n) {
-            hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, begin);
-            begin += n;
-            return hipGetLastError();
-        };
+    if ((e = stage(BNT)) != hipSuccess) return e;
+    for (int l = 0; l < a.n_layers; l++) {
+        if ((e = stage(n_att)) != hipSuccess) return e;
         if ((e = stage(BNT)) != hipSuccess) return e;
-        for (int l = 0; l < a.n_layers; l++) {
-            if ((e = stage(n_att)) != hipSuccess) return e;
-            if ((e = stage(BNT)) != hipSuccess) return e;
-        }
-        return hipSuccess;
     }
-    const int grid = min(a.n_tasks, PQ_GRID_CUS * PER_CU);
-    hipLaunchKernelGGL(pq_zero_kernel, dim3((n_ctr + 255) / 256), dim3(256), 0, s, a.ctr, n_ctr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((pq_kernel<WT, D, DH>), dim3(grid), dim3(PQ_THREADS), 0, s, a);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <class WT>
-hipError_t pq_launch_mode(int d, int dh, const PqArgs& a, int n_ctr, bool single_launch, hipStream_t s) {
+hipError_t pq_launch_mode(int d, int dh, const PqArgs& a, hipStream_t s) {
     if (dh == 64) {
-        if (d == 64) return pq_launch_t<WT, 64, 64>(a, n_ctr, single_launch, s);
-        if (d == 128) return pq_launch_t<WT, 128, 64>(a, n_ctr, single_launch, s);
-        if (d == 256) return pq_launch_t<WT, 256, 64>(a, n_ctr, single_launch, s);
+        if (d == 64) return pq_launch_t<WT, 64, 64>(a, s);
+        if (d == 128) return pq_launch_t<WT, 128, 64>(a, s);
+        if (d == 256) return pq_launch_t<WT, 256, 64>(a, s);
     } else if (dh == 32) {
-        if (d == 64) return pq_launch_t<WT, 64, 32>(a, n_ctr, single_launch, s);
-        if (d == 128) return pq_launch_t<WT, 128, 32>(a, n_ctr, single_launch, s);
-        if (d == 256) return pq_launch_t<WT, 256, 32>(a, n_ctr, single_launch, s);
+        if (d == 64) return pq_launch_t<WT, 64, 32>(a, s);
+        if (d == 128) return pq_launch_t<WT, 128, 32>(a, s);
+        if (d == 256) return pq_launch_t<WT, 256, 32>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -453,6 +453,9 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
             const int kmax = min(q0 + 16 * TPW, len);
             const int swk = swz<KCPR>(c16);
             const int nch = (kmax + 31) >> 5;  // 32-key chunks that matter (1 or 2)
+            if constexpr (MASK_ALL) {
+                if (lane == 0 && b < p.B) audit_add(p.audit, AUD_SEQ_WAVE, nch);
+            }
             f16x8 qh[NHC][TPW], ql[NHC][TPW];
 #pragma unroll
             for (int tb = 0; tb < TPW; tb++)
@@ -499,6 +502,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                     // keys of this chunk can be masked only if it reaches past the
                     // wave's first query or past the sequence end (wave-uniform)
                     const bool need_mask =
+                        MASK_ALL ||
                         __builtin_amdgcn_readfirstlane((cc * 32 + 31 > q0) || (cc * 32 + 31 >= len) ? 1 : 0) != 0;
 #pragma unroll
                     for (int tb = 0; tb < TPW; tb++) {

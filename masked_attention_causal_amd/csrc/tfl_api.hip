@@ -1,6 +1,7 @@
 // C ABI of tfl: argument checks, the frozen per-shape plan, the workspace
 // layout and the launch sequence.  Declarations and contracts: include/tfl.h.
 #include "tfl.h"
+#include "tfl_audit.h"
 
 #include <cstdlib>
 #include <cstring>
@@ -92,6 +93,8 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
     if (overlap(x, io_bytes, y, io_bytes)) return fail(TFL_E_INVALID, "tfl_forward: y overlaps x");
     if (P.ws_bytes > 0 && overlap(y, io_bytes, workspace, P.ws_bytes))
         return fail(TFL_E_INVALID, "tfl_forward: y overlaps the workspace");
+    if (P.ws_bytes > 0 && overlap(x, io_bytes, workspace, P.ws_bytes))
+        return fail(TFL_E_INVALID, "tfl_forward: x overlaps the workspace");
     hipStream_t s = (hipStream_t)hip_stream;
 
     const char* chk = std::getenv("TFL_CHECK");
@@ -109,16 +112,6 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
     tfl::StageTimer* tm = h->timer.stage ? &h->timer : nullptr;
     const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s, tm);
     if (e != hipSuccess) return hip_fail(e, "tfl_forward: kernel launch");
-    if (check && P.path == TFL_PATH_PQ && P.pq_single) {
-        // The persistent path raises a flag instead of waiting forever on a
-        // dependency that never completes; read it back.
-        int32_t flag = 0;
-        hipError_t e2 = hipMemcpyAsync(&flag, (char*)workspace + P.off_ctr + sizeof(int32_t), sizeof(flag),
-                                       hipMemcpyDeviceToHost, s);
-        if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
-        if (e2 != hipSuccess) return hip_fail(e2, "tfl_forward: TFL_CHECK read of the task-queue flag");
-        if (flag != 0) return fail(TFL_E_INTERNAL, "tfl_forward: task-queue dependency wait timed out");
-    }
     return TFL_OK;
 }
 
@@ -191,5 +184,14 @@ const char* tfl_plan_name(const tfl_handle* h) { return h ? h->plan.name : "(nul
 int32_t tfl_plan_path(const tfl_handle* h) { return h ? h->plan.path : -1; }
 
 const char* tfl_last_error(void) { return g_err.c_str(); }
+
+#if TFL_AUDIT
+// Test build only (include/tfl_audit.h).
+tfl_status tfl_audit_attach(void* counters) {
+    if (counters && !aligned(counters, 8)) return fail(TFL_E_INVALID, "tfl_audit_attach: counters not 8-byte aligned");
+    tfl::audit_counters = (unsigned long long*)counters;
+    return TFL_OK;
+}
+#endif
 
 }  // extern "C"

@@ -50,13 +50,14 @@ def oracle_forward(inp, eps: float = 1e-5) -> np.ndarray:
     return oracle.forward(inp.x64(), inp.lens, inp.layers64(), inp.w.H, eps)
 
 
-def gpu_forward(inp, force_path: str = "auto", eps: float = 0.0, return_encoder: bool = False):
+def gpu_forward(inp, force_path: str = "auto", eps: float = 0.0, return_encoder: bool = False, lib_path=None):
     import torch
 
     import masked_attention_causal_amd as tfl
     w = inp.w
     layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
-    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, ln_eps=eps, force_path=force_path)
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, ln_eps=eps, force_path=force_path,
+                      lib_path=lib_path or tfl.LIB_PATH)
     x = tfl.to_device(inp.x, w.dtype)
     lens = torch.from_numpy(inp.lens).cuda()
     y = enc.forward(x, lens)

@@ -60,7 +60,7 @@ def test_dispatcher_rules():
 
 def test_pq_dispatch_rules():
     # fewer (sequence, head, 64-query tile) units than compute units and no
-    # sequence-resident fit -> persistent task-queue path
+    # sequence-resident fit -> PQ path (task list over 64-row tiles)
     assert tfl.plan_for(2, 128, 2, 512, 1, 4096, "f32")[1] == "pq"
     assert tfl.plan_for(2, 256, 4, 1024, 1, 1000, "bf16")[1] == "pq"
     assert tfl.plan_for(2, 128, 2, 512, 2, 4096, "f32")[1] == "tiled"    # 256 units
@@ -69,6 +69,23 @@ def test_pq_dispatch_rules():
     with pytest.raises(tfl.TflError) as e:
         tfl.plan_for(2, 64, 4, 256, 1, 300, "f16", force_path="pq")
     assert e.value.status == 2
+
+
+def test_pq_single_launch_is_refused():
+    # the single persistent launch of the PQ tasks stays disabled until the
+    # cause of its one unfinished GPU run is shown (include/tfl.h)
+    with pytest.raises(tfl.TflError) as e:
+        tfl.plan_for(2, 128, 2, 512, 1, 4096, "f32", force_path="pq_single")
+    assert e.value.status == 2 and "persistent" in str(e.value)
+
+
+def test_audit_build_exports_and_product_does_not(lib):
+    # the audit entry point (include/tfl_audit.h) exists only in the test build
+    assert not hasattr(lib, "tfl_audit_attach")
+    audit = tfl.load_library(tfl.AUDIT_LIB_PATH)
+    assert ctypes.cast(audit.tfl_audit_attach, ctypes.c_void_p).value
+    for n in declared_symbols():
+        assert hasattr(audit, n), n
 
 
 def test_pq_workspace_layout():
@@ -82,7 +99,7 @@ def test_pq_workspace_layout():
     pairs = NT + ks * q * (q - 1) // 2 + q * r          # (tile, split) pairs per (sequence, head)
     assert pairs == sum(t // ks + 1 for t in range(NT))
     T, dh, Lp = B * L, d // H, NT * 64
-    need = (up((64 + 2 * n_layers * B * NT) * 4) + up(T * d * 4) + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
+    need = (up(T * d * 4) + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
             + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8))
     assert ws == need
 
@@ -135,6 +152,7 @@ def test_forward_argument_checks_before_any_device_call(lib):
         ((X, LN, Y, WS + 16, n), 1),      # workspace misaligned
         ((X, LN, X + 256, WS, n), 1),     # y overlaps x
         ((X, LN, WS + 512, WS, n), 1),    # y overlaps workspace
+        ((WS + 256, LN, Y, WS, n), 1),    # x overlaps workspace
     ]
     for args, status in cases:
         with pytest.raises(tfl.TflError) as e:

@@ -1,4 +1,5 @@
-"""GPU parity of the persistent task-queue (PQ) path against the fp64 oracle.
+"""GPU parity of the PQ path (task list over 64-row tiles, one launch per
+stage) against the fp64 oracle.
 
 Shapes cover every (d, head dim) the path supports, the three I/O dtypes,
 ragged sequence ends (L not a multiple of 64), several key splits per query
@@ -90,7 +91,7 @@ def test_pq_check_mode_and_clamped_lengths(monkeypatch):
     with pytest.raises(tfl.TflError) as e:
         h.forward_raw(x.data_ptr(), bad.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
     assert e.value.status == 1
-    # a good forward in check mode also reads back the task-queue watchdog flag
+    # a good forward passes the host-side length check
     h.forward_raw(x.data_ptr(), lens.data_ptr(), y.data_ptr(), ws.data_ptr(), h.workspace_bytes, st)
     monkeypatch.delenv("TFL_CHECK")
     say("[pq clamp] lengths 0 and 81 behave as 1 and L")
@@ -102,8 +103,8 @@ def test_pq_check_mode_and_clamped_lengths(monkeypatch):
 
 
 def test_pq_repeated_forwards_reuse_the_workspace():
-    # counters are re-zeroed by every forward: back-to-back calls on one
-    # workspace give identical results
+    # every forward overwrites the partial attention states it reads: back-to-
+    # back calls on one workspace give identical results
     import torch
 
     import masked_attention_causal_amd as tfl
@@ -125,3 +126,14 @@ def test_pq_repeated_forwards_reuse_the_workspace():
         assert np.array_equal(ys[0], ys[i]), i
     assert_gate(ys[0], oracle_forward(inp), "pq repeated")
     enc.close()
+
+
+@pytest.mark.skip(reason="the single persistent launch of the PQ tasks (TFL_PATH_PQ_SINGLE) is disabled: "
+                         "its one GPU run did not finish and no cause has been shown; tfl_create returns "
+                         "TFL_E_UNSUPPORTED for it (checked on the CPU in tests/test_abi_host.py)")
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+def test_pq_single_launch(scale):
+    w = synth.WORKLOADS["latency_d128_b1_l4096"]
+    inp = synth.make_inputs(w, 0, scale)
+    say(f"[pq single] scale={scale}")
+    assert_gate(gpu_forward(inp, force_path="pq_single"), oracle_forward(inp), f"pq single scale {scale}")
