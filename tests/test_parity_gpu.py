@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from masked_attention_causal_amd import synth
-from tests.gate import assert_gate, gate, gpu_forward, oracle_forward, say
+from tests.gate import assert_gate, assert_gate_near_ties, gate, gpu_forward, oracle_forward, say
 
 pytestmark = pytest.mark.gpu
 
@@ -111,7 +111,7 @@ def test_batch4096_workload_every_sequence(seed, scale):
     say(f"[batch4096 all] seed={seed} scale={inp.scale:.4g}")
     y = gpu_forward(inp)
     say(f"[batch4096 all] oracle on all {BATCH.B} sequences")
-    assert_gate(y, oracle_forward(inp), f"batch4096 seed {seed} scale {inp.scale}")
+    assert_gate_near_ties(y, oracle_forward(inp), inp, f"batch4096 seed {seed} scale {inp.scale}")
 
 
 @pytest.mark.parametrize("seed,scale", [(0, None), (0, 1e-2), (0, 1e-1), (0, 10.0), (0, 1e2)])
