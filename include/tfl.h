@@ -140,6 +140,26 @@ tfl_status tfl_workspace_bytes(const tfl_handle *h, size_t *bytes);
 tfl_status tfl_forward(tfl_handle *h, const void *x, const int32_t *valid_len, void *y,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Size of the static device workspace behind tfl_forward_noalloc (32 MiB). */
+#define TFL_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as tfl_forward, on the same kernels, with the workspace taken from
+ * a static device array of TFL_STATIC_WORKSPACE_BYTES that the library owns
+ * (each GPU holds its own copy until the process ends).  No device or host
+ * memory is allocated.  Arguments as for tfl_forward; the current HIP device
+ * must be the one that x, y, valid_len and the stream belong to.
+ * TFL_CHECK is not honoured here (its length check copies to host memory).
+ * Errors: TFL_E_WORKSPACE when the plan needs more workspace than the static
+ * array holds (tfl_workspace_bytes() > TFL_STATIC_WORKSPACE_BYTES); otherwise
+ * as tfl_forward.  All calls on one GPU share that GPU's array: calls that
+ * overlap in time on one GPU (several streams, several threads) race and give
+ * undefined results; calls ordered on one stream are safe.  Nothing in the
+ * array has to start at zero: every forward writes what it reads. */
+tfl_status tfl_forward_noalloc(tfl_handle *h, const void *x, const int32_t *valid_len, void *y,
+                               void *hip_stream);
+
 /* Frees the handle (host memory only; the borrowed weights stay the
  * caller's).  NULL is accepted. */
 tfl_status tfl_destroy(tfl_handle *h);

@@ -15,8 +15,9 @@ AUDIT_LIB_PATH = os.path.join(PKG, "libtfl_audit.so")   # test build (include/tf
 
 LAYER_KEYS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
               "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
-SYMBOLS = ("tfl_create", "tfl_workspace_bytes", "tfl_forward", "tfl_destroy",
+SYMBOLS = ("tfl_create", "tfl_workspace_bytes", "tfl_forward", "tfl_forward_noalloc", "tfl_destroy",
            "tfl_plan_name", "tfl_plan_path", "tfl_timer_arm", "tfl_timer_read", "tfl_last_error")
+STATIC_WORKSPACE_BYTES = 32 << 20   # TFL_STATIC_WORKSPACE_BYTES
 STAGES = {"prep": 1, "qkv": 2, "attn": 3, "out": 4, "ln": 5, "ffn1": 6, "ffn2": 7, "fused": 8}
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
@@ -65,6 +66,8 @@ def load_library(path: str = LIB_PATH):
     L.tfl_workspace_bytes.restype = ctypes.c_int
     L.tfl_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.tfl_forward.restype = ctypes.c_int
+    L.tfl_forward_noalloc.argtypes = [vp, vp, vp, vp, vp]
+    L.tfl_forward_noalloc.restype = ctypes.c_int
     L.tfl_destroy.argtypes = [vp]
     L.tfl_destroy.restype = ctypes.c_int
     L.tfl_plan_name.argtypes = [vp]
@@ -125,6 +128,10 @@ class Handle:
 
     def forward_raw(self, x: int, lens: int, y: int, ws: int, ws_bytes: int, stream: int) -> None:
         _check(self._L.tfl_forward(self._h, x, lens, y, ws, ws_bytes, stream), self._L)
+
+    def forward_noalloc_raw(self, x: int, lens: int, y: int, stream: int) -> None:
+        """tfl_forward_noalloc: the library's static workspace, no allocation."""
+        _check(self._L.tfl_forward_noalloc(self._h, x, lens, y, stream), self._L)
 
     def timer_arm(self, stage: str, max_launches: int) -> None:
         _check(self._L.tfl_timer_arm(self._h, STAGES[stage], int(max_launches)), self._L)

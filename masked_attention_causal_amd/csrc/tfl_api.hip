@@ -5,6 +5,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -36,6 +37,35 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 tfl_status hip_fail(hipError_t e, const char* what) {
     return fail(TFL_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Workspace of tfl_forward_noalloc: one static array in device memory, which
+// every GPU the library runs on holds (at its own address) until the process
+// ends.  Host code never passes the array's name to a kernel or copy (on the
+// host it is a stand-in, not a device address): the address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t STATIC_WS_MAX = (size_t)TFL_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[STATIC_WS_MAX];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+tfl_status static_workspace(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "tfl_forward_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(TFL_E_UNSUPPORTED, "tfl_forward_noalloc: device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "tfl_forward_noalloc: hipGetSymbolAddress of the static workspace");
+        if (!p || !aligned(p, 256)) return fail(TFL_E_INTERNAL, "tfl_forward_noalloc: static workspace address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TFL_OK;
 }
 
 }  // namespace
@@ -77,8 +107,10 @@ tfl_status tfl_workspace_bytes(const tfl_handle* h, size_t* bytes) {
     return TFL_OK;
 }
 
-tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, void* y, void* workspace,
-                       size_t workspace_bytes, void* hip_stream) {
+// tfl_forward with the host-side length check of TFL_CHECK=1 allowed or not
+// (that check copies the lengths into host memory).
+static tfl_status forward_impl(tfl_handle* h, const void* x, const int32_t* valid_len, void* y, void* workspace,
+                               size_t workspace_bytes, void* hip_stream, bool allow_check) {
     if (!h) return fail(TFL_E_INVALID, "tfl_forward: null handle");
     if (!x || !y || !valid_len) return fail(TFL_E_INVALID, "tfl_forward: null x, y or valid_len");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(valid_len, 4))
@@ -97,7 +129,7 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
         return fail(TFL_E_INVALID, "tfl_forward: x overlaps the workspace");
     hipStream_t s = (hipStream_t)hip_stream;
 
-    const char* chk = std::getenv("TFL_CHECK");
+    const char* chk = allow_check ? std::getenv("TFL_CHECK") : nullptr;
     const bool check = chk && chk[0] == '1';
     if (check) {
         std::vector<int32_t> lens(P.B);
@@ -113,6 +145,26 @@ tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, v
     const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s, tm);
     if (e != hipSuccess) return hip_fail(e, "tfl_forward: kernel launch");
     return TFL_OK;
+}
+
+tfl_status tfl_forward(tfl_handle* h, const void* x, const int32_t* valid_len, void* y, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    return forward_impl(h, x, valid_len, y, workspace, workspace_bytes, hip_stream, true);
+}
+
+tfl_status tfl_forward_noalloc(tfl_handle* h, const void* x, const int32_t* valid_len, void* y, void* hip_stream) {
+    if (!h) return fail(TFL_E_INVALID, "tfl_forward_noalloc: null handle");
+    const size_t need = h->plan.ws_bytes;
+    if (need > STATIC_WS_MAX)
+        return fail(TFL_E_WORKSPACE, "tfl_forward_noalloc: the plan " + std::string(h->plan.name) + " needs " +
+                                         std::to_string(need) + " bytes of workspace; the static workspace holds " +
+                                         std::to_string(STATIC_WS_MAX) + " (use tfl_forward with a workspace)");
+    void* ws = nullptr;
+    if (need > 0) {
+        const tfl_status st = static_workspace(&ws);
+        if (st != TFL_OK) return st;
+    }
+    return forward_impl(h, x, valid_len, y, ws, need, hip_stream, false);
 }
 
 static void timer_release(tfl::StageTimer& t) {

@@ -71,6 +71,20 @@ def test_pq_dispatch_rules():
     assert e.value.status == 2
 
 
+def test_noalloc_refuses_plans_beyond_the_static_workspace(lib):
+    # the d=1024 workload's layer-wise plan needs 136 MiB of workspace; the
+    # static array holds 32 MiB: refused before any device call
+    w = synth.WORKLOADS["gemm_d1024_b8_l512"]
+    cfg = tfl.make_config(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype)
+    h = tfl.Handle(cfg, [{k: 0x10000 for k in tfl.LAYER_KEYS}] * w.n_layers)
+    assert h.workspace_bytes > tfl.binding.STATIC_WORKSPACE_BYTES
+    with pytest.raises(tfl.TflError) as e:
+        h.forward_noalloc_raw(0x100000, 0x200000, 0x300000, 0)
+    assert e.value.status == 3 and "static workspace" in str(e.value)
+    h.close()
+    assert lib.tfl_forward_noalloc(None, 0x100000, 0x200000, 0x300000, None) == 1
+
+
 def test_pq_single_launch_is_refused():
     # the single persistent launch of the PQ tasks stays disabled until the
     # cause of its one unfinished GPU run is shown (include/tfl.h)
