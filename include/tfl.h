@@ -180,7 +180,9 @@ typedef enum {
     TFL_STAGE_LN = 5,    /* residual LayerNorm */
     TFL_STAGE_FFN1 = 6,  /* FFN up-projection + exact-erf GELU */
     TFL_STAGE_FFN2 = 7,  /* FFN down-projection + bias + residual */
-    TFL_STAGE_FUSED = 8  /* whole-stack kernels of the SEQ and PQ paths */
+    TFL_STAGE_FUSED = 8, /* whole-stack kernels of the SEQ and PQ paths */
+    TFL_STAGE_ROW = 9    /* layer-wise path, d_model <= 256, 16-bit I/O: one kernel per layer
+                            for out-projection + LayerNorm + FFN + LayerNorm + next QKV */
 } tfl_stage;
 
 /* Measurement aid.  Arms HIP-event timing of every launch of one stage in

@@ -18,7 +18,7 @@ LAYER_KEYS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
 SYMBOLS = ("tfl_create", "tfl_workspace_bytes", "tfl_forward", "tfl_forward_noalloc", "tfl_destroy",
            "tfl_plan_name", "tfl_plan_path", "tfl_timer_arm", "tfl_timer_read", "tfl_last_error")
 STATIC_WORKSPACE_BYTES = 32 << 20   # TFL_STATIC_WORKSPACE_BYTES
-STAGES = {"prep": 1, "qkv": 2, "attn": 3, "out": 4, "ln": 5, "ffn1": 6, "ffn2": 7, "fused": 8}
+STAGES = {"prep": 1, "qkv": 2, "attn": 3, "out": 4, "ln": 5, "ffn1": 6, "ffn2": 7, "fused": 8, "row": 9}
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 PATHS = {"auto": 0, "seq": 1, "pq": 2, "tiled": 3, "pq_single": 4}
@@ -66,8 +66,9 @@ def load_library(path: str = LIB_PATH):
     L.tfl_workspace_bytes.restype = ctypes.c_int
     L.tfl_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.tfl_forward.restype = ctypes.c_int
-    L.tfl_forward_noalloc.argtypes = [vp, vp, vp, vp, vp]
-    L.tfl_forward_noalloc.restype = ctypes.c_int
+    if hasattr(L, "tfl_forward_noalloc"):   # absent only from builds that predate it
+        L.tfl_forward_noalloc.argtypes = [vp, vp, vp, vp, vp]
+        L.tfl_forward_noalloc.restype = ctypes.c_int
     L.tfl_destroy.argtypes = [vp]
     L.tfl_destroy.restype = ctypes.c_int
     L.tfl_plan_name.argtypes = [vp]

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libtfl.so")
 AUDIT_LIB = os.path.join(PKG, "libtfl_audit.so")
 
 SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "gemm_pipe.hip", "attn.hip", "ln.hip", "seq.hip", "seq_small.hip",
-           "pq.hip", "pq_f32.hip", "pq_f16.hip", "pq_bf16.hip"]
+           "pq.hip", "pq_f32.hip", "pq_f16.hip", "pq_bf16.hip", "rowfuse.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -96,6 +96,28 @@ struct PqArgs {
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
+// Fused row kernel of the layer-wise path (16-bit I/O, d in {64, 128, 256}):
+// for one 64-row tile, the out-projection of the attention output + bias +
+// residual + LayerNorm, the FFN (exact-erf GELU) + bias + residual +
+// LayerNorm, then the next layer's QKV projection (head-major Q and K, V^T)
+// or, after the last layer, y.
+struct RowArgs {
+    const void* O;   // [B*L, d] fp16 attention output of this layer
+    float* X;        // [B*L, d] fp32 residual stream: layer input, overwritten with the layer output
+    void* y;         // [B, L, d] I/O dtype, written after the last layer
+    _Float16* Q;     // next layer: [B, H, L, dh] fp16
+    _Float16* K;     // next layer: [B, H, L, dh] fp16, multiplied by kscale
+    _Float16* Vt;    // next layer: [B, H, dh, Lp] fp16
+    int B, L, Lp, F;
+    float eps;
+    float kscale;    // 0 means 1
+    int last;        // 1: write y instead of the next layer's Q, K, V^T
+    LayerPtrs w;     // this layer
+    LayerPtrs wn;    // next layer (unused when last)
+};
+bool row_supported(Mode m, int d, int dh, int f);
+hipError_t launch_row(Mode m, int d, int dh, const RowArgs& a, hipStream_t s);
+
 // Fixed tile shapes shared with the planner.
 constexpr int ATT_KT = 64;   // keys per attention tile
 constexpr int ATT_BQ = 64;   // queries per attention workgroup

@@ -12,6 +12,7 @@ namespace tfl {
 struct Plan {
     int path;       // tfl_path actually used
     int seq_kind;   // SEQ path: 0 MFMA kernel (two sequences per workgroup), 1 small-shape kernel
+    bool row_fused; // TILED path: one fused row kernel per layer after attention
     char name[64];
     Mode mode;
     int n_layers, d, H, dh, f, B, L, Lp;

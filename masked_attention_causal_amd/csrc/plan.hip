@@ -147,19 +147,27 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     // V^T rows are padded to whole 128-key tiles (the head-dim-16 attention
     // kernel reads 128 keys per tile).
     q.Lp = (c.seq_len + 127) / 128 * 128;
+    // d_model <= 256 with 16-bit I/O: after attention, one fused row kernel
+    // per layer (out-projection, LayerNorms, FFN, next QKV), so Z, X1 and
+    // the FFN activations never reach HBM
+    q.row_fused = row_supported(mode, q.d, q.dh, q.f);
     size_t o = 0;
     q.off_Xr = o; o += up256(Td * 4);
-    q.off_X1 = o; o += up256(Td * 4);
-    q.off_Z = o;  o += up256(Td * 4);
+    if (!q.row_fused) {
+        q.off_X1 = o; o += up256(Td * 4);
+        q.off_Z = o;  o += up256(Td * 4);
+    }
     q.off_Q = o;  o += up256(Td * 4);
     q.off_K = o;  o += up256(Td * 4);
     q.off_A = o;  o += up256(Td * q.op);
     q.off_O = o;  o += up256(Td * q.op);
     q.off_Vt = o; o += up256((size_t)q.B * q.d * q.Lp * q.op);
-    q.off_G = o;  o += up256((size_t)T * q.f * q.op);
+    if (!q.row_fused) {
+        q.off_G = o;  o += up256((size_t)T * q.f * q.op);
+    }
     q.ws_bytes = o;
-    std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s", ATT_BQ, ATT_KT,
-                  q.mode == MODE_F32 ? "f32" : "f16op");
+    std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s%s", ATT_BQ, ATT_KT,
+                  q.mode == MODE_F32 ? "f32" : "f16op", q.row_fused ? "/rowfused" : "");
     *p = q;
     return TFL_OK;
 }
@@ -213,7 +221,9 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         g.split = l == 0;
         // the head-dim-16 attention kernel (16-bit modes) reads K pre-scaled
         if (P.mode != MODE_F32 && P.dh == 16) g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
-        {
+        // with the fused row kernel, layers after the first get their Q, K
+        // and V^T from the previous layer's row kernel
+        if (!P.row_fused || l == 0) {
             Timed tm(T, TFL_STAGE_QKV, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_QKV, g, s))) != hipSuccess) return e;
         }
@@ -229,6 +239,25 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
             if ((e = tm.done(launch_attn(P.mode, P.dh, l == 0, a, s))) != hipSuccess) return e;
+        }
+        if (P.row_fused) {
+            // out-projection .. LayerNorm 2 and the next layer's QKV in one launch
+            RowArgs r{};
+            r.O = O; r.X = Xr; r.y = y;
+            r.Q = (f16*)Q; r.K = (f16*)K; r.Vt = (f16*)Vt;
+            r.B = P.B; r.L = P.L; r.Lp = P.Lp; r.F = P.f;
+            r.eps = P.eps;
+            r.kscale = P.dh == 16 ? (float)(1.4426950408889634 / std::sqrt((double)P.dh)) : 0.f;
+            r.last = last ? 1 : 0;
+            r.w = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b, w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
+            if (!last) {
+                const tfl_layer& n = layers[l + 1];
+                r.wn = LayerPtrs{n.w_qkv, n.b_qkv, n.w_o, n.b_o, n.ln1_g, n.ln1_b, n.w_1, n.b_1, n.w_2, n.b_2, n.ln2_g,
+                                 n.ln2_b};
+            }
+            Timed tm(T, TFL_STAGE_ROW, s);
+            if ((e = tm.done(launch_row(P.mode, P.d, P.dh, r, s))) != hipSuccess) return e;
+            continue;
         }
 
         GemmArgs r{};

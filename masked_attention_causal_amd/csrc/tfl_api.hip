@@ -179,7 +179,7 @@ static void timer_release(tfl::StageTimer& t) {
 
 tfl_status tfl_timer_arm(tfl_handle* h, int32_t stage, int32_t max_launches) {
     if (!h) return fail(TFL_E_INVALID, "tfl_timer_arm: null handle");
-    if (stage < TFL_STAGE_PREP || stage > TFL_STAGE_FUSED || max_launches < 1 || max_launches > 1 << 20)
+    if (stage < TFL_STAGE_PREP || stage > TFL_STAGE_ROW || max_launches < 1 || max_launches > 1 << 20)
         return fail(TFL_E_INVALID, "tfl_timer_arm: bad stage or launch count");
     timer_release(h->timer);
     tfl::StageTimer t;

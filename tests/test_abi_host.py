@@ -119,12 +119,25 @@ def test_pq_workspace_layout():
 
 
 def test_workspace_covers_the_tiled_buffers():
+    # d_model <= 256, 16-bit I/O: fused row kernel, no Z / X1 / FFN buffers:
+    # residual, Q, K (fp32-sized: hi and lo fp16 planes), A, O, V^T
     w = synth.WORKLOADS["stream_d64_b1_l100000"]
-    _, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
+    plan, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
+    assert plan.endswith("/rowfused"), plan
     T = w.B * w.L
     Lp = (w.L + 127) // 128 * 128          # V^T rows padded to whole 128-key tiles
+    need = 3 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2
+    assert need <= ws <= need + 6 * 256
+    # d_model 1024: separate kernels, all buffers
+    w = synth.WORKLOADS["gemm_d1024_b8_l512"]
+    plan, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype)
+    assert not plan.endswith("/rowfused"), plan
+    T = w.B * w.L
+    Lp = (w.L + 127) // 128 * 128
     need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2
     assert need <= ws <= need + 9 * 256
+    # fp32 I/O stays on the separate kernels
+    assert not tfl.plan_for(2, 64, 4, 256, 1, 4096, "f32", force_path="tiled")[0].endswith("/rowfused")
 
 
 @pytest.mark.parametrize("cfg,status", [
