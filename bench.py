@@ -12,7 +12,11 @@ Prints one JSON line: sequences/s (value), ms per forward, the roofline of
 the dominant kernel (its algorithmic bytes or FLOPs per launch over its
 average launch time, measured with HIP events on the forward's stream inside
 the timed region) and the fp64 CPU oracle timed on a bounded sample of the
-same workload on this host's cores.
+same workload on this host's cores.  Beside the headline, "workloads" gives
+the same figures (fewer steps, no CPU leg) for the four other named
+workloads, and "dispatch" the paths the dispatcher chooses between, timed
+in interleaved rounds with rotating order on the workloads where the
+choice matters.
 """
 from __future__ import annotations
 
@@ -66,6 +70,12 @@ def stage_work(w, stage, lens):
         return 2.0 * T * d * f, T * d * op + f * d * wt + T * f * op
     if stage == "ffn2":
         return 2.0 * T * f * d, T * f * op + d * f * wt + 2 * T * d * 4
+    if stage == "row":
+        # fused row kernel of the layer-wise path, per launch (a non-last layer):
+        # out-projection, FFN, next layer's QKV; O in, residual in/out twice, Q K V out
+        flops = 2.0 * T * d * d + 4.0 * T * d * f + 2.0 * T * d * 3 * d
+        nbytes = T * d * op + 4 * T * d * 4 + 3 * T * d * op + (4 * d * d + 2 * d * f) * wt
+        return flops, nbytes
     if stage == "fused":
         S = allowed_pairs(lens, w.L)
         flops = w.n_layers * (2.0 * T * d * 3 * d + 4.0 * d * S + 2.0 * T * d * d + 4.0 * T * d * f)
@@ -75,6 +85,13 @@ def stage_work(w, stage, lens):
 
 
 STAGES_TILED = ("prep", "qkv", "attn", "out", "ln", "ffn1", "ffn2")
+STAGES_ROWFUSED = ("prep", "qkv", "attn", "row")
+
+
+def plan_stages(plan, path):
+    if path in ("seq", "pq"):
+        return ("fused",)
+    return STAGES_ROWFUSED if plan.endswith("/rowfused") else STAGES_TILED
 
 def arith_dtype(plan):
     """Operand type the plan's products are computed in (fp16 operands with
@@ -96,6 +113,8 @@ def stage_kernel(stage, plan, w):
         if arith_dtype(plan) == "f32":
             return "attn_kernel", ("attn.hip",) + base
         return ("attn_ring16_kernel" if w.dh == 16 else "attn_ring_kernel"), ("attn.hip",) + base
+    if stage == "row":
+        return "row_kernel", ("rowfuse.hip", "pq_impl.h") + base
     if stage in ("qkv", "out", "ffn1", "ffn2"):
         if arith_dtype(plan) == "f32":
             return "gemm_kernel", ("gemm.hip",) + base
@@ -133,7 +152,9 @@ def measured_traffic(stage, workload, plan, w):
     return None
 
 
-def launches_per_forward(stage, n_layers):
+def launches_per_forward(stage, n_layers, plan=""):
+    if stage == "qkv" and plan.endswith("/rowfused"):
+        return 1   # later layers' QKV runs inside the fused row kernel
     return {"prep": 1, "ln": 2 * n_layers, "fused": 1}.get(stage, n_layers)
 
 
@@ -210,6 +231,137 @@ def cpu_baseline(w, inp, target_s=15.0):
             "cpu": cpu_model(), "sample": f"first {n} of {w.B} sequences of the same seeded batch, {dt:.1f} s"}
 
 
+def measure(tfl, torch, w, name, inp, steps, warmup, path="auto"):
+    """Warm-up, per-stage survey, then `steps` forwards between HIP events
+    with the dominant stage's launches timed as they run; then a separate
+    pass of single-forward events for the distribution."""
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=path)
+    x = tfl.to_device(inp.x, w.dtype)
+    lens = torch.from_numpy(inp.lens).cuda()
+    y = torch.empty_like(x)
+    ws = enc.workspace()
+    h = enc.handle
+    plan = enc.plan_name
+    print(f"# workload {name} plan {plan} workspace {h.workspace_bytes / 2**20:.1f} MiB", file=sys.stderr,
+          flush=True)
+
+    # first call in this process for this plan, then warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    enc.forward(x, lens, y, ws)
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(warmup):
+        enc.forward(x, lens, y, ws)
+    torch.cuda.synchronize()
+
+    # per-stage survey (not timed): which kernel dominates the forward
+    stages = plan_stages(plan, enc.plan_path)
+    survey = {}
+    reps = 3 if w.B * w.L < 50000 else 1
+    for st in stages:
+        per = launches_per_forward(st, w.n_layers, plan)
+        h.timer_arm(st, per * reps)
+        for _ in range(reps):
+            enc.forward(x, lens, y, ws)
+        ms, n = h.timer_read()
+        survey[st] = ms / reps
+    dom = max(survey, key=survey.get)
+
+    # timed region: K steps, dominant stage timed with HIP events as it runs
+    per = launches_per_forward(dom, w.n_layers, plan)
+    h.timer_arm(dom, per * steps)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        enc.forward(x, lens, y, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dom_ms, dom_n = h.timer_read()
+    ms_step = total_ms / steps
+    roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1), plan)
+    roof["kernel"] = stage_kernel(dom, plan, w)[0]
+    roof["launches_timed"] = dom_n
+    roof["traffic"] = measured_traffic(dom, name, plan, w)
+
+    # per-forward distribution, in a pass of its own after the timed region
+    # (one event pair per forward; the timed region above has none of these)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        enc.forward(x, lens, y, ws)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
+    pick = lambda q: round(per_us[min(len(per_us) - 1, int(q * len(per_us)))], 2)
+    dist = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "forwards": len(per_us)}
+
+    # whole-forward figure for context
+    tot_flops = 0.0
+    fstages = ("fused",) if enc.plan_path in ("seq", "pq") else ("qkv", "attn", "out", "ffn1", "ffn2")
+    for st in fstages:
+        tot_flops += stage_work(w, st, inp.lens)[0] * (1 if st == "fused" else w.n_layers)
+    launches = sum(launches_per_forward(st, w.n_layers, plan) for st in stages)
+    if enc.plan_path == "pq":
+        launches = 1 + 2 * w.n_layers
+    res = {
+        "plan": plan,
+        "ms_per_step": ms_step,
+        "sequences_per_s": w.B / (ms_step / 1e3),
+        "roofline": roof,
+        "forward_tflops": round(tot_flops / (ms_step / 1e3) / 1e12, 2),
+        "stage_ms_per_forward": {k: round(v, 4) for k, v in survey.items()},
+        "us_per_forward_dist": dist,
+        "cold_first_call_ms": round(cold_ms, 2),
+        "launches_per_forward": launches + (1 if enc.plan_path == "tiled" and "f16op" in plan else 0),
+    }
+    enc.close()
+    return res
+
+
+def interleaved(tfl, torch, w, inp, paths, rounds=6, iters=5):
+    """Median us per forward of each path, timed in rounds of `iters`
+    forwards with the order of the paths rotated every round."""
+    import numpy as np
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
+    x = tfl.to_device(inp.x, w.dtype)
+    lens = torch.from_numpy(inp.lens).cuda()
+    encs = {p: tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=p) for p in paths}
+    ys = {p: torch.empty_like(x) for p in paths}
+    for p in paths:
+        for _ in range(2):
+            encs[p].forward(x, lens, ys[p])
+    torch.cuda.synchronize()
+    times = {p: [] for p in paths}
+    for r in range(rounds):
+        order = paths[r % len(paths):] + paths[:r % len(paths)]
+        for p in order:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                encs[p].forward(x, lens, ys[p])
+            b.record()
+            torch.cuda.synchronize()
+            times[p].append(a.elapsed_time(b) * 1e3 / iters)
+    out = {p: {"plan": encs[p].plan_name, "us_median": round(float(np.median(times[p])), 2),
+               "us_rounds": [round(v, 1) for v in times[p]]} for p in paths}
+    for e in encs.values():
+        e.close()
+    return out
+
+
+# Steps and warm-up for the workloads reported beside the headline (the
+# 100k-token forward takes ~7 ms, the others well under 1 ms).
+EXTRA_STEPS = {"tiny_d32_b4_l32": (50, 10), "gemm_d1024_b8_l512": (20, 5),
+               "latency_d128_b1_l4096": (30, 5), "stream_d64_b1_l100000": (4, 1)}
+# Workloads whose plan choice is timed against its alternative.
+DISPATCH = {"batch4096_d256_l64": ["seq", "tiled"], "latency_d128_b1_l4096": ["pq", "tiled"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +371,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--path", default="auto", choices=["auto", "seq", "pq", "tiled"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the path comparison")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -226,7 +379,6 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import masked_attention_causal_amd as tfl
@@ -236,80 +388,32 @@ def main():
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w, args.seed)
     torch.cuda.set_device(0)
-    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
-    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=args.path)
-    x = tfl.to_device(inp.x, w.dtype)
-    lens = torch.from_numpy(inp.lens).cuda()
-    y = torch.empty_like(x)
-    ws = enc.workspace()
-    h = enc.handle
-    print(f"# workload {name} plan {enc.plan_name} workspace {h.workspace_bytes / 2**20:.1f} MiB", file=sys.stderr,
-          flush=True)
+    m = measure(tfl, torch, w, name, inp, args.steps, args.warmup, args.path)
+    ms_step = m["ms_per_step"]
 
-    # first call in this process, then warm-up
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    enc.forward(x, lens, y, ws)
-    torch.cuda.synchronize()
-    cold_ms = (time.perf_counter() - t0) * 1e3
-    for _ in range(args.warmup):
-        enc.forward(x, lens, y, ws)
-    torch.cuda.synchronize()
-
-    # per-stage survey (not timed): which kernel dominates the forward
-    stages = ("fused",) if enc.plan_path in ("seq", "pq") else STAGES_TILED
-    survey = {}
-    for st in stages:
-        per = launches_per_forward(st, w.n_layers)
-        h.timer_arm(st, per * 3)
-        for _ in range(3):
-            enc.forward(x, lens, y, ws)
-        ms, n = h.timer_read()
-        survey[st] = ms / 3.0
-    dom = max(survey, key=survey.get)
-
-    # timed region: K steps, dominant stage timed with HIP events as it runs
-    per = launches_per_forward(dom, w.n_layers)
-    h.timer_arm(dom, per * args.steps)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        enc.forward(x, lens, y, ws)
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    dom_ms, dom_n = h.timer_read()
-    ms_step = total_ms / args.steps
-    seqs = w.B / (ms_step / 1e3)
-    roof = roofline(w, dom, inp.lens, dom_ms / max(dom_n, 1), enc.plan_name)
-    roof["kernel"] = stage_kernel(dom, enc.plan_name, w)[0]
-    roof["launches_timed"] = dom_n
-    roof["traffic"] = measured_traffic(dom, name, enc.plan_name, w)
-
-    # per-forward distribution, in a pass of its own after the timed region
-    # (one event pair per forward; the timed region above has none of these)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record()
-    for i in range(args.steps):
-        enc.forward(x, lens, y, ws)
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
-    pick = lambda q: round(per_us[min(len(per_us) - 1, int(q * len(per_us)))], 2)
-    dist = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "forwards": len(per_us)}
-
-    # whole-forward roofline figure for context
-    tot_flops = 0.0
-    for st in (("fused",) if enc.plan_path in ("seq", "pq") else ("qkv", "attn", "out", "ffn1", "ffn2")):
-        tot_flops += stage_work(w, st, inp.lens)[0] * (1 if st == "fused" else w.n_layers)
-    fwd_tflops = tot_flops / (ms_step / 1e3) / 1e12
+    extra, dispatch = {}, {}
+    if not args.no_extra:
+        for other, (st, wu) in EXTRA_STEPS.items():
+            if other == name:
+                continue
+            ow = synth.WORKLOADS[other]
+            oi = synth.make_inputs(ow, args.seed)
+            r = measure(tfl, torch, ow, other, oi, st, wu)
+            extra[other] = {"plan": r["plan"], "us_per_forward": round(r["ms_per_step"] * 1e3, 2),
+                            "sequences_per_s": round(r["sequences_per_s"], 2), "steps": st,
+                            "launches_per_forward": r["launches_per_forward"], "roofline": r["roofline"],
+                            "stage_ms_per_forward": r["stage_ms_per_forward"],
+                            "us_per_forward_dist": r["us_per_forward_dist"]}
+            del oi
+        for dn, paths in DISPATCH.items():
+            dw = synth.WORKLOADS[dn]
+            di = inp if dn == name else synth.make_inputs(dw, args.seed)
+            dispatch[dn] = interleaved(tfl, torch, dw, di, paths)
 
     cpu = None if args.no_cpu else cpu_baseline(w, inp)
     out = {
         "metric": "sequences/s per stack forward (with us per forward and roofline fraction)",
-        "value": round(seqs, 1),
+        "value": round(m["sequences_per_s"], 1),
         "unit": "sequences/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -319,20 +423,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": arith_dtype(enc.plan_name),
+        "dtype": arith_dtype(m["plan"]),
         "data": "synthetic (seeded normals, weights N(0,0.02^2), random valid lengths)",
-        "config": {"workload": name, "io_dtype": w.dtype, "n_layers": w.n_layers, "d_model": w.d, "n_heads": w.H, "d_ffn": w.f,
-                   "batch": w.B, "seq_len": w.L, "valid_len": [w.len_lo, w.len_hi],
-                   "input_scale": round(inp.scale, 6), "seed": args.seed, "plan": enc.plan_name,
+        "config": {"workload": name, "io_dtype": w.dtype, "n_layers": w.n_layers, "d_model": w.d, "n_heads": w.H,
+                   "d_ffn": w.f, "batch": w.B, "seq_len": w.L, "valid_len": [w.len_lo, w.len_hi],
+                   "input_scale": round(inp.scale, 6), "seed": args.seed, "plan": m["plan"],
                    "parallelism": "single GPU"},
-        "roofline": roof,
-        "forward_tflops": round(fwd_tflops, 2),
-        "stage_ms_per_forward": {k: round(v, 4) for k, v in survey.items()},
-        "us_per_forward_dist": dist,
-        "cold_first_call_ms": round(cold_ms, 2),
+        "roofline": m["roofline"],
+        "forward_tflops": m["forward_tflops"],
+        "stage_ms_per_forward": m["stage_ms_per_forward"],
+        "us_per_forward_dist": m["us_per_forward_dist"],
+        "cold_first_call_ms": m["cold_first_call_ms"],
+        "launches_per_forward": m["launches_per_forward"],
         "cpu_baseline": cpu,
+        "workloads": extra,
+        "dispatch": dispatch,
     }
-    enc.close()
     print(json.dumps(out), flush=True)
 
 
