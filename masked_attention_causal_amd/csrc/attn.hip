@@ -358,6 +358,16 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
         qh[kk] = qok ? *(const f16x8*)(Qh + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
         if constexpr (SPLIT) ql[kk] = qok ? *(const f16x8*)(Ql + (size_t)myq * DH + kk * 32 + 8 * g) : f16x8{};
     }
+    // The query loads complete here, before any tile DMA is issued: passed
+    // through an opaque asm, the registers count as written by it, so the
+    // compiler does not wait for those loads inside the tile loop -- a wait
+    // that would also cover the DMAs issued ahead (its counter does not see
+    // them) and stall every tile on the ring's newest load.
+#pragma unroll
+    for (int kk = 0; kk < QK; kk++) {
+        asm volatile("" : "+v"(qh[kk]));
+        if constexpr (SPLIT) asm volatile("" : "+v"(ql[kk]));
+    }
 
     // Swizzle: chunk c of row r of a tile lives in slot c ^ (r % chunks-per-row).
     // DMA lane writes slot q of the tile; it fetches the chunk that belongs there.
@@ -547,8 +557,11 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 
     const int myq = qw0 + c16;
     const bool qok = myq < L;
-    const f16x4 qh = qok ? *(const f16x4*)(Qh + (size_t)myq * DH + 4 * g) : f16x4{};
-    const f16x4 ql = (SPLIT && qok) ? *(const f16x4*)(Ql + (size_t)myq * DH + 4 * g) : f16x4{};
+    f16x4 qh = qok ? *(const f16x4*)(Qh + (size_t)myq * DH + 4 * g) : f16x4{};
+    f16x4 ql = (SPLIT && qok) ? *(const f16x4*)(Ql + (size_t)myq * DH + 4 * g) : f16x4{};
+    // the query loads complete here, before any tile DMA (see attn_ring_kernel)
+    asm volatile("" : "+v"(qh));
+    if constexpr (SPLIT) asm volatile("" : "+v"(ql));
 
     // DMA: thread tid fetches K chunk slot tid & 1 of LDS row tid >> 1 and V^T
     // row tid >> 4 (chunk slot tid & 15).  LDS K row 16 kb + i holds the key
