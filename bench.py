@@ -96,7 +96,7 @@ def plan_stages(plan, path):
 def arith_dtype(plan):
     """Operand type the plan's products are computed in (fp16 operands with
     fp32 accumulation, or fp32 throughout)."""
-    return "f16" if "f16op" in plan else "f32"
+    return "f16" if ("f16op" in plan or "f16x3" in plan) else "f32"
 
 
 def stage_kernel(stage, plan, w):
@@ -110,15 +110,11 @@ def stage_kernel(stage, plan, w):
             return "seq_kernel", ("seq.hip",) + base
         return "pq_stage_kernel", ("pq_impl.h", "pq.hip") + base
     if stage == "attn":
-        if arith_dtype(plan) == "f32":
-            return "attn_kernel", ("attn.hip",) + base
         return ("attn_ring16_kernel" if w.dh == 16 else "attn_ring_kernel"), ("attn.hip",) + base
     if stage == "row":
         return "row_kernel", ("rowfuse.hip", "pq_impl.h") + base
     if stage in ("qkv", "out", "ffn1", "ffn2"):
-        if arith_dtype(plan) == "f32":
-            return "gemm_kernel", ("gemm.hip",) + base
-        return "gemm_pipe_kernel", ("gemm_pipe.hip", "gemm.hip") + base
+        return "gemm_pipe_kernel", ("gemm.hip",) + base
     if stage == "ln":
         return "ln_kernel", ("ln.hip",) + base
     if stage == "prep":
@@ -317,7 +313,10 @@ def measure(tfl, torch, w, name, inp, steps, warmup, path="auto"):
         "stage_ms_per_forward": {k: round(v, 4) for k, v in survey.items()},
         "us_per_forward_dist": dist,
         "cold_first_call_ms": round(cold_ms, 2),
-        "launches_per_forward": launches + (1 if enc.plan_path == "tiled" and "f16op" in plan else 0),
+        # the layer-wise prep stage also pads V^T and, with bf16 or fp32 I/O,
+        # converts the GEMM weights to fp16 planes (one launch per 8 layers)
+        "launches_per_forward": launches + ((1 + (0 if w.dtype == "f16" else (w.n_layers + 7) // 8))
+                                            if enc.plan_path == "tiled" else 0),
     }
     enc.close()
     return res

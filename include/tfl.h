@@ -135,8 +135,9 @@ tfl_status tfl_workspace_bytes(const tfl_handle *h, size_t *bytes);
  * Errors: TFL_E_INVALID (null or misaligned pointer, overlap, bad length
  * with TFL_CHECK=1), TFL_E_WORKSPACE (too small), TFL_E_HIP (launch failed).
  * Inputs must be finite.  The first layer's products take x rounded to fp16
- * operands on the fp16-operand paths (bf16 I/O on every path, fp32 I/O on
- * the PQ path); there |x| must stay below 65504. */
+ * operands, and weights converted to fp16, on the fp16-operand paths (bf16
+ * I/O on every path, fp32 I/O on the PQ and layer-wise paths); there |x| and
+ * every weight must stay below 65504 in magnitude. */
 tfl_status tfl_forward(tfl_handle *h, const void *x, const int32_t *valid_len, void *y,
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
@@ -173,7 +174,8 @@ int32_t tfl_plan_path(const tfl_handle *h);
 
 /* Kernel stages, for stage timing. */
 typedef enum {
-    TFL_STAGE_PREP = 1,  /* input staging: x -> fp32 residual + operand copy */
+    TFL_STAGE_PREP = 1,  /* input staging: x -> fp32 residual + operand planes; weights -> fp16 planes
+                            (bf16 / fp32 I/O); V^T padding */
     TFL_STAGE_QKV = 2,   /* fused QKV projection, head-major epilogue */
     TFL_STAGE_ATTN = 3,  /* streaming masked attention */
     TFL_STAGE_OUT = 4,   /* out-projection + bias + residual */

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtfl.so")
 AUDIT_LIB = os.path.join(PKG, "libtfl_audit.so")
 
-SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "gemm_pipe.hip", "attn.hip", "ln.hip", "seq.hip", "seq_small.hip",
+SOURCES = ["tfl_api.hip", "plan.hip", "gemm.hip", "attn.hip", "ln.hip", "seq.hip", "seq_small.hip",
            "pq.hip", "pq_f32.hip", "pq_f16.hip", "pq_bf16.hip", "rowfuse.hip"]
 ARCH = "gfx950"
 FLAGS = [
@@ -42,11 +42,14 @@ def _hipcc() -> str:
 
 
 # Per-file extra flags.  attn.hip: MFMA accumulators in VGPRs (the softmax
-# reads every score, and AGPR operands would cost a move each way).  attn.hip
+# reads every score, and AGPR operands would cost a move each way).
+# gemm.hip: the same (with AGPR accumulators the compiler copied all of them
+# to VGPRs and back at every stage of the K loop).  attn.hip
 # and seq.hip: no NaN honouring, so a max over scores needs no quieting pass
 # (the kernels never produce NaN from finite inputs; masks use -inf, which is
 # still honoured).
 EXTRA: dict = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+               "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "seq.hip": ["-fno-honor-nans"]}
 
 

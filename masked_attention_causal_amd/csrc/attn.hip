@@ -22,18 +22,18 @@
 // that owns the query, and the running max needs only a reduction across
 // the four 16-lane groups of the wave.
 //
-// Precision: F32 mode takes fp32 Q and K and multiplies them on fp32 MFMA.
-// F16/BF16 modes take Q and K as fp16 planes written by the QKV epilogue:
-// the rounded value, and for the first layer (raw inputs up to 1e3 give
-// scores near 1e5) also the rounding remainder, so scores are formed as
-// hi*hi + hi*lo + lo*hi (three MFMAs) at about fp32 accuracy.  P is rounded
-// to the operand dtype (fp16 or fp32) for the P V product; the row sum uses
-// fp32 P.
+// Precision: Q and K arrive as fp16 planes written by the QKV epilogue: the
+// rounded value and, where the scores need it, the rounding remainder, so
+// scores are formed as hi*hi + hi*lo + lo*hi (three MFMAs) at about fp32
+// accuracy.  The remainder planes are used for the first layer in the 16-bit
+// I/O modes (raw inputs up to 1e3 give scores near 1e5) and for every layer
+// with fp32 I/O.  P is rounded to fp16 for the P V product; the row sums use
+// the same weights.  With fp32 I/O the output also leaves as two fp16
+// planes (hi, and the remainder times 2^11) for the split out-projection.
 //
-// Two kernels: attn_kernel stages K and V^T through registers (F32 mode,
-// and head dim 16); attn_ring_kernel (16-bit modes, head dim 32 or 64)
-// streams them with LDS-DMA into a ring of three tile buffers, two tiles
-// ahead of the MFMAs.
+// Two kernels stream K and V^T with LDS-DMA into a ring of three tile
+// buffers, two tiles ahead of the MFMAs: attn_ring_kernel (head dim 32 or
+// 64, 64-key tiles) and attn_ring16_kernel (head dim 16, 128-key tiles).
 #include "common.h"
 #include "kernels.h"
 
@@ -48,276 +48,20 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
-template <class OpT, int DH, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs p) {
-    constexpr bool F32 = sizeof(OpT) == 4;
-    constexpr int KT = ATT_KT;
-    constexpr int BQW = 16;               // queries per wave
-    constexpr int BQ = 4 * BQW;           // queries per workgroup
-    static_assert(BQ == ATT_BQ, "planner and kernel disagree on the query tile");
-    constexpr int ND = DH / 16;           // 16-row blocks of the head dimension
-    constexpr int KLD = F32 ? DH + 1 : DH + 8;   // LDS pitch of the K tile
-    constexpr int VLD = F32 ? KT + 1 : KT + 8;   // LDS pitch of the V^T tile
-    typedef typename std::conditional<F32, float, f16>::type LT;
-    __shared__ __attribute__((aligned(16))) LT Ks[2][KT * KLD];
-    __shared__ __attribute__((aligned(16))) LT Kls[SPLIT ? 2 : 1][SPLIT ? KT * KLD : 1];
-    __shared__ __attribute__((aligned(16))) LT Vs[2][DH * VLD];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c16 = lane & 15, g = lane >> 4;
-    const int nqt = gridDim.x;
-    const int qt = nqt - 1 - (int)blockIdx.x;    // heaviest query tiles first
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int L = p.L, Lp = p.Lp;
-    int len = p.lens[b];
-    len = len < 1 ? 1 : (len > L ? L : len);     // clamp keeps every access in bounds
-    const int q0 = qt * BQ;
-    const int qw0 = q0 + wave * BQW;             // first query of this wave
-    const int kend = min(q0 + BQ, len);          // keys [0, kend) matter to the workgroup
-    const int ntiles = (kend + KT - 1) / KT;
-    const size_t bh = (size_t)b * p.H + h;
-    // F32: fp32 Q, K.  16-bit modes: fp16 hi planes (and lo planes when SPLIT).
-    const float* __restrict__ Qg = (const float*)p.Q + bh * L * DH;
-    const float* __restrict__ Kg = (const float*)p.K + bh * L * DH;
-    const f16* __restrict__ Qhg = (const f16*)p.Q + bh * L * DH;
-    const f16* __restrict__ Qlg = (const f16*)p.Ql + bh * L * DH;
-    const f16* __restrict__ Khg = (const f16*)p.K + bh * L * DH;
-    const f16* __restrict__ Klg = (const f16*)p.Kl + bh * L * DH;
-    const OpT* __restrict__ Vg = (const OpT*)p.Vt + bh * DH * Lp;
-
-    // ---- this lane's query operand (B operand of S^T = K Q^T), query qw0 + c16
-    const int myq = qw0 + c16;
-    const bool qok = myq < L;
-    constexpr int QK = F32 ? DH / 4 : (DH >= 32 ? DH / 32 : 1);
-    float qf[F32 ? QK : 1];
-    f16x8 qh8[(!F32 && DH >= 32) ? QK : 1], ql8[(!F32 && DH >= 32 && SPLIT) ? QK : 1];
-    f16x4 qh4, ql4;
-    if constexpr (F32) {
+// ---------------------------------------------------------------- LDS-DMA ring
+// Four output values of one query as fp16; with lo_plane != 0 the rounding
+// remainders times 2^11 go lo_plane elements further (fp32 I/O).
+__device__ __forceinline__ void store_o4(f16* out, const float (&v)[4], size_t lo_plane) {
+    f16x4 hv, lv;
 #pragma unroll
-        for (int ks = 0; ks < QK; ks++) qf[ks] = qok ? Qg[(size_t)myq * DH + ks * 4 + g] : 0.f;
-    } else if constexpr (DH >= 32) {
-#pragma unroll
-        for (int ks = 0; ks < QK; ks++) {
-            qh8[ks] = qok ? *(const f16x8*)(Qhg + (size_t)myq * DH + ks * 32 + g * 8) : f16x8{};
-            if constexpr (SPLIT) ql8[ks] = qok ? *(const f16x8*)(Qlg + (size_t)myq * DH + ks * 32 + g * 8) : f16x8{};
-        }
-    } else {
-        qh4 = qok ? *(const f16x4*)(Qhg + (size_t)myq * DH + g * 4) : f16x4{};
-        if constexpr (SPLIT) ql4 = qok ? *(const f16x4*)(Qlg + (size_t)myq * DH + g * 4) : f16x4{};
+    for (int e = 0; e < 4; e++) {
+        hv[e] = (f16)v[e];
+        lv[e] = (f16)((v[e] - (float)hv[e]) * 2048.0f);
     }
-
-    // ---- staging of one key tile: K rows and V^T rows through registers
-    // (F32: fp32 K, 4-float chunks; 16-bit: fp16 hi/lo planes, 8-half chunks)
-    constexpr int KE = F32 ? 4 : 8;
-    constexpr int KCH = KT * DH / KE;
-    constexpr int KPT = (KCH + 255) / 256;
-    constexpr int VE = F32 ? 4 : 8;                  // V elements per 16-byte chunk
-    constexpr int VCH = DH * KT / VE;
-    constexpr int VPT = (VCH + 255) / 256;
-    float4 rk[F32 ? KPT : 1];
-    uint4 rkh[F32 ? 1 : KPT], rkl[(!F32 && SPLIT) ? KPT : 1];
-    uint4 rv[VPT];
-
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < KPT; i++) {
-            const int c = tid + i * 256;
-            if (KCH % 256 != 0 && c >= KCH) break;
-            const int key = c / (DH / KE), col = (c % (DH / KE)) * KE;
-            const bool ok = k0 + key < L;
-            if constexpr (F32) {
-                rk[i] = ok ? *(const float4*)(Kg + (size_t)(k0 + key) * DH + col) : float4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                rkh[i] = ok ? *(const uint4*)(Khg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
-                if constexpr (SPLIT) rkl[i] = ok ? *(const uint4*)(Klg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; i++) {
-            const int c = tid + i * 256;
-            if (VCH % 256 != 0 && c >= VCH) break;
-            const int row = c / (KT / VE), kc = (c % (KT / VE)) * VE;
-            const OpT* src = Vg + (size_t)row * Lp + k0 + kc;
-            if (k0 + kc + VE <= L) {
-                rv[i] = *(const uint4*)src;
-            } else {
-                union { uint4 u; OpT e[VE]; } tmp;
-#pragma unroll
-                for (int e = 0; e < VE; e++) tmp.e[e] = (k0 + kc + e < L) ? src[e] : from_f32<OpT>(0.f);
-                rv[i] = tmp.u;
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KPT; i++) {
-            const int c = tid + i * 256;
-            if (KCH % 256 != 0 && c >= KCH) break;
-            const int key = c / (DH / KE), col = (c % (DH / KE)) * KE;
-            if constexpr (F32) {
-                const float v[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) Ks[buf][key * KLD + col + e] = v[e];
-            } else {
-                *(uint4*)&Ks[buf][key * KLD + col] = rkh[i];
-                if constexpr (SPLIT) *(uint4*)&Kls[buf][key * KLD + col] = rkl[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; i++) {
-            const int c = tid + i * 256;
-            if (VCH % 256 != 0 && c >= VCH) break;
-            const int row = c / (KT / VE), kc = (c % (KT / VE)) * VE;
-            if constexpr (F32) {
-                const float* v = (const float*)&rv[i];
-#pragma unroll
-                for (int e = 0; e < 4; e++) Vs[buf][row * VLD + kc + e] = v[e];
-            } else {
-                *(uint4*)&Vs[buf][row * VLD + kc] = rv[i];
-            }
-        }
-    };
-
-    // ---- running state (query c16 of this wave)
-    f32x4 o[ND];
-#pragma unroll
-    for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = p.scale_log2;
-
-    int n_vis = 0;                               // tiles scored by this wave (audit build)
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; t++) {
-        const int buf = t & 1;
-        const int k0 = t * KT;
-        if (t + 1 < ntiles) gload(k0 + KT);
-        // A wave whose queries all precede this tile has nothing to add.
-        if (k0 <= qw0 + BQW - 1) {
-            if constexpr (MASK_ALL) n_vis++;
-            const LT* ks = Ks[buf];
-            const LT* vs = Vs[buf];
-            f32x4 s[4];
-            // key held by (block kb, lane group g, element e):
-            //   F32:  kb*16 + 4g + e
-            //   F16:  (kb/2)*32 + 8g + 4*(kb%2) + e   (8 consecutive keys per group per 32-key chunk)
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-                s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int r = c16;
-                const int krow = F32 ? kb * 16 + r : (kb >> 1) * 32 + (r >> 2) * 8 + (kb & 1) * 4 + (r & 3);
-                if constexpr (F32) {
-#pragma unroll
-                    for (int kk = 0; kk < QK; kk++) s[kb] = mfma_16x16x4(ks[krow * KLD + kk * 4 + g], qf[kk], s[kb]);
-                } else if constexpr (DH >= 32) {
-#pragma unroll
-                    for (int kk = 0; kk < QK; kk++) {
-                        const f16x8 a = *(const f16x8*)&ks[krow * KLD + kk * 32 + g * 8];
-                        s[kb] = mfma_16x16x32(a, qh8[kk], s[kb]);
-                        if constexpr (SPLIT) {
-                            const f16x8 al = *(const f16x8*)&Kls[buf][krow * KLD + kk * 32 + g * 8];
-                            s[kb] = mfma_16x16x32(al, qh8[kk], s[kb]);
-                            s[kb] = mfma_16x16x32(a, ql8[kk], s[kb]);
-                        }
-                    }
-                } else {
-                    const f16x4 a = *(const f16x4*)&ks[krow * KLD + g * 4];
-                    s[kb] = mfma_16x16x16(a, qh4, s[kb]);
-                    if constexpr (SPLIT) {
-                        const f16x4 al = *(const f16x4*)&Kls[buf][krow * KLD + g * 4];
-                        s[kb] = mfma_16x16x16(al, qh4, s[kb]);
-                        s[kb] = mfma_16x16x16(a, ql4, s[kb]);
-                    }
-                }
-            }
-            // ---- scale, mask (boundary tiles only), online softmax
-            const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    float v = s[kb][e] * sl2;
-                    if (need_mask) {
-                        const int key = k0 + (F32 ? kb * 16 + 4 * g + e : (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e);
-                        if (key > myq || key >= len) v = -INFINITY;
-                    }
-                    s[kb][e] = v;
-                    mx = fmaxf(mx, v);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run - m_use);
-            m_run = m_new;
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float pv = exp2f(s[kb][e] - m_use);
-                    s[kb][e] = pv;
-                    ls += pv;
-                }
-            }
-            l_run = l_run * alpha + ls;
-#pragma unroll
-            for (int db = 0; db < ND; db++) o[db] *= alpha;
-            // ---- O^T += V^T P^T
-            if constexpr (F32) {
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-#pragma unroll
-                        for (int db = 0; db < ND; db++)
-                            o[db] = mfma_16x16x4(vs[(db * 16 + c16) * VLD + kb * 16 + 4 * g + e], s[kb][e], o[db]);
-            } else {
-#pragma unroll
-                for (int cc = 0; cc < 2; cc++) {
-                    f16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        pb[e] = (f16)s[2 * cc][e];
-                        pb[4 + e] = (f16)s[2 * cc + 1][e];
-                    }
-#pragma unroll
-                    for (int db = 0; db < ND; db++) {
-                        const f16x8 va = *(const f16x8*)&vs[(db * 16 + c16) * VLD + cc * 32 + g * 8];
-                        o[db] = mfma_16x16x32(va, pb, o[db]);
-                    }
-                }
-            }
-        }
-        if (t + 1 < ntiles) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- normalise and write O [B*L, d] at this head's columns
-    l_run += __shfl_xor(l_run, 16, WAVE);
-    l_run += __shfl_xor(l_run, 32, WAVE);
-    if constexpr (MASK_ALL) {
-        if (lane == 0) audit_add(p.audit, AUD_TILED_WAVE, n_vis);
-        if (tid == 0) audit_add(p.audit, AUD_TILED_WG, ntiles);
-    }
-    if (!qok) return;
-    const float inv = 1.0f / l_run;
-    OpT* out = (OpT*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
-#pragma unroll
-    for (int db = 0; db < ND; db++) {
-        if constexpr (F32) {
-            *(float4*)(out + db * 16 + 4 * g) = float4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
-        } else {
-            f16x4 v = {(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
-            *(f16x4*)(out + db * 16 + 4 * g) = v;
-        }
-    }
+    *(f16x4*)out = hv;
+    if (lo_plane) *(f16x4*)(out + lo_plane) = lv;
 }
 
-// ---------------------------------------------------------------- LDS-DMA ring
 template <int DH, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     constexpr int KT = ATT_KT, ST = 3;
@@ -505,9 +249,10 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     const float inv = 1.0f / l_run;
     f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
 #pragma unroll
-    for (int db = 0; db < ND; db++)
-        *(f16x4*)(out + db * 16 + 4 * g) =
-            f16x4{(f16)(o[db][0] * inv), (f16)(o[db][1] * inv), (f16)(o[db][2] * inv), (f16)(o[db][3] * inv)};
+    for (int db = 0; db < ND; db++) {
+        float v[4] = {o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+        store_o4(out + db * 16 + 4 * g, v, p.o_lo ? (size_t)p.B * L * p.d : 0);
+    }
 }
 
 // ---------------------------------------------------------------- head dim 16
@@ -734,32 +479,13 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     if (!qok) return;
     const float inv = 1.0f / l;
     f16* out = (f16*)p.O + ((size_t)b * L + myq) * p.d + (size_t)h * DH;
-    *(f16x4*)(out + 4 * g) = f16x4{(f16)(o[0] * inv), (f16)(o[1] * inv), (f16)(o[2] * inv), (f16)(o[3] * inv)};
-}
-
-template <class OpT, int DH>
-static hipError_t attn_dh(bool split, const AttnArgs& a, hipStream_t s) {
-    dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
-    if (split && sizeof(OpT) == 2)
-        hipLaunchKernelGGL((attn_kernel<OpT, DH, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((attn_kernel<OpT, DH, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-template <class OpT>
-static hipError_t attn_mode(int dh, bool split, const AttnArgs& a, hipStream_t s) {
-    switch (dh) {
-        case 16: return attn_dh<OpT, 16>(split, a, s);
-        case 32: return attn_dh<OpT, 32>(split, a, s);
-        case 64: return attn_dh<OpT, 64>(split, a, s);
-    }
-    return hipErrorInvalidValue;
+    float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    store_o4(out + 4 * g, v, p.o_lo ? (size_t)p.B * L * p.d : 0);
 }
 
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s) {
     if (a.B <= 0 || a.L <= 0) return hipSuccess;
-    if (m == MODE_F32) return attn_mode<float>(dh, false, a, s);
+    (void)m;  // every mode takes fp16 Q/K/V planes
     if (dh == 32 || dh == 64) {
         dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
         if (dh == 64 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, true>), grid, dim3(256), 0, s, a);
@@ -776,7 +502,7 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
             hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
         return hipGetLastError();
     }
-    return attn_mode<f16>(dh, split_qk, a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace tfl

@@ -6,24 +6,29 @@
 
 namespace tfl {
 
-// Arithmetic mode, fixed by the I/O dtype:
-//   F32:  every GEMM/attention operand fp32, fp32 MFMA.
-//   F16:  operands fp16 (activations rounded once to fp16), weights fp16.
-//   BF16: operands fp16; bf16 weights are widened to fp16 as they are loaded.
-// The residual stream, LayerNorm, Q and K are fp32 in every mode.
+// Arithmetic mode, fixed by the I/O dtype.  On the layer-wise (TILED) path
+// every GEMM and attention operand is fp16 with fp32 accumulation:
+//   F32:  operands as two fp16 planes, the rounded value (hi) and the
+//         rounding remainder times 2^11 (lo); each product is three MFMAs
+//         (hi*hi + (hi*lo + lo*hi) * 2^-11).  Weights are split into the two
+//         planes once per forward.
+//   F16:  operands fp16 (activations rounded once to fp16), weights as given.
+//   BF16: operands fp16; bf16 weights converted to fp16 once per forward.
+// The residual stream and LayerNorm are fp32 in every mode.  The fused
+// kernels (SEQ, PQ, row) read the weights in their I/O dtype themselves.
 enum Mode { MODE_F32 = 0, MODE_F16 = 1, MODE_BF16 = 2 };
 
 enum Epi { EPI_QKV = 0, EPI_GELU = 1, EPI_RES = 2 };
 
 struct GemmArgs {
-    const void* A;     // [M, K] operand dtype, row-major
-    const void* W;     // [N, K] weight dtype (nn.Linear layout)
-    const void* bias;  // [N] weight dtype
-    int M, N, K;
-    // EPI_QKV: N = 3d; writes Q, K [B, H, L, dh] and V^T [B, H, dh, Lp] operand dtype.
-    // F32 mode: Q, K fp32.  16-bit modes: Q and K as fp16 planes of M*d
-    // elements each: the rounded value (hi) at Q / K and, when split != 0,
-    // the rounding remainder (lo) one plane further.
+    const void* A;     // [M, K] fp16 (F32 mode: hi plane, lo plane M*K elements further)
+    const void* W;     // [N, K] fp16 (F32 mode: hi plane, lo plane N*K elements further)
+    const void* bias;  // [N] I/O dtype
+    int M, N, K;       // K % 32 == 0, N % 4 == 0
+    // EPI_QKV: N = 3d; writes Q, K [B, H, L, dh] and V^T [B, H, dh, Lp] fp16.
+    // Q and K as fp16 planes of M*d elements each: the rounded value (hi) at
+    // Q / K and, when split != 0, the rounding remainder (lo) one plane
+    // further.
     float* Q;
     float* Kd;
     void* Vt;
@@ -33,7 +38,7 @@ struct GemmArgs {
     // attention kernel takes keys pre-multiplied by log2(e)/sqrt(dh), so its
     // score products come out in the exp2 domain.
     float kscale;
-    // EPI_GELU: out [M, N] operand dtype
+    // EPI_GELU: out [M, N] fp16 (F32 mode: hi plane, lo plane M*N elements further)
     void* out;
     // EPI_RES: Z = acc + bias + R, [M, N] fp32
     const float* R;
@@ -41,12 +46,13 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
-    const void* Q;     // [B, H, L, dh]: fp32 (F32 mode) or fp16 hi plane (16-bit modes)
+    const void* Q;     // [B, H, L, dh] fp16 hi plane
     const void* K;     // [B, H, L, dh], same
-    const void* Ql;    // 16-bit modes, first layer: fp16 lo planes of Q and K
+    const void* Ql;    // fp16 lo planes of Q and K (read when the scores are split)
     const void* Kl;
-    const void* Vt;    // [B, H, dh, Lp] operand dtype; columns >= L hold zeros in 16-bit modes
-    void* O;           // [B*L, d] operand dtype, head h at columns h*dh
+    const void* Vt;    // [B, H, dh, Lp] fp16; columns >= L hold zeros
+    void* O;           // [B*L, d] fp16, head h at columns h*dh
+    int o_lo;          // 1: also the remainder times 2^11, B*L*d elements further (F32 mode)
     const int32_t* lens;
     int B, H, L, Lp, d;
     float scale_log2;  // log2(e) / sqrt(dh); the head-dim-16 kernel reads K already multiplied by it
@@ -122,14 +128,30 @@ hipError_t launch_row(Mode m, int d, int dh, const RowArgs& a, hipStream_t s);
 constexpr int ATT_KT = 64;   // keys per attention tile
 constexpr int ATT_BQ = 64;   // queries per attention workgroup
 
+// x (I/O dtype) -> fp32 residual Xr and fp16 operand A (F32 mode: hi plane
+// at A, lo plane n elements further).
 hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s);
 // Zeroes columns [L, Lp) of every V^T row (rows of Lp fp16).
 hipError_t launch_vt_pad(void* Vt, long rows, int L, int Lp, hipStream_t s);
 hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
-// Multi-stage LDS-DMA pipelined GEMM (16-bit operand modes, K % 64 == 0).
-bool gemm_pipe_ok(const GemmArgs& a);
-hipError_t launch_gemm_pipe(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
+// Weight staging of the layer-wise path (BF16 and F32 modes): each segment's
+// n source weights (I/O dtype) become n fp16 values at dst (F32 mode: hi at
+// dst, lo times 2^11 at dst + n).  n % 8 == 0.
+struct WconvSeg {
+    const void* src;
+    _Float16* dst;
+    long n;
+};
+constexpr int WCONV_MAX_SEGS = 32;
+struct WconvArgs {
+    WconvSeg seg[WCONV_MAX_SEGS];
+    int nseg;
+};
+hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s);
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
+// LayerNorm of fp32 rows Z: optionally to the fp32 residual Xo, the fp16
+// operand Ao (F32 mode: hi plane, lo plane T*d elements further) and the I/O
+// dtype output Y.
 hipError_t launch_ln(Mode m, const float* Z, const void* gamma, const void* beta, float eps,
                      int T, int d, float* Xo, void* Ao, void* Y, hipStream_t s);
 

@@ -7,8 +7,13 @@
 // "Challenges").  A row is spread over a group of lanes of one wave
 // (up to 64) that read it as coalesced float4 chunks; the reductions are
 // butterfly shuffles inside the group.  The row then leaves as fp32 (the
-// residual stream), as an operand-dtype copy for the next GEMM, and/or, in
+// residual stream), as an fp16 operand copy for the next GEMM (with fp32 I/O
+// two planes: the rounded value and the remainder times 2^11), and/or, in
 // the last layer, as the I/O dtype output.
+//
+// Also here: the staging kernels of the layer-wise path (input rows to the
+// fp32 residual and the operand planes; weights to fp16 planes; zero padding
+// of the V^T rows).
 #include "common.h"
 #include "kernels.h"
 
@@ -61,10 +66,22 @@ bool ln_shape(int d, int* lanes_per_row, int* chunks) {
     return true;
 }
 
-template <class OpT, class PT, int LPR, int NC>
+// fp16 rounding of four values and, for LO, the remainders times 2^11.
+__device__ __forceinline__ void st4_split(f16* p, size_t lo_plane, const float (&v)[4]) {
+    float h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        h[e] = (float)(f16)v[e];
+        l[e] = (v[e] - h[e]) * 2048.0f;
+    }
+    st4(p, h);
+    st4(p + lo_plane, l);
+}
+
+template <class PT, int LPR, int NC, bool LO>
 __global__ __launch_bounds__(256) void ln_kernel(const float* __restrict__ Z, const PT* __restrict__ gamma,
                                                  const PT* __restrict__ beta, float eps, int T, int d,
-                                                 float* __restrict__ Xo, OpT* __restrict__ Ao,
+                                                 float* __restrict__ Xo, f16* __restrict__ Ao,
                                                  PT* __restrict__ Y) {
     constexpr int RPB = 256 / LPR;  // rows per block
     const int tid = threadIdx.x;
@@ -98,20 +115,25 @@ __global__ __launch_bounds__(256) void ln_kernel(const float* __restrict__ Z, co
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = o[e] * rstd * ga[e] + be[e];
         if (Xo) *(float4*)(Xo + row * d + col) = float4{o[0], o[1], o[2], o[3]};
-        if (Ao) st4(Ao + row * d + col, o);
+        if (Ao) {
+            if constexpr (LO)
+                st4_split(Ao + row * d + col, (size_t)T * d, o);
+            else
+                st4(Ao + row * d + col, o);
+        }
         if (Y) st4(Y + row * d + col, o);
     }
 }
 
-template <class OpT, class PT, int LPR>
+template <class PT, int LPR, bool LO>
 static hipError_t ln_nc(int nc, const float* Z, const void* g, const void* b, float eps, int T, int d,
                         float* Xo, void* Ao, void* Y, hipStream_t s) {
     constexpr int RPB = 256 / LPR;
     dim3 grid((T + RPB - 1) / RPB);
 #define TFL_LN_CASE(NC)                                                                          \
     case NC:                                                                                     \
-        hipLaunchKernelGGL((ln_kernel<OpT, PT, LPR, NC>), grid, dim3(256), 0, s, Z, (const PT*)g, \
-                           (const PT*)b, eps, T, d, Xo, (OpT*)Ao, (PT*)Y);                        \
+        hipLaunchKernelGGL((ln_kernel<PT, LPR, NC, LO>), grid, dim3(256), 0, s, Z, (const PT*)g,  \
+                           (const PT*)b, eps, T, d, Xo, (f16*)Ao, (PT*)Y);                        \
         break;
     switch (nc) {
         TFL_LN_CASE(1) TFL_LN_CASE(2) TFL_LN_CASE(3) TFL_LN_CASE(4)
@@ -122,19 +144,19 @@ static hipError_t ln_nc(int nc, const float* Z, const void* g, const void* b, fl
     return hipGetLastError();
 }
 
-template <class OpT, class PT>
+template <class PT, bool LO>
 static hipError_t ln_mode(const float* Z, const void* g, const void* b, float eps, int T, int d, float* Xo,
                           void* Ao, void* Y, hipStream_t s) {
     int lpr, nc;
     if (!ln_shape(d, &lpr, &nc)) return hipErrorInvalidValue;
     switch (lpr) {
-        case 1: return ln_nc<OpT, PT, 1>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 2: return ln_nc<OpT, PT, 2>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 4: return ln_nc<OpT, PT, 4>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 8: return ln_nc<OpT, PT, 8>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 16: return ln_nc<OpT, PT, 16>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 32: return ln_nc<OpT, PT, 32>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case 64: return ln_nc<OpT, PT, 64>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 1: return ln_nc<PT, 1, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 2: return ln_nc<PT, 2, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 4: return ln_nc<PT, 4, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 8: return ln_nc<PT, 8, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 16: return ln_nc<PT, 16, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 32: return ln_nc<PT, 32, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case 64: return ln_nc<PT, 64, LO>(nc, Z, g, b, eps, T, d, Xo, Ao, Y, s);
     }
     return hipErrorInvalidValue;
 }
@@ -143,26 +165,28 @@ hipError_t launch_ln(Mode m, const float* Z, const void* g, const void* b, float
                      void* Ao, void* Y, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     switch (m) {
-        case MODE_F32: return ln_mode<float, float>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case MODE_F16: return ln_mode<f16, f16>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
-        case MODE_BF16: return ln_mode<f16, bf16>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case MODE_F32: return ln_mode<float, true>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case MODE_F16: return ln_mode<f16, false>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
+        case MODE_BF16: return ln_mode<bf16, false>(Z, g, b, eps, T, d, Xo, Ao, Y, s);
     }
     return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- input staging
-// x (I/O dtype) -> fp32 residual stream and operand-dtype copy.
-template <class OpT, class XT>
+// x (I/O dtype) -> fp32 residual stream and fp16 operand copy (fp32 I/O: hi
+// plane and the remainder times 2^11 n elements further).
+template <class XT>
 __global__ __launch_bounds__(256) void prep_kernel(const XT* __restrict__ x, float* __restrict__ Xr,
-                                                   OpT* __restrict__ A, long n) {
+                                                   f16* __restrict__ A, long n) {
     const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n) return;  // n is a multiple of 4 (d % 4 == 0)
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const float v = to_f32(x[i + e]);
-        Xr[i + e] = v;
-        A[i + e] = from_f32<OpT>(v);
-    }
+    float v[4];
+    ld4(x + i, v);
+    *(float4*)(Xr + i) = float4{v[0], v[1], v[2], v[3]};
+    if constexpr (sizeof(XT) == 4)
+        st4_split(A + i, (size_t)n, v);
+    else
+        st4(A + i, v);
 }
 
 hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStream_t s) {
@@ -170,14 +194,55 @@ hipError_t launch_prep(Mode m, const void* x, float* Xr, void* A, long n, hipStr
     dim3 grid((unsigned)((n / 4 + 255) / 256));
     switch (m) {
         case MODE_F32:
-            hipLaunchKernelGGL((prep_kernel<float, float>), grid, dim3(256), 0, s, (const float*)x, Xr, (float*)A, n);
+            hipLaunchKernelGGL((prep_kernel<float>), grid, dim3(256), 0, s, (const float*)x, Xr, (f16*)A, n);
             break;
         case MODE_F16:
-            hipLaunchKernelGGL((prep_kernel<f16, f16>), grid, dim3(256), 0, s, (const f16*)x, Xr, (f16*)A, n);
+            hipLaunchKernelGGL((prep_kernel<f16>), grid, dim3(256), 0, s, (const f16*)x, Xr, (f16*)A, n);
             break;
         case MODE_BF16:
-            hipLaunchKernelGGL((prep_kernel<f16, bf16>), grid, dim3(256), 0, s, (const bf16*)x, Xr, (f16*)A, n);
+            hipLaunchKernelGGL((prep_kernel<bf16>), grid, dim3(256), 0, s, (const bf16*)x, Xr, (f16*)A, n);
             break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- weight staging
+// Each segment's weights to fp16: bf16 values are exact in fp16 within its
+// range (8 significant bits); fp32 values leave as the rounded value and the
+// remainder times 2^11 (n elements further), the split operands of the
+// three-MFMA products.  Eight weights per thread per step.
+template <class WT>
+__global__ __launch_bounds__(256) void wconv_kernel(WconvArgs a) {
+    const WconvSeg sg = a.seg[blockIdx.y];
+    const long step = (long)gridDim.x * 256 * 8;
+    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < sg.n; i += step) {
+        float v[8];
+        ld4((const WT*)sg.src + i, *(float(*)[4])v);
+        ld4((const WT*)sg.src + i + 4, *(float(*)[4])(v + 4));
+        if constexpr (sizeof(WT) == 4) {
+            st4_split(sg.dst + i, (size_t)sg.n, *(const float(*)[4])v);
+            st4_split(sg.dst + i + 4, (size_t)sg.n, *(const float(*)[4])(v + 4));
+        } else {
+            st4(sg.dst + i, *(const float(*)[4])v);
+            st4(sg.dst + i + 4, *(const float(*)[4])(v + 4));
+        }
+    }
+}
+
+hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s) {
+    if (a.nseg <= 0) return hipSuccess;
+    if (a.nseg > WCONV_MAX_SEGS) return hipErrorInvalidValue;
+    long mx = 0;
+    for (int i = 0; i < a.nseg; i++) {
+        if (a.seg[i].n % 8 != 0) return hipErrorInvalidValue;
+        mx = a.seg[i].n > mx ? a.seg[i].n : mx;
+    }
+    const long blocks = (mx / 8 + 255) / 256;
+    dim3 grid((unsigned)(blocks < 1024 ? (blocks > 0 ? blocks : 1) : 1024), (unsigned)a.nseg);
+    switch (m) {
+        case MODE_F32: hipLaunchKernelGGL((wconv_kernel<float>), grid, dim3(256), 0, s, a); break;
+        case MODE_BF16: hipLaunchKernelGGL((wconv_kernel<bf16>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

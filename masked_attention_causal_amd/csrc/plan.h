@@ -19,8 +19,10 @@ struct Plan {
     long T;         // B * L token rows
     float eps;
     size_t op;      // operand element size (4 in F32 mode, 2 otherwise)
-    // workspace offsets in bytes (TILED)
-    size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G;
+    // workspace offsets in bytes (TILED); off_W: fp16 weight planes of the
+    // GEMMs (BF16 and F32 modes), n_wconv layers of them
+    size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G, off_W;
+    int n_wconv;
     // PQ path: key tiles per split, (tile, split) pairs per (sequence, head),
     // tasks, and workspace offsets
     int pq_ks, pq_ctot, pq_tasks;

@@ -151,6 +151,8 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     // per layer (out-projection, LayerNorms, FFN, next QKV), so Z, X1 and
     // the FFN activations never reach HBM
     q.row_fused = row_supported(mode, q.d, q.dh, q.f);
+    // GEMM operands are fp16 planes: one (16-bit I/O) or two (fp32 I/O: hi
+    // and the remainder times 2^11), q.op bytes per element in all
     size_t o = 0;
     q.off_Xr = o; o += up256(Td * 4);
     if (!q.row_fused) {
@@ -161,13 +163,23 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     q.off_K = o;  o += up256(Td * 4);
     q.off_A = o;  o += up256(Td * q.op);
     q.off_O = o;  o += up256(Td * q.op);
-    q.off_Vt = o; o += up256((size_t)q.B * q.d * q.Lp * q.op);
+    q.off_Vt = o; o += up256((size_t)q.B * q.d * q.Lp * 2);
     if (!q.row_fused) {
         q.off_G = o;  o += up256((size_t)T * q.f * q.op);
     }
+    // weights in their fp16 planes: every GEMM weight of every layer, or,
+    // with the fused row kernel (which reads the I/O dtype itself), the
+    // first layer's QKV weights only
+    q.n_wconv = 0;
+    q.off_W = o;
+    if (q.mode != MODE_F16) {
+        q.n_wconv = q.row_fused ? 1 : q.n_layers;
+        const size_t per_layer = q.row_fused ? (size_t)3 * q.d * q.d : (size_t)4 * q.d * q.d + (size_t)2 * q.d * q.f;
+        o += up256(per_layer * q.n_wconv * q.op);
+    }
     q.ws_bytes = o;
     std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s%s", ATT_BQ, ATT_KT,
-                  q.mode == MODE_F32 ? "f32" : "f16op", q.row_fused ? "/rowfused" : "");
+                  q.mode == MODE_F32 ? "f32io.f16x3" : "f16op", q.row_fused ? "/rowfused" : "");
     *p = q;
     return TFL_OK;
 }
@@ -189,6 +201,24 @@ struct Timed {
     }
 };
 
+// fp16 weight planes of layer l's four GEMM matrices in the workspace (BF16
+// and F32 modes), laid out as the plan sized them.
+struct WPlanes {
+    const void *qkv, *o, *w1, *w2;
+};
+static WPlanes weight_planes(const Plan& P, char* ws, int l) {
+    const size_t ew = P.op / 2;  // fp16 planes per weight
+    const size_t dd = (size_t)P.d * P.d, df = (size_t)P.d * P.f;
+    const size_t per_layer = P.row_fused ? 3 * dd : 4 * dd + 2 * df;
+    const f16* base = (const f16*)(ws + P.off_W) + (size_t)l * per_layer * ew;
+    WPlanes w;
+    w.qkv = base;
+    w.o = base + 3 * dd * ew;
+    w.w1 = base + 4 * dd * ew;
+    w.w2 = base + (4 * dd + df) * ew;
+    return w;
+}
+
 static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* x, const int32_t* lens, void* y,
                             char* ws, hipStream_t s, StageTimer* T) {
     float* Xr = (float*)(ws + P.off_Xr);
@@ -201,26 +231,50 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
     void* Vt = ws + P.off_Vt;
     void* G = ws + P.off_G;
     const int M = (int)P.T;
-    hipError_t e;
+    const bool f32 = P.mode == MODE_F32;
+    hipError_t e = hipSuccess;
     {
         Timed tm(T, TFL_STAGE_PREP, s);
-        e = tm.done(launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s));
-        if (e == hipSuccess && P.mode != MODE_F32) e = launch_vt_pad(Vt, (long)P.B * P.d, P.L, P.Lp, s);
+        // weights to fp16 planes, up to WCONV_MAX_SEGS matrices per launch
+        const size_t dd = (size_t)P.d * P.d, df = (size_t)P.d * P.f;
+        WconvArgs wa{};
+        for (int l = 0; l < P.n_wconv && e == hipSuccess; l++) {
+            const tfl_layer& w = layers[l];
+            const WPlanes wp = weight_planes(P, ws, l);
+            const void* src[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
+            const void* dst[4] = {wp.qkv, wp.o, wp.w1, wp.w2};
+            const size_t n[4] = {3 * dd, dd, df, df};
+            for (int k = 0; k < (P.row_fused ? 1 : 4); k++) {
+                wa.seg[wa.nseg++] = WconvSeg{src[k], (f16*)dst[k], (long)n[k]};
+                if (wa.nseg == WCONV_MAX_SEGS) {
+                    e = launch_wconv(P.mode, wa, s);
+                    wa.nseg = 0;
+                }
+            }
+        }
+        if (e == hipSuccess) e = launch_wconv(P.mode, wa, s);
+        if (e == hipSuccess) e = launch_prep(P.mode, x, Xr, A, (long)P.T * P.d, s);
+        if (e == hipSuccess) e = launch_vt_pad(Vt, (long)P.B * P.d, P.L, P.Lp, s);
+        e = tm.done(e);
     }
     if (e != hipSuccess) return e;
     for (int l = 0; l < P.n_layers; l++) {
         const tfl_layer& w = layers[l];
         const bool last = l == P.n_layers - 1;
+        const WPlanes wp =
+            l < P.n_wconv ? weight_planes(P, ws, l) : WPlanes{w.w_qkv, w.w_o, w.w_1, w.w_2};
+        // Scores of the first layer see the raw input (up to 1e3 in scale):
+        // fp32-accurate there; LayerNorm bounds every later layer's input.
+        // With fp32 I/O every layer's scores are split.
+        const bool split = f32 || l == 0;
         GemmArgs g{};
-        g.A = A; g.W = w.w_qkv; g.bias = w.b_qkv;
+        g.A = A; g.W = wp.qkv; g.bias = w.b_qkv;
         g.M = M; g.N = 3 * P.d; g.K = P.d;
         g.Q = Q; g.Kd = K; g.Vt = Vt;
         g.L = P.L; g.Lp = P.Lp; g.H = P.H; g.dh = P.dh; g.d = P.d;
-        // Scores of the first layer see the raw input (up to 1e3 in scale):
-        // fp32-accurate there; LayerNorm bounds every later layer's input.
-        g.split = l == 0;
-        // the head-dim-16 attention kernel (16-bit modes) reads K pre-scaled
-        if (P.mode != MODE_F32 && P.dh == 16) g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+        g.split = split;
+        // the head-dim-16 attention kernel reads K pre-scaled
+        if (P.dh == 16) g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
         // with the fused row kernel, layers after the first get their Q, K
         // and V^T from the previous layer's row kernel
         if (!P.row_fused || l == 0) {
@@ -230,7 +284,8 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
 
         AttnArgs a{};
         a.Q = Q; a.K = K; a.Vt = Vt; a.O = O; a.lens = lens;
-        // 16-bit modes: fp16 lo planes follow the hi planes in the same buffers
+        a.o_lo = f32;
+        // fp16 lo planes follow the hi planes in the same buffers
         a.Ql = (const f16*)Q + (size_t)P.T * P.d;
         a.Kl = (const f16*)K + (size_t)P.T * P.d;
         a.B = P.B; a.H = P.H; a.L = P.L; a.Lp = P.Lp; a.d = P.d;
@@ -238,7 +293,7 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         a.audit = audit_counters;
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
-            if ((e = tm.done(launch_attn(P.mode, P.dh, l == 0, a, s))) != hipSuccess) return e;
+            if ((e = tm.done(launch_attn(P.mode, P.dh, split, a, s))) != hipSuccess) return e;
         }
         if (P.row_fused) {
             // out-projection .. LayerNorm 2 and the next layer's QKV in one launch
@@ -261,7 +316,7 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         }
 
         GemmArgs r{};
-        r.A = O; r.W = w.w_o; r.bias = w.b_o; r.M = M; r.N = P.d; r.K = P.d; r.R = Xr; r.Z = Z;
+        r.A = O; r.W = wp.o; r.bias = w.b_o; r.M = M; r.N = P.d; r.K = P.d; r.R = Xr; r.Z = Z;
         {
             Timed tm(T, TFL_STAGE_OUT, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_RES, r, s))) != hipSuccess) return e;
@@ -273,13 +328,13 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         }
 
         GemmArgs u{};
-        u.A = A; u.W = w.w_1; u.bias = w.b_1; u.M = M; u.N = P.f; u.K = P.d; u.out = G;
+        u.A = A; u.W = wp.w1; u.bias = w.b_1; u.M = M; u.N = P.f; u.K = P.d; u.out = G;
         {
             Timed tm(T, TFL_STAGE_FFN1, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_GELU, u, s))) != hipSuccess) return e;
         }
         GemmArgs dn{};
-        dn.A = G; dn.W = w.w_2; dn.bias = w.b_2; dn.M = M; dn.N = P.d; dn.K = P.f; dn.R = X1; dn.Z = Z;
+        dn.A = G; dn.W = wp.w2; dn.bias = w.b_2; dn.M = M; dn.N = P.d; dn.K = P.f; dn.R = X1; dn.Z = Z;
         {
             Timed tm(T, TFL_STAGE_FFN2, s);
             if ((e = tm.done(launch_gemm(P.mode, EPI_RES, dn, s))) != hipSuccess) return e;

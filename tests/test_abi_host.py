@@ -128,16 +128,23 @@ def test_workspace_covers_the_tiled_buffers():
     Lp = (w.L + 127) // 128 * 128          # V^T rows padded to whole 128-key tiles
     need = 3 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2
     assert need <= ws <= need + 6 * 256
-    # d_model 1024: separate kernels, all buffers
+    # d_model 1024, bf16 I/O: separate kernels, all buffers, plus every
+    # layer's four GEMM weights converted to one fp16 plane
     w = synth.WORKLOADS["gemm_d1024_b8_l512"]
     plan, _, ws = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype)
     assert not plan.endswith("/rowfused"), plan
     T = w.B * w.L
     Lp = (w.L + 127) // 128 * 128
-    need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2
-    assert need <= ws <= need + 9 * 256
-    # fp32 I/O stays on the separate kernels
-    assert not tfl.plan_for(2, 64, 4, 256, 1, 4096, "f32", force_path="tiled")[0].endswith("/rowfused")
+    wts = w.n_layers * (4 * w.d * w.d + 2 * w.d * w.f)
+    need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2 + wts * 2
+    assert need <= ws <= need + 10 * 256
+    # fp32 I/O stays on the separate kernels, with two fp16 planes (hi, lo)
+    # for every operand and weight
+    L, d, f, n_layers = 4096, 64, 256, 2
+    plan, _, ws = tfl.plan_for(n_layers, d, 4, f, 1, L, "f32", force_path="tiled")
+    assert not plan.endswith("/rowfused") and "f16x3" in plan, plan
+    need = 5 * L * d * 4 + 2 * L * d * 4 + d * L * 2 + L * f * 4 + n_layers * (4 * d * d + 2 * d * f) * 4
+    assert need <= ws <= need + 10 * 256
 
 
 @pytest.mark.parametrize("cfg,status", [

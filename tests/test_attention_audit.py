@@ -7,8 +7,8 @@ include/tfl_audit.h).
    the padding boundary) is bit-identical to masking every tile: the audit
    build masks every tile it visits, and its outputs must equal the product
    build's exactly, on every attention kernel (layer-wise kernels at head
-   dims 16, 32 and 64 in fp16/bf16 operands and fp32, the fused SEQ kernel,
-   the PQ split-K tasks).
+   dims 16, 32 and 64 with single and split scores, the fused SEQ kernel, the
+   PQ split-K tasks).
 2. A causal loop visits only the key tiles that hold an allowed key.  The
    allowed keys of a block of queries q0 .. q_end-1 of sequence b are
    0 .. min(q_end, len_b) - 1, so a block visits ceil(min(q_end, len_b) / BK)
@@ -52,7 +52,7 @@ def blocks_sum(lens, L, block, waves_of, kt):
 def expected(w, path, lens):
     per = w.H * w.n_layers
     if path == "tiled":
-        block, kt = (128, 128) if (w.dtype != "f32" and w.dh == 16) else (64, 64)
+        block, kt = (128, 128) if w.dh == 16 else (64, 64)
         wg, wave = blocks_sum(lens, w.L, block, block // 16, kt)
         return {"tiled_wg": wg * per, "tiled_wave": wave * per}
     if path == "seq":
@@ -99,6 +99,7 @@ CASES = [
     (W("a_tiled_bf16_dh16", 1, 64, 4, 128, 2, 300, "bf16", 1, 300, 1.0), "tiled", [1, 300]),
     (W("a_tiled_f32_dh64", 2, 128, 2, 256, 2, 150, "f32", 1, 150, 1.0), "tiled", [150, 64]),
     (W("a_tiled_f32_dh16", 1, 64, 4, 128, 2, 130, "f32", 1, 130, 1.0), "tiled", [129, 130]),
+    (W("a_tiled_f32_dh32", 2, 128, 4, 256, 2, 200, "f32", 1, 200, 1.0), "tiled", [200, 71]),
     (W("a_seq_f16_d128_dh64", 2, 128, 2, 256, 5, 64, "f16", 1, 64, 1.0), "seq", [64, 1, 33, 31, 17]),
     (W("a_seq_bf16_d256_dh32", 2, 256, 8, 256, 3, 50, "bf16", 1, 50, 1.0), "seq", [50, 32, 9]),
     (W("a_pq_f32_d128_dh64", 2, 128, 2, 512, 2, 1000, "f32", 1, 1000, 1.0), "pq", [1000, 555]),
@@ -137,7 +138,7 @@ def test_full_length_visits_triangle(dh, dtype):
     import masked_attention_causal_amd as tfl
     H = 64 // dh if dh < 64 else 2
     d = dh * H
-    block = 128 if (dh == 16 and dtype != "f32") else 64
+    block = 128 if dh == 16 else 64
     M = 6
     L = M * block
     w = W(f"a_full_dh{dh}_{dtype}", 1, d, H, 128, 2, L, dtype, L, L, 1.0)

@@ -221,6 +221,31 @@ def test_pipelined_gemm_shapes(w):
         assert_gate(gpu_forward(inp, force_path="tiled"), oracle_forward(inp), f"{w.name} seed {seed}")
 
 
+# fp32 I/O: every product as three fp16 MFMAs on 128 x 128 tiles (FFN up:
+# 4096 tokens x 2048 features = 512 tiles), and on 64 x 128 tiles elsewhere;
+# d = 96 and f = 160 give 32-column last stages.
+SPLIT3 = [
+    W("x_f32_d512_f2048", 1, 512, 8, 2048, 8, 512, "f32", 256, 512, 1.0),
+    W("x_f32_d96_f160", 2, 96, 3, 160, 3, 90, "f32", 1, 90, 1.0),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT3, ids=lambda w: w.name)
+def test_fp32_split_gemm_tiles(w):
+    import masked_attention_causal_amd as tfl
+    plan, path, _ = tfl.plan_for(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, force_path="tiled")
+    assert "f16x3" in plan, plan
+    for seed, scale, affine in ((0, 1.0, False), (1, 1e3, True), (2, 1e-3, False)):
+        inp = _case(w, seed, scale, affine=affine)
+        inp.lens[0] = w.L
+        say(f"[split3] {w.name} seed={seed} scale={scale} affine={affine} lens={inp.lens.tolist()}")
+        # at 1e3 with random affine parameters the first-layer scores reach
+        # ~5e5, where rows whose two largest scores are tied within the fp32
+        # score rounding may fail (the near-tie rule)
+        assert_gate_near_ties(gpu_forward(inp, force_path="tiled"), oracle_forward(inp), inp,
+                              f"{w.name} seed {seed} scale {scale}")
+
+
 # ---------------------------------------------------------------- edge cases
 
 
