@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     // wave-uniform wave index: the tile skip and mask tests are scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
-    const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // heaviest query tiles first
-    const int h = blockIdx.y, b = blockIdx.z;
+    // (sequence, head) fastest, heaviest query tiles first (attn_grid)
+    const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
+    const int b = (int)blockIdx.x / p.H, h = (int)blockIdx.x - b * p.H;
     const int L = p.L, Lp = p.Lp;
     int len = p.lens[b];
     len = len < 1 ? 1 : (len > L ? L : len);
@@ -285,8 +286,9 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     // below are scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
-    const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    // (sequence, head) fastest, heaviest query tiles first (attn_grid)
+    const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
+    const int b = (int)blockIdx.x / p.H, h = (int)blockIdx.x - b * p.H;
     const int L = p.L, Lp = p.Lp;
     int len = p.lens[b];
     len = len < 1 ? 1 : (len > L ? L : len);
@@ -483,11 +485,20 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     store_o4(out + 4 * g, v, p.o_lo ? (size_t)p.B * L * p.d : 0);
 }
 
+// Launch grid: x = (sequence, head), y = query tile.  Workgroups are handed
+// to the eight XCDs round-robin in linear order (x fastest), so with
+// (sequence, head) fastest every query tile of one (sequence, head) lands on
+// the same XCD whenever B*H is a multiple of 8 or divides 8, and its K/V
+// tiles are fetched into that XCD's L2 once instead of once per XCD; the
+// kernels take query tiles from the last (the most keys) to the first.
+static dim3 attn_grid(const AttnArgs& a, int bq) { return dim3((unsigned)(a.B * a.H), (unsigned)((a.L + bq - 1) / bq)); }
+
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s) {
     if (a.B <= 0 || a.L <= 0) return hipSuccess;
+    if ((a.L + ATT_BQ - 1) / ATT_BQ > 65535) return hipErrorInvalidValue;  // query tiles: grid y
     (void)m;  // every mode takes fp16 Q/K/V planes
     if (dh == 32 || dh == 64) {
-        dim3 grid((a.L + ATT_BQ - 1) / ATT_BQ, a.H, a.B);
+        const dim3 grid = attn_grid(a, ATT_BQ);
         if (dh == 64 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, true>), grid, dim3(256), 0, s, a);
         if (dh == 64 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, false>), grid, dim3(256), 0, s, a);
         if (dh == 32 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, true>), grid, dim3(256), 0, s, a);
@@ -495,7 +506,7 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
         return hipGetLastError();
     }
     if (dh == 16) {   // the plan pads V^T rows to whole 128-key tiles
-        dim3 grid((a.L + ATT16_BQ - 1) / ATT16_BQ, a.H, a.B);
+        const dim3 grid = attn_grid(a, ATT16_BQ);
         if (split_qk)
             hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
         else
