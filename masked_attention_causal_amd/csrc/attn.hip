@@ -48,6 +48,31 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// Whether the scores of this workgroup's (sequence, head) need the hi/lo
+// split.  A single fp16 pass rounds each of q and k by at most u = 2^-11
+// relative, so a score q.k (in exp2 units: times c) moves by at most
+// (2u + u^2) |q| |k| c (Cauchy-Schwarz over the head dimension; the fp32
+// accumulation of exact fp16 products adds far less).  The single pass is
+// taken when that bound, formed from the maxima of |q_i| and |k_j| over the
+// (sequence, head), is at most SPLIT_EXP_ERR: a relative error of at most
+// 0.27% in any softmax weight.  Every wave forms the same answer.
+constexpr float SPLIT_EXP_ERR = 0.00390625f;  // 2^-8
+__device__ __forceinline__ bool split_needed(const AttnArgs& p, float c) {
+    const float2* st = p.qk_stats + (size_t)blockIdx.x * p.stats_nch;
+    float mq = 0.f, mk = 0.f;
+    for (int i = (int)(threadIdx.x & 63); i < p.stats_nch; i += 64) {
+        mq = fmaxf(mq, st[i].x);
+        mk = fmaxf(mk, st[i].y);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, o, WAVE));
+        mk = fmaxf(mk, __shfl_xor(mk, o, WAVE));
+    }
+    const float bound = (0.0009765625f + 2.384185791015625e-07f) * mq * mk * c;  // (2u + u^2) |q| |k| c
+    return !(bound <= SPLIT_EXP_ERR);  // NaN or inf: split
+}
+
 // ---------------------------------------------------------------- LDS-DMA ring
 // Four output values of one query as fp16; with lo_plane != 0 the rounding
 // remainders times 2^11 go lo_plane elements further (fp32 I/O).
@@ -62,8 +87,13 @@ __device__ __forceinline__ void store_o4(f16* out, const float (&v)[4], size_t l
     if (lo_plane) *(f16x4*)(out + lo_plane) = lv;
 }
 
+// LDS bytes of the head-dim-32/64 ring: three stages of K (hi, and lo when
+// SPLIT) and V^T, 64 keys each.
 template <int DH, bool SPLIT>
-__global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
+constexpr int ring_lds_bytes() { return 3 * (ATT_KT * DH * 2 * (SPLIT ? 2 : 1) + DH * ATT_KT * 2); }
+
+template <int DH, bool SPLIT>
+__device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
     constexpr int KT = ATT_KT, ST = 3;
     constexpr int KROW = DH * 2, KCH = KROW / 16;    // bytes and 16-byte chunks per K row
     constexpr int KB = KT * KROW;                    // one K plane tile
@@ -74,7 +104,7 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     constexpr int ND = DH / 16, QK = DH / 32;
     static_assert(NKD >= 1 && NVD >= 1 && NKD * 256 == KT * KCH && NVD * 256 == DH * 8, "head dim 32 or 64");
     static_assert(4 * 16 == ATT_BQ, "planner and kernel disagree on the query tile");
-    __shared__ __attribute__((aligned(16))) char lds[ST * SB];
+    static_assert(ST * SB == ring_lds_bytes<DH, SPLIT>(), "LDS accounting");
 
     // wave-uniform wave index: the tile skip and mask tests are scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,6 +286,27 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     }
 }
 
+template <int DH, bool SPLIT>
+__global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, SPLIT>()];
+    ring_body<DH, SPLIT>(p, lds);
+}
+
+// First-layer attention with the precision chosen per (sequence, head) from
+// the row-norm maxima of its Q and K (split_needed).
+template <int DH>
+__global__ __launch_bounds__(256) void attn_ring_adaptive_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, true>()];
+    const bool split = split_needed(p, p.scale_log2);
+    if constexpr (MASK_ALL) {
+        if (threadIdx.x == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+    }
+    if (split)
+        ring_body<DH, true>(p, lds);
+    else
+        ring_body<DH, false>(p, lds);
+}
+
 // ---------------------------------------------------------------- head dim 16
 // With 16-dim heads the products are a small part of the work and the
 // softmax arithmetic dominates ("KernelForge", "Challenges": the 100k-token
@@ -271,7 +322,10 @@ __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
 constexpr int ATT16_WAVES = 8, ATT16_BQ = 16 * ATT16_WAVES;
 
 template <bool SPLIT>
-__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs p) {
+constexpr int ring16_lds_bytes() { return 3 * (128 * 16 * 2 * (SPLIT ? 2 : 1) + 16 * 128 * 2); }
+
+template <bool SPLIT>
+__device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
     constexpr int DH = 16, KT = 128, ST = 3;
     constexpr int KROW = DH * 2;                     // 32-byte K rows: two 16-byte chunks
     constexpr int KB = KT * KROW;                    // 4 KB per K plane tile
@@ -280,7 +334,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     constexpr int SB = KB * (SPLIT ? 2 : 1) + VB;
     constexpr int NDMA = (SPLIT ? 2 : 1) + 1;        // one K chunk per plane and one V^T chunk per thread
     static_assert(KT * 2 == 256 && DH * 16 == 256, "one DMA chunk per thread per plane");
-    __shared__ __attribute__((aligned(16))) char lds[ST * SB];
+    static_assert(ST * SB == ring16_lds_bytes<SPLIT>(), "LDS accounting");
 
     // the wave index is made wave-uniform, so the tile skip and mask tests
     // below are scalar branches
@@ -485,6 +539,87 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
     store_o4(out + 4 * g, v, p.o_lo ? (size_t)p.B * L * p.d : 0);
 }
 
+template <bool SPLIT>
+__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(16))) char lds[ring16_lds_bytes<SPLIT>()];
+    ring16_body<SPLIT>(p, lds);
+}
+
+// Keys are stored multiplied by log2(e)/sqrt(dh), so their norms are already
+// in exp2 units.
+__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_adaptive_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(16))) char lds[ring16_lds_bytes<true>()];
+    const bool split = split_needed(p, 1.0f);
+    if constexpr (MASK_ALL) {
+        if (threadIdx.x == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+    }
+    if (split)
+        ring16_body<true>(p, lds);
+    else
+        ring16_body<false>(p, lds);
+}
+
+// ---------------------------------------------------------------- Q/K statistics
+// Maxima of the row norms |q_i| and |k_j| of one (sequence, head) over a
+// chunk of QKS_ROWS rows of the hi planes, one workgroup per (sequence
+// head, chunk): out[bh * nch + chunk] = (max |q_i|, max |k_j|).
+constexpr int QKS_ROWS = 2048;
+
+template <int DH>
+__global__ __launch_bounds__(256) void qk_stats_kernel(const f16* __restrict__ Q, const f16* __restrict__ K, int L,
+                                                       float2* __restrict__ out, int nch) {
+    const int bh = blockIdx.x, ch = blockIdx.y;
+    const size_t base = (size_t)bh * L * DH;
+    const int r1 = min(L, (ch + 1) * QKS_ROWS);
+    float mq = 0.f, mk = 0.f;
+    for (int r = ch * QKS_ROWS + (int)threadIdx.x; r < r1; r += 256) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int c = 0; c < DH / 8; c++) {
+            const f16x8 a = *(const f16x8*)(Q + base + (size_t)r * DH + 8 * c);
+            const f16x8 k = *(const f16x8*)(K + base + (size_t)r * DH + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                sq = fmaf((float)a[e], (float)a[e], sq);
+                sk = fmaf((float)k[e], (float)k[e], sk);
+            }
+        }
+        mq = fmaxf(mq, sq);
+        mk = fmaxf(mk, sk);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, o, WAVE));
+        mk = fmaxf(mk, __shfl_xor(mk, o, WAVE));
+    }
+    __shared__ float2 part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = float2{mq, mk};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; w++) {
+            mq = fmaxf(mq, part[w].x);
+            mk = fmaxf(mk, part[w].y);
+        }
+        // sqrt rounds to nearest; one ulp up keeps the result an upper bound
+        out[(size_t)bh * nch + ch] = float2{__uint_as_float(__float_as_uint(sqrtf(mq)) + 1u),
+                                            __uint_as_float(__float_as_uint(sqrtf(mk)) + 1u)};
+    }
+}
+
+int qk_stats_chunks(int L) { return (L + QKS_ROWS - 1) / QKS_ROWS; }
+
+hipError_t launch_qk_stats(int dh, const void* Q, const void* K, int BH, int L, float2* out, hipStream_t s) {
+    if (BH <= 0 || L <= 0) return hipSuccess;
+    const dim3 grid((unsigned)BH, (unsigned)qk_stats_chunks(L));
+    switch (dh) {
+        case 16: hipLaunchKernelGGL(qk_stats_kernel<16>, grid, dim3(256), 0, s, (const f16*)Q, (const f16*)K, L, out, (int)grid.y); break;
+        case 32: hipLaunchKernelGGL(qk_stats_kernel<32>, grid, dim3(256), 0, s, (const f16*)Q, (const f16*)K, L, out, (int)grid.y); break;
+        case 64: hipLaunchKernelGGL(qk_stats_kernel<64>, grid, dim3(256), 0, s, (const f16*)Q, (const f16*)K, L, out, (int)grid.y); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // Launch grid: x = (sequence, head), y = query tile.  Workgroups are handed
 // to the eight XCDs round-robin in linear order (x fastest), so with
 // (sequence, head) fastest every query tile of one (sequence, head) lands on
@@ -499,6 +634,11 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
     (void)m;  // every mode takes fp16 Q/K/V planes
     if (dh == 32 || dh == 64) {
         const dim3 grid = attn_grid(a, ATT_BQ);
+        if (split_qk && a.qk_stats) {
+            if (dh == 64) hipLaunchKernelGGL(attn_ring_adaptive_kernel<64>, grid, dim3(256), 0, s, a);
+            if (dh == 32) hipLaunchKernelGGL(attn_ring_adaptive_kernel<32>, grid, dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
         if (dh == 64 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, true>), grid, dim3(256), 0, s, a);
         if (dh == 64 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, false>), grid, dim3(256), 0, s, a);
         if (dh == 32 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, true>), grid, dim3(256), 0, s, a);
@@ -507,7 +647,9 @@ hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStre
     }
     if (dh == 16) {   // the plan pads V^T rows to whole 128-key tiles
         const dim3 grid = attn_grid(a, ATT16_BQ);
-        if (split_qk)
+        if (split_qk && a.qk_stats)
+            hipLaunchKernelGGL(attn_ring16_adaptive_kernel, grid, dim3(64 * ATT16_WAVES), 0, s, a);
+        else if (split_qk)
             hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
         else
             hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(64 * ATT16_WAVES), 0, s, a);

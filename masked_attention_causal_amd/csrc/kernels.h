@@ -53,6 +53,11 @@ struct AttnArgs {
     const void* Vt;    // [B, H, dh, Lp] fp16; columns >= L hold zeros
     void* O;           // [B*L, d] fp16, head h at columns h*dh
     int o_lo;          // 1: also the remainder times 2^11, B*L*d elements further (F32 mode)
+    // First layer with 16-bit I/O: per (sequence, head) row-norm maxima of Q
+    // and K written by qk_stats (stats_nch chunks each); when given, each
+    // workgroup takes the split scores only where their bound requires it.
+    const float2* qk_stats;
+    int stats_nch;
     const int32_t* lens;
     int B, H, L, Lp, d;
     float scale_log2;  // log2(e) / sqrt(dh); the head-dim-16 kernel reads K already multiplied by it
@@ -149,6 +154,10 @@ struct WconvArgs {
 };
 hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s);
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
+// Row-norm maxima of the Q and K hi planes ([BH, L, dh] fp16) per (sequence,
+// head) and chunk of rows: out [BH][qk_stats_chunks(L)] (max |q|, max |k|).
+int qk_stats_chunks(int L);
+hipError_t launch_qk_stats(int dh, const void* Q, const void* K, int BH, int L, float2* out, hipStream_t s);
 // LayerNorm of fp32 rows Z: optionally to the fp32 residual Xo, the fp16
 // operand Ao (F32 mode: hi plane, lo plane T*d elements further) and the I/O
 // dtype output Y.

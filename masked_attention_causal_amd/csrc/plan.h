@@ -21,7 +21,7 @@ struct Plan {
     size_t op;      // operand element size (4 in F32 mode, 2 otherwise)
     // workspace offsets in bytes (TILED); off_W: fp16 weight planes of the
     // GEMMs (BF16 and F32 modes), n_wconv layers of them
-    size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G, off_W;
+    size_t off_Xr, off_X1, off_Z, off_A, off_Q, off_K, off_Vt, off_O, off_G, off_W, off_S;
     int n_wconv;
     // PQ path: key tiles per split, (tile, split) pairs per (sequence, head),
     // tasks, and workspace offsets

@@ -177,6 +177,9 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         const size_t per_layer = q.row_fused ? (size_t)3 * q.d * q.d : (size_t)4 * q.d * q.d + (size_t)2 * q.d * q.f;
         o += up256(per_layer * q.n_wconv * q.op);
     }
+    // first-layer Q/K row-norm maxima (16-bit I/O: adaptive score precision)
+    q.off_S = o;
+    if (q.mode != MODE_F32) o += up256((size_t)q.B * q.H * qk_stats_chunks(q.L) * sizeof(float2));
     q.ws_bytes = o;
     std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s%s", ATT_BQ, ATT_KT,
                   q.mode == MODE_F32 ? "f32io.f16x3" : "f16op", q.row_fused ? "/rowfused" : "");
@@ -293,7 +296,16 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         a.audit = audit_counters;
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
-            if ((e = tm.done(launch_attn(P.mode, P.dh, split, a, s))) != hipSuccess) return e;
+            // 16-bit I/O, first layer: the split scores only where the Q/K
+            // magnitudes of a (sequence, head) need them
+            if (split && !f32) {
+                float2* st = (float2*)(ws + P.off_S);
+                a.qk_stats = st;
+                a.stats_nch = qk_stats_chunks(P.L);
+                e = launch_qk_stats(P.dh, Q, K, P.B * P.H, P.L, st, s);
+            }
+            if (e == hipSuccess) e = launch_attn(P.mode, P.dh, split, a, s);
+            if ((e = tm.done(e)) != hipSuccess) return e;
         }
         if (P.row_fused) {
             // out-projection .. LayerNorm 2 and the next layer's QKV in one launch

@@ -29,7 +29,7 @@ from tests.gate import say
 pytestmark = pytest.mark.gpu
 
 W = synth.Workload
-SLOTS = {"tiled_wg": 0, "tiled_wave": 1, "seq_wave": 2, "pq_wg": 3, "pq_wave": 4}
+SLOTS = {"tiled_wg": 0, "tiled_wave": 1, "seq_wave": 2, "pq_wg": 3, "pq_wave": 4, "split_wg": 5}
 
 
 def cdiv(a, b):
@@ -149,3 +149,29 @@ def test_full_length_visits_triangle(dh, dtype):
     run(inp, "tiled", tfl.AUDIT_LIB_PATH, counters)
     wg = int(counters.cpu().numpy()[SLOTS["tiled_wg"]])
     assert wg == w.B * w.H * w.n_layers * M * (M + 1) // 2, wg
+
+
+@pytest.mark.parametrize("dh", [16, 64])
+def test_first_layer_split_follows_magnitude(dh):
+    """With 16-bit I/O the first layer's scores take the hi/lo split only
+    where the bound on a single fp16 pass's score error, formed from the
+    largest |q_i| and |k_j| of a (sequence, head), exceeds 2^-8 in exp2
+    units.  Inputs of scale 1 (|q|, |k| ~ 1) stay on the single pass; at scale
+    1e3 every first-layer workgroup takes the split, and the output still
+    meets the gate against the oracle."""
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    from tests.gate import assert_gate, oracle_forward
+    H = 4 if dh == 16 else 2
+    w = W(f"a_adapt_dh{dh}", 2, dh * H, H, 256, 2, 300, "f16", 1, 300, 1.0)
+    bq = 128 if dh == 16 else 64
+    layer0_wgs = w.B * w.H * cdiv(w.L, bq)
+    for scale, want in ((1.0, 0), (1e3, layer0_wgs)):
+        inp = synth.make_inputs(w, 7, scale=scale)
+        counters = torch.zeros(8, dtype=torch.int64, device="cuda")
+        say(f"[audit adapt] {w.name} scale={scale}")
+        y = run(inp, "tiled", tfl.AUDIT_LIB_PATH, counters)
+        got = int(counters.cpu().numpy()[SLOTS["split_wg"]])
+        assert got == want, (scale, got, want)
+        assert_gate(y, oracle_forward(inp), f"{w.name} scale {scale}")
