@@ -87,6 +87,20 @@ __device__ __forceinline__ void store_o4(f16* out, const float (&v)[4], size_t l
     if (lo_plane) *(f16x4*)(out + lo_plane) = lv;
 }
 
+// Slot swizzle of K row r in the head-dim-32/64 ring (chunk c of the row in
+// slot c ^ ksw(r)).  A score block's 16 lanes read key rows
+// {0..3, 8..11, 16..19, 24..27} (+4, +32), and LDS serves a 16-byte read
+// eight lanes at a time, so the eight rows {0..3, 8..11} (or {16..19,
+// 24..27}) of one chunk must fall on eight distinct 16-byte bank groups:
+// (r mod 2, slot) distinct for 128-byte rows, (r mod 4, slot) for 64-byte
+// rows.  XOR-ing with r mod 8 (as for consecutive rows) put rows r and r + 8
+// on the same banks.
+template <int DH>
+__device__ __forceinline__ int ksw(int r) {
+    if constexpr (DH == 64) return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);
+    else return (r >> 3) & 3;
+}
+
 // LDS bytes of the head-dim-32/64 ring: three stages of K (hi, and lo when
 // SPLIT) and V^T, 64 keys each.
 template <int DH, bool SPLIT>
@@ -144,14 +158,15 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
         if constexpr (SPLIT) asm volatile("" : "+v"(ql[kk]));
     }
 
-    // Swizzle: chunk c of row r of a tile lives in slot c ^ (r % chunks-per-row).
-    // DMA lane writes slot q of the tile; it fetches the chunk that belongs there.
+    // Swizzle: chunk c of K row r lives in slot c ^ ksw(r), of V^T row r in
+    // slot c ^ (r % 8).  DMA lane writes slot q of the tile; it fetches the
+    // chunk that belongs there.
     int krow[NKD], kchk[NKD], vrow[NVD], vchk[NVD];
 #pragma unroll
     for (int i = 0; i < NKD; i++) {
         const int q = i * 256 + tid;
         krow[i] = q / KCH;
-        kchk[i] = (q % KCH) ^ (krow[i] % KCH);
+        kchk[i] = (q % KCH) ^ ksw<DH>(krow[i]);
     }
 #pragma unroll
     for (int i = 0; i < NVD; i++) {
@@ -206,7 +221,7 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
             const int r = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
 #pragma unroll
             for (int kk = 0; kk < QK; kk++) {
-                const int slot = ((kk * 4 + g) ^ (r % KCH)) * 16;
+                const int slot = ((kk * 4 + g) ^ ksw<DH>(r)) * 16;
                 const f16x8 a = *(const f16x8*)(ks + r * KROW + slot);
                 sc[kb] = mfma_16x16x32(a, qh[kk], sc[kb]);
                 if constexpr (SPLIT) {
