@@ -127,7 +127,9 @@ tfl_status tfl_workspace_bytes(const tfl_handle *h, size_t *bytes);
  *              kernels clamp values outside that range (results are those
  *              of the clamped lengths); with the environment variable
  *              TFL_CHECK=1 they are copied to the host (synchronising the
- *              stream) and out-of-range values return TFL_E_INVALID
+ *              stream) and out-of-range values return TFL_E_INVALID; that
+ *              mode also checks the magnitude precondition below (and that
+ *              x is finite) with device reductions, returning TFL_E_INVALID
  *   y          [batch, seq_len, d_model] I/O dtype, 16-byte aligned, must
  *              not overlap x or the workspace
  *   workspace  at least tfl_workspace_bytes() bytes, 256-byte aligned, must

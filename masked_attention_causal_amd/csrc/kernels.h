@@ -153,6 +153,8 @@ struct WconvArgs {
     int nseg;
 };
 hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s);
+// atomicMax of the fp32 bits of max |v| over n values (n % 4 == 0) into *out.
+hipError_t launch_amax(int dtype_size, bool is_bf16, const void* x, long n, unsigned* out, hipStream_t s);
 hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
 // Row-norm maxima of the Q and K hi planes ([BH, L, dh] fp16) per (sequence,
 // head) and chunk of rows: out [BH][qk_stats_chunks(L)] (max |q|, max |k|).

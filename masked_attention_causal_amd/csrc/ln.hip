@@ -248,6 +248,39 @@ hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- magnitude check
+// Largest |v| over n stored values, as fp32 bits atomically maxed into *out
+// (non-negative floats order like their bit patterns; a NaN has larger bits
+// than inf, so it shows as not finite).  Used by the TFL_CHECK=1 argument check.
+template <class T>
+__global__ __launch_bounds__(256) void amax_kernel(const T* __restrict__ x, long n, unsigned* __restrict__ out) {
+    unsigned m = 0;
+    const long step = (long)gridDim.x * 256 * 4;
+    for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += step) {
+        float v[4];
+        ld4(x + i, v);
+#pragma unroll
+        for (int e = 0; e < 4; e++) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o, WAVE));
+    if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+}
+
+hipError_t launch_amax(int dtype_size, bool is_bf16, const void* x, long n, unsigned* out, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (n % 4 != 0) return hipErrorInvalidValue;
+    const long blocks = (n / 4 + 255) / 256;
+    dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));
+    if (dtype_size == 4)
+        hipLaunchKernelGGL(amax_kernel<float>, grid, dim3(256), 0, s, (const float*)x, n, out);
+    else if (is_bf16)
+        hipLaunchKernelGGL(amax_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)x, n, out);
+    else
+        hipLaunchKernelGGL(amax_kernel<f16>, grid, dim3(256), 0, s, (const f16*)x, n, out);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- V^T padding
 // Columns [L, Lp) of the V^T rows are read as whole 64-key tiles by the
 // attention kernel's LDS-DMA; they must hold finite values (zeros), since

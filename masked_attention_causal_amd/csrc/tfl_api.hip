@@ -68,6 +68,65 @@ tfl_status static_workspace(void** out) {
     return TFL_OK;
 }
 
+// Device word of the TFL_CHECK=1 magnitude check (one per GPU, its address
+// taken with that device current).
+static __device__ unsigned check_amax_word;
+void* g_amax_ptr[MAX_DEVICES];
+
+// TFL_CHECK=1: the inputs the kernels round to fp16 operands must be finite
+// and below 65504 in magnitude (x and the GEMM weights with bf16 I/O on every
+// path and with fp32 I/O on the PQ and layer-wise paths); x must be finite on
+// every path.  One reduction launch per array, then a synchronising copy.
+tfl_status check_magnitudes(const tfl_handle* h, const void* x, hipStream_t s) {
+    const tfl::Plan& P = h->plan;
+    const int dt = h->cfg.dtype;
+    const bool f16_operands = dt == TFL_BF16 || (dt == TFL_F32 && !(P.path == TFL_PATH_SEQ && P.seq_kind == 1));
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return hip_fail(e, "tfl_forward: TFL_CHECK hipGetDevice");
+    if (!g_amax_ptr[dev]) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_amax_word));
+        if (e != hipSuccess) return hip_fail(e, "tfl_forward: TFL_CHECK hipGetSymbolAddress");
+        g_amax_ptr[dev] = p;
+    }
+    unsigned* word = (unsigned*)g_amax_ptr[dev];
+    const size_t esz = tfl::dtype_size(dt);
+    auto amax = [&](const void* a, long n, unsigned* bits) -> hipError_t {
+        hipError_t r = hipMemsetAsync(word, 0, sizeof(unsigned), s);
+        if (r == hipSuccess) r = tfl::launch_amax((int)esz, dt == TFL_BF16, a, n, word, s);
+        if (r == hipSuccess) r = hipMemcpyAsync(bits, word, sizeof(unsigned), hipMemcpyDeviceToHost, s);
+        if (r == hipSuccess) r = hipStreamSynchronize(s);
+        return r;
+    };
+    const float limit = 65504.f;
+    unsigned bits = 0;
+    if ((e = amax(x, (long)P.T * P.d, &bits)) != hipSuccess) return hip_fail(e, "tfl_forward: TFL_CHECK of x");
+    float v;
+    std::memcpy(&v, &bits, 4);
+    if (!(v <= 3.4028235e38f)) return fail(TFL_E_INVALID, "tfl_forward: x holds a non-finite value");
+    if (f16_operands && !(v < limit))
+        return fail(TFL_E_INVALID, "tfl_forward: |x| reaches " + std::to_string(v) +
+                                       "; the fp16 operands of this path need |x| < 65504");
+    if (!f16_operands) return TFL_OK;
+    const long dd = (long)P.d * P.d, df = (long)P.d * P.f;
+    for (int l = 0; l < P.n_layers; l++) {
+        const tfl_layer& w = h->layers[l];
+        const void* m[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
+        const long n[4] = {3 * dd, dd, df, df};
+        for (int k = 0; k < 4; k++) {
+            if ((e = amax(m[k], n[k], &bits)) != hipSuccess) return hip_fail(e, "tfl_forward: TFL_CHECK of the weights");
+            std::memcpy(&v, &bits, 4);
+            if (!(v < limit))
+                return fail(TFL_E_INVALID, "tfl_forward: layer " + std::to_string(l) + " weight matrix " +
+                                               std::to_string(k) + " reaches |w| = " + std::to_string(v) +
+                                               "; the fp16 operands of this path need |w| < 65504");
+        }
+    }
+    return TFL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,6 +199,8 @@ static tfl_status forward_impl(tfl_handle* h, const void* x, const int32_t* vali
             if (lens[b] < 1 || lens[b] > P.L)
                 return fail(TFL_E_INVALID, "tfl_forward: valid_len[" + std::to_string(b) + "] = " +
                                                std::to_string(lens[b]) + " outside [1, seq_len]");
+        const tfl_status st = check_magnitudes(h, x, s);
+        if (st != TFL_OK) return st;
     }
     tfl::StageTimer* tm = h->timer.stage ? &h->timer : nullptr;
     const hipError_t e = tfl::run_plan(P, h->layers.data(), x, valid_len, y, (char*)workspace, s, tm);

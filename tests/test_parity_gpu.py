@@ -394,6 +394,47 @@ def test_forward_error_statuses(monkeypatch, path):
     enc.close()
 
 
+@pytest.mark.parametrize("dtype,path,guarded", [("bf16", "tiled", True), ("bf16", "seq", True), ("f32", "pq", True),
+                                                ("f32", "seq", False)])
+def test_check_mode_magnitude_guard(monkeypatch, dtype, path, guarded):
+    """TFL_CHECK=1 refuses inputs the path would round into fp16 operands past
+    65504 (x, or a GEMM weight) and non-finite x, with TFL_E_INVALID; the
+    small fp32 kernel (fp32 arithmetic) takes large finite x."""
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    w = {"tiled": W("guard_t", 1, 64, 2, 64, 2, 16, dtype, 1, 16, 1.0),
+         "seq": W("guard_s", 1, 64, 2, 64, 2, 16, dtype, 1, 16, 1.0),
+         "pq": W("guard_p", 1, 64, 2, 128, 1, 256, dtype, 256, 256, 1.0)}[path]
+    inp = _case(w, 0)
+    layers = [{k: tfl.to_device(v, w.dtype) for k, v in lw.items()} for lw in inp.layers]
+    enc = tfl.Encoder(w.n_layers, w.d, w.H, w.f, w.B, w.L, w.dtype, layers, force_path=path)
+    lens = torch.from_numpy(inp.lens).cuda()
+    monkeypatch.setenv("TFL_CHECK", "1")
+    x = tfl.to_device(inp.x, w.dtype)
+    enc.forward(x, lens)                       # in range: accepted
+    big = x.clone()
+    big[0, 3, 5] = 70000.0
+    if guarded:
+        with pytest.raises(tfl.TflError) as e:
+            enc.forward(big, lens)
+        assert e.value.status == 1 and "65504" in str(e.value)
+    else:
+        enc.forward(big, lens)
+    nan = x.clone()
+    nan[-1, -1, -1] = float("nan")
+    with pytest.raises(tfl.TflError) as e:
+        enc.forward(nan, lens)
+    assert e.value.status == 1 and "finite" in str(e.value)
+    if guarded:
+        layers[0]["w_1"][7, 3] = 1e5
+        with pytest.raises(tfl.TflError) as e:
+            enc.forward(x, lens)
+        assert e.value.status == 1 and "weight" in str(e.value)
+    torch.cuda.synchronize()
+    enc.close()
+
+
 # ---------------------------------------------------------------- every path that supports a shape
 
 PATH_SHAPES = [
