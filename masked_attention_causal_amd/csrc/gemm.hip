@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_pipe_kernel(GemmArgs p) {
                 f16x4 o, ol;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const float gv = gelu_erf(v[e]);
+                    const float gv = gelu_full(v[e]);
                     o[e] = (f16)gv;
                     if constexpr (SPLIT) ol[e] = (f16)((gv - (float)o[e]) * LO_SCALE);
                 }

@@ -16,6 +16,7 @@ import os
 import re
 
 import numpy as np
+import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HDR = os.path.join(HERE, "..", "masked_attention_causal_amd", "csrc", "common.h")
@@ -85,3 +86,75 @@ def test_gelu_poly_identities():
 
 def test_gelu_small_threshold_inside_fit_range():
     assert _threshold() * 0.7071067811865475 <= 1.0
+
+
+# ---------------------------------------------------------------- whole-range form (gelu_full)
+
+def _full_coefficients():
+    """gelu_full's R, degree 0..9, read from the header."""
+    src = open(HDR).read()
+    body = src[src.index("float gelu_full(float h)"):]
+    body = body[:body.index("const float e = ")]
+    nums = [float(v) for v in re.findall(r"(-?\d+\.\d+(?:e-?\d+)?)f", body)]
+    # 1/sqrt(2), 2.0, then fmaf(u, c9, c8), fmaf(u, r, c7) ... fmaf(u, r, c0)
+    assert len(nums) == 2 + 10, nums
+    return nums[2:][::-1]
+
+
+def _gelu_full(h, ulp_rcp=0, ulp_exp=0):
+    """The kernel's arithmetic in fp32: fused multiply-adds rounded once, the
+    reciprocal and exp2 correctly rounded and then moved by ulp_rcp / ulp_exp
+    ulps (the hardware instructions are within one ulp)."""
+    c = _full_coefficients()
+    h = np.asarray(h, dtype=np.float32)
+    a = (np.abs(h) * np.float32(0.70710678118654752)).astype(np.float32)
+    u = (1.0 / (a + np.float32(2.0)).astype(np.float64)).astype(np.float32)
+    for _ in range(abs(ulp_rcp)):
+        u = np.nextafter(u, np.float32(np.inf if ulp_rcp > 0 else 0)).astype(np.float32)
+    r = _fma32(u, np.float32(c[9]), np.float32(c[8]))
+    for k in range(7, -1, -1):
+        r = _fma32(u, r, np.float32(c[k]))
+    arg = _fma32((a * a).astype(np.float32), np.float32(-1.4426950408889634), r)
+    ex = np.exp2(arg.astype(np.float64)).astype(np.float32)
+    ex = np.where(ex < np.float32(2.0 ** -126), np.float32(0), ex)      # exp2 flushes denormal results
+    for _ in range(abs(ulp_exp)):
+        ex = np.nextafter(ex, np.float32(np.inf if ulp_exp > 0 else 0)).astype(np.float32)
+    e = (u * ex).astype(np.float32)
+    he = (h * e).astype(np.float32)
+    return np.where(h >= 0, (h - he).astype(np.float32), he)
+
+
+def _gelu_ref(h):
+    return np.array([0.5 * v * math.erfc(-v / math.sqrt(2.0)) for v in np.asarray(h, np.float64)])
+
+
+@pytest.mark.parametrize("ulp_rcp,ulp_exp", [(0, 0), (1, 1), (-1, -1), (1, -1)])
+def test_gelu_full_error_bounds(ulp_rcp, ulp_exp):
+    h = np.concatenate([np.linspace(-13.0, 13.0, 130001), np.linspace(-1e-3, 1e-3, 2001)]).astype(np.float32)
+    got = _gelu_full(h, ulp_rcp, ulp_exp).astype(np.float64)
+    ref = _gelu_ref(h)
+    assert np.max(np.abs(got - ref)) <= 3e-7
+    mid = (np.abs(h) <= 3.0) & (ref != 0)
+    assert np.max(np.abs(got - ref)[mid] / np.abs(ref[mid])) <= 2e-6
+
+
+def test_gelu_full_implied_erfc():
+    # erfc(a) = 2e for a in [0, 6]: the fit itself, relative 5e-7
+    c = _full_coefficients()
+    a = np.linspace(0.0, 6.0, 6001)
+    u = 1.0 / (2.0 + a)
+    r = np.polyval(c[::-1], u)
+    got = 2.0 * u * np.exp2(r - a * a * 1.4426950408889634)
+    ref = np.array([math.erfc(v) for v in a])
+    assert np.max(np.abs(got - ref) / ref) <= 5e-7
+
+
+def test_gelu_full_identities_and_limits():
+    h = np.float32([0.125, 0.5, 1.0, 2.5, 4.0, 7.0])
+    assert _gelu_full(np.float32([0.0]))[0] == 0.0
+    d = _gelu_full(h).astype(np.float64) - _gelu_full(-h).astype(np.float64)
+    assert np.allclose(d, h.astype(np.float64), rtol=0, atol=1e-6)
+    big = np.float32([9.5, 13.0, 30.0, 1e4])
+    assert np.array_equal(_gelu_full(big), big)          # h e is below half an ulp of h
+    huge = np.float32([13.5, 30.0, 1e4])                 # a > 9.3: erfc(a)/2 < 2^-126, flushed
+    assert np.all(_gelu_full(-huge) == 0.0)
