@@ -48,16 +48,32 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
-// Whether the scores of this workgroup's (sequence, head) need the hi/lo
-// split.  A single fp16 pass rounds each of q and k by at most u = 2^-11
-// relative, so a score q.k (in exp2 units: times c) moves by at most
-// (2u + u^2) |q| |k| c (Cauchy-Schwarz over the head dimension; the fp32
-// accumulation of exact fp16 products adds far less).  The single pass is
-// taken when that bound, formed from the maxima of |q_i| and |k_j| over the
-// (sequence, head), is at most SPLIT_EXP_ERR: a relative error of at most
-// 0.27% in any softmax weight.  Every wave forms the same answer.
+// Score variant of this workgroup's (sequence, head), from the maxima of
+// |q_i| and |k_j| over it (qk_stats; c converts a score to exp2 units).
+//  * split: a single fp16 pass rounds each of q and k by at most u = 2^-11
+//    relative, so a score moves by at most (2u + u^2) |q| |k| c
+//    (Cauchy-Schwarz over the head dimension; the fp32 accumulation of exact
+//    fp16 products adds far less).  With split_mode 1 the hi/lo split is
+//    taken only when that bound exceeds SPLIT_EXP_ERR = 2^-8 (a relative
+//    error of at most 0.27% in any softmax weight); mode 0 never splits,
+//    mode 2 always does.
+//  * bounded: every score lies within +-|q| |k| c (times 1 + 2^-9 for the
+//    lo parts the hi-plane norms leave out).  When that is at most
+//    BOUND_EXP = 14 the weights 2^s lie in [2^-14, 2^14]: exact in fp16
+//    range with no reference subtracted (softmax is shift-invariant), so the
+//    kernels keep no running max and never rescale.
+// Every wave forms the same answers.
 constexpr float SPLIT_EXP_ERR = 0.00390625f;  // 2^-8
-__device__ __forceinline__ bool split_needed(const AttnArgs& p, float c) {
+constexpr float BOUND_EXP = 14.f;
+__device__ __forceinline__ void score_variant(const AttnArgs& p, float c, bool& split, bool& bounded) {
+    if (!p.qk_stats) {  // no statistics: the variant the split mode names, with a reference
+        split = p.split_mode == 2;
+        bounded = false;
+        if constexpr (MASK_ALL) {
+            if (threadIdx.x == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+        }
+        return;
+    }
     const float2* st = p.qk_stats + (size_t)blockIdx.x * p.stats_nch;
     float mq = 0.f, mk = 0.f;
     for (int i = (int)(threadIdx.x & 63); i < p.stats_nch; i += 64) {
@@ -69,8 +85,16 @@ __device__ __forceinline__ bool split_needed(const AttnArgs& p, float c) {
         mq = fmaxf(mq, __shfl_xor(mq, o, WAVE));
         mk = fmaxf(mk, __shfl_xor(mk, o, WAVE));
     }
-    const float bound = (0.0009765625f + 2.384185791015625e-07f) * mq * mk * c;  // (2u + u^2) |q| |k| c
-    return !(bound <= SPLIT_EXP_ERR);  // NaN or inf: split
+    const float qk = mq * mk * c;
+    const float err = (0.0009765625f + 2.384185791015625e-07f) * qk;  // (2u + u^2) |q| |k| c
+    split = p.split_mode == 2 || (p.split_mode == 1 && !(err <= SPLIT_EXP_ERR));  // NaN or inf: split
+    bounded = qk * 1.001953125f <= BOUND_EXP;
+    if constexpr (MASK_ALL) {
+        if (threadIdx.x == 0) {
+            if (split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+            if (bounded) audit_add(p.audit, AUD_BOUNDED_WG, 1);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- LDS-DMA ring
@@ -106,7 +130,7 @@ __device__ __forceinline__ int ksw(int r) {
 template <int DH, bool SPLIT>
 constexpr int ring_lds_bytes() { return 3 * (ATT_KT * DH * 2 * (SPLIT ? 2 : 1) + DH * ATT_KT * 2); }
 
-template <int DH, bool SPLIT>
+template <int DH, bool SPLIT, bool BOUNDED>
 __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
     constexpr int KT = ATT_KT, ST = 3;
     constexpr int KROW = DH * 2, KCH = KROW / 16;    // bytes and 16-byte chunks per K row
@@ -244,30 +268,40 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
                     if (key > myq || key >= len) sc[kb][e] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        // BOUNDED: every score of this (sequence, head) is within +-14 in
+        // exp2 units (bound_scores), so the weights 2^s need no reference:
+        // no running max, no rescaling, and none overflows or underflows fp16
+        float m_use = 0.f, alpha = 1.f;
+        if constexpr (!BOUNDED) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
-            mx = max3f(mx, sc[kb][0], sc[kb][1]);
-            mx = max3f(mx, sc[kb][2], sc[kb][3]);
+            for (int kb = 0; kb < 4; kb++) {
+                mx = max3f(mx, sc[kb][0], sc[kb][1]);
+                mx = max3f(mx, sc[kb][2], sc[kb][3]);
+            }
+            mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
+            mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
+            const float m_new = fmaxf(m_run, mx * sl2);
+            m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
+            m_run = m_new;
         }
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
-        m_run = m_new;
         float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], sl2, -m_use));
+                const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] * sl2 : fmaf(sc[kb][e], sl2, -m_use));
                 sc[kb][e] = pv;
                 ls += pv;
             }
-        l_run = l_run * alpha + ls;
+        if constexpr (BOUNDED) {
+            l_run += ls;
+        } else {
+            l_run = l_run * alpha + ls;
 #pragma unroll
-        for (int db = 0; db < ND; db++) o[db] *= alpha;
+            for (int db = 0; db < ND; db++) o[db] *= alpha;
+        }
 #pragma unroll
         for (int cc = 0; cc < 2; cc++) {
             f16x8 pb;
@@ -301,25 +335,25 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
     }
 }
 
-template <int DH, bool SPLIT>
+// The variant of a workgroup's (sequence, head) is chosen from the row-norm
+// maxima of its Q and K (score_variant): split or single scores, bounded or
+// referenced weights.
+// CAN_SPLIT: launched with split_mode 1 or 2 (the LDS ring then holds the lo
+// K planes too); split_mode 0 launches the copy without them.
+template <int DH, bool CAN_SPLIT>
 __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, SPLIT>()];
-    ring_body<DH, SPLIT>(p, lds);
-}
-
-// First-layer attention with the precision chosen per (sequence, head) from
-// the row-norm maxima of its Q and K (split_needed).
-template <int DH>
-__global__ __launch_bounds__(256) void attn_ring_adaptive_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, true>()];
-    const bool split = split_needed(p, p.scale_log2);
-    if constexpr (MASK_ALL) {
-        if (threadIdx.x == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+    __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, CAN_SPLIT>()];
+    bool split, bounded;
+    score_variant(p, p.scale_log2, split, bounded);
+    if (CAN_SPLIT && split) {
+        if constexpr (CAN_SPLIT) {
+            if (bounded) ring_body<DH, true, true>(p, lds);
+            else ring_body<DH, true, false>(p, lds);
+        }
+    } else {
+        if (bounded) ring_body<DH, false, true>(p, lds);
+        else ring_body<DH, false, false>(p, lds);
     }
-    if (split)
-        ring_body<DH, true>(p, lds);
-    else
-        ring_body<DH, false>(p, lds);
 }
 
 // ---------------------------------------------------------------- head dim 16
@@ -339,7 +373,7 @@ constexpr int ATT16_WAVES = 8, ATT16_BQ = 16 * ATT16_WAVES;
 template <bool SPLIT>
 constexpr int ring16_lds_bytes() { return 3 * (128 * 16 * 2 * (SPLIT ? 2 : 1) + 16 * 128 * 2); }
 
-template <bool SPLIT>
+template <bool SPLIT, bool BOUNDED>
 __device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
     constexpr int DH = 16, KT = 128, ST = 3;
     constexpr int KROW = DH * 2;                     // 32-byte K rows: two 16-byte chunks
@@ -467,7 +501,7 @@ __device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
             ka[kb] = *(lds_f16x4*)(size_t)(kad[kb] + BO);
             if constexpr (SPLIT) kl[kb] = *(lds_f16x4*)(size_t)(kadl[kb] + BO);
         }
-        const f32x4 c0 = f32x4{-m_ref, -m_ref, -m_ref, -m_ref};
+        const f32x4 c0 = BOUNDED ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{-m_ref, -m_ref, -m_ref, -m_ref};
 #pragma unroll
         for (int kb = 0; kb < 8; kb++) {
             sc[kb] = mfma_16x16x16(ka[kb], qh, c0);
@@ -490,6 +524,10 @@ __device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
                     if (key > myq || key >= len) sc[kb][e] = -INFINITY;
                 }
         }
+        // BOUNDED: every score of this (sequence, head) is within +-14 in
+        // exp2 units (score_variant), so the weights 2^s need no reference:
+        // no running max, no raise, and none overflows or underflows fp16
+        if constexpr (!BOUNDED) {
         // running max as a chain of three-input maxima (two new values each;
         // left to itself the compiler spends three instructions per four)
         float mx = -INFINITY;
@@ -520,6 +558,7 @@ __device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
             const float alpha = __builtin_amdgcn_exp2f(-dl);
             o *= alpha;
             lsum *= alpha;
+        }
         }
 #pragma unroll
         for (int cc = 0; cc < 4; cc++) {
@@ -554,24 +593,22 @@ __device__ __forceinline__ void ring16_body(const AttnArgs& p, char* lds) {
     store_o4(out + 4 * g, v, p.o_lo ? (size_t)p.B * L * p.d : 0);
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[ring16_lds_bytes<SPLIT>()];
-    ring16_body<SPLIT>(p, lds);
-}
-
 // Keys are stored multiplied by log2(e)/sqrt(dh), so their norms are already
 // in exp2 units.
-__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_adaptive_kernel(AttnArgs p) {
-    __shared__ __attribute__((aligned(16))) char lds[ring16_lds_bytes<true>()];
-    const bool split = split_needed(p, 1.0f);
-    if constexpr (MASK_ALL) {
-        if (threadIdx.x == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+template <bool CAN_SPLIT>
+__global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs p) {
+    __shared__ __attribute__((aligned(16))) char lds[ring16_lds_bytes<CAN_SPLIT>()];
+    bool split, bounded;
+    score_variant(p, 1.0f, split, bounded);
+    if (CAN_SPLIT && split) {
+        if constexpr (CAN_SPLIT) {
+            if (bounded) ring16_body<true, true>(p, lds);
+            else ring16_body<true, false>(p, lds);
+        }
+    } else {
+        if (bounded) ring16_body<false, true>(p, lds);
+        else ring16_body<false, false>(p, lds);
     }
-    if (split)
-        ring16_body<true>(p, lds);
-    else
-        ring16_body<false>(p, lds);
 }
 
 // ---------------------------------------------------------------- Q/K statistics
@@ -643,34 +680,29 @@ hipError_t launch_qk_stats(int dh, const void* Q, const void* K, int BH, int L, 
 // kernels take query tiles from the last (the most keys) to the first.
 static dim3 attn_grid(const AttnArgs& a, int bq) { return dim3((unsigned)(a.B * a.H), (unsigned)((a.L + bq - 1) / bq)); }
 
-hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s) {
-    if (a.B <= 0 || a.L <= 0) return hipSuccess;
-    if ((a.L + ATT_BQ - 1) / ATT_BQ > 65535) return hipErrorInvalidValue;  // query tiles: grid y
+hipError_t launch_attn(Mode m, int dh, const AttnArgs& a, hipStream_t s) {
     (void)m;  // every mode takes fp16 Q/K/V planes
-    if (dh == 32 || dh == 64) {
-        const dim3 grid = attn_grid(a, ATT_BQ);
-        if (split_qk && a.qk_stats) {
-            if (dh == 64) hipLaunchKernelGGL(attn_ring_adaptive_kernel<64>, grid, dim3(256), 0, s, a);
-            if (dh == 32) hipLaunchKernelGGL(attn_ring_adaptive_kernel<32>, grid, dim3(256), 0, s, a);
-            return hipGetLastError();
-        }
-        if (dh == 64 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, true>), grid, dim3(256), 0, s, a);
-        if (dh == 64 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<64, false>), grid, dim3(256), 0, s, a);
-        if (dh == 32 && split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, true>), grid, dim3(256), 0, s, a);
-        if (dh == 32 && !split_qk) hipLaunchKernelGGL((attn_ring_kernel<32, false>), grid, dim3(256), 0, s, a);
-        return hipGetLastError();
+    if (a.B <= 0 || a.L <= 0) return hipSuccess;
+    if ((a.qk_stats && a.stats_nch < 1) || (!a.qk_stats && a.split_mode == 1)) return hipErrorInvalidValue;
+    if ((a.L + ATT_BQ - 1) / ATT_BQ > 65535) return hipErrorInvalidValue;  // query tiles: grid y
+    const bool cs = a.split_mode != 0;
+    const dim3 g64 = attn_grid(a, ATT_BQ), g16 = attn_grid(a, ATT16_BQ);
+    switch (dh) {
+        case 64:
+            if (cs) hipLaunchKernelGGL((attn_ring_kernel<64, true>), g64, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((attn_ring_kernel<64, false>), g64, dim3(256), 0, s, a);
+            break;
+        case 32:
+            if (cs) hipLaunchKernelGGL((attn_ring_kernel<32, true>), g64, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((attn_ring_kernel<32, false>), g64, dim3(256), 0, s, a);
+            break;
+        case 16:  // the plan pads V^T rows to whole 128-key tiles
+            if (cs) hipLaunchKernelGGL((attn_ring16_kernel<true>), g16, dim3(64 * ATT16_WAVES), 0, s, a);
+            else hipLaunchKernelGGL((attn_ring16_kernel<false>), g16, dim3(64 * ATT16_WAVES), 0, s, a);
+            break;
+        default: return hipErrorInvalidValue;
     }
-    if (dh == 16) {   // the plan pads V^T rows to whole 128-key tiles
-        const dim3 grid = attn_grid(a, ATT16_BQ);
-        if (split_qk && a.qk_stats)
-            hipLaunchKernelGGL(attn_ring16_adaptive_kernel, grid, dim3(64 * ATT16_WAVES), 0, s, a);
-        else if (split_qk)
-            hipLaunchKernelGGL((attn_ring16_kernel<true>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
-        else
-            hipLaunchKernelGGL((attn_ring16_kernel<false>), grid, dim3(64 * ATT16_WAVES), 0, s, a);
-        return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace tfl

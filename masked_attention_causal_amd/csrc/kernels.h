@@ -53,11 +53,12 @@ struct AttnArgs {
     const void* Vt;    // [B, H, dh, Lp] fp16; columns >= L hold zeros
     void* O;           // [B*L, d] fp16, head h at columns h*dh
     int o_lo;          // 1: also the remainder times 2^11, B*L*d elements further (F32 mode)
-    // First layer with 16-bit I/O: per (sequence, head) row-norm maxima of Q
-    // and K written by qk_stats (stats_nch chunks each); when given, each
-    // workgroup takes the split scores only where their bound requires it.
+    // Per (sequence, head) row-norm maxima of Q and K written by qk_stats
+    // (stats_nch chunks each): each workgroup picks its score variant from
+    // them (split or single scores; weights with or without a reference).
     const float2* qk_stats;
     int stats_nch;
+    int split_mode;    // 0 single fp16 scores, 1 split where the bound needs it, 2 always split
     const int32_t* lens;
     int B, H, L, Lp, d;
     float scale_log2;  // log2(e) / sqrt(dh); the head-dim-16 kernel reads K already multiplied by it
@@ -155,7 +156,7 @@ struct WconvArgs {
 hipError_t launch_wconv(Mode m, const WconvArgs& a, hipStream_t s);
 // atomicMax of the fp32 bits of max |v| over n values (n % 4 == 0) into *out.
 hipError_t launch_amax(int dtype_size, bool is_bf16, const void* x, long n, unsigned* out, hipStream_t s);
-hipError_t launch_attn(Mode m, int dh, bool split_qk, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn(Mode m, int dh, const AttnArgs& a, hipStream_t s);
 // Row-norm maxima of the Q and K hi planes ([BH, L, dh] fp16) per (sequence,
 // head) and chunk of rows: out [BH][qk_stats_chunks(L)] (max |q|, max |k|).
 int qk_stats_chunks(int L);

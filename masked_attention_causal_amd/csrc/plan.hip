@@ -177,9 +177,9 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         const size_t per_layer = q.row_fused ? (size_t)3 * q.d * q.d : (size_t)4 * q.d * q.d + (size_t)2 * q.d * q.f;
         o += up256(per_layer * q.n_wconv * q.op);
     }
-    // first-layer Q/K row-norm maxima (16-bit I/O: adaptive score precision)
+    // per-layer Q/K row-norm maxima (the attention's score variant)
     q.off_S = o;
-    if (q.mode != MODE_F32) o += up256((size_t)q.B * q.H * qk_stats_chunks(q.L) * sizeof(float2));
+    o += up256((size_t)q.B * q.H * qk_stats_chunks(q.L) * sizeof(float2));
     q.ws_bytes = o;
     std::snprintf(q.name, sizeof(q.name), "TILED/attn.q%d.k%d/%s%s", ATT_BQ, ATT_KT,
                   q.mode == MODE_F32 ? "f32io.f16x3" : "f16op", q.row_fused ? "/rowfused" : "");
@@ -296,15 +296,21 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         a.audit = audit_counters;
         {
             Timed tm(T, TFL_STAGE_ATTN, s);
-            // 16-bit I/O, first layer: the split scores only where the Q/K
-            // magnitudes of a (sequence, head) need them
-            if (split && !f32) {
+            // Q/K magnitudes of each (sequence, head) choose its score
+            // variant: with 16-bit I/O the first layer splits only where they
+            // need it, fp32 I/O splits every layer; bounded scores take no
+            // softmax reference.  The statistics are formed where they can
+            // pay: the first layer of 16-bit I/O (the split), and head dim 16
+            // (whose softmax work dominates; at head dims 32/64 the bounded
+            // weights measured no faster than the statistics launch costs)
+            a.split_mode = f32 ? 2 : (l == 0 ? 1 : 0);
+            if (a.split_mode == 1 || P.dh == 16) {
                 float2* st = (float2*)(ws + P.off_S);
                 a.qk_stats = st;
                 a.stats_nch = qk_stats_chunks(P.L);
                 e = launch_qk_stats(P.dh, Q, K, P.B * P.H, P.L, st, s);
             }
-            if (e == hipSuccess) e = launch_attn(P.mode, P.dh, split, a, s);
+            if (e == hipSuccess) e = launch_attn(P.mode, P.dh, a, s);
             if ((e = tm.done(e)) != hipSuccess) return e;
         }
         if (P.row_fused) {

@@ -29,7 +29,10 @@ from tests.gate import say
 pytestmark = pytest.mark.gpu
 
 W = synth.Workload
-SLOTS = {"tiled_wg": 0, "tiled_wave": 1, "seq_wave": 2, "pq_wg": 3, "pq_wave": 4, "split_wg": 5}
+SLOTS = {"tiled_wg": 0, "tiled_wave": 1, "seq_wave": 2, "pq_wg": 3, "pq_wave": 4, "split_wg": 5, "bounded_wg": 6}
+# per-workgroup score-variant counts of the layer-wise kernels (checked by
+# test_score_variant_follows_magnitude, not by the tile-count test)
+VARIANT_SLOTS = {"split_wg", "bounded_wg"}
 
 
 def cdiv(a, b):
@@ -125,7 +128,7 @@ def test_mask_every_tile_is_bit_identical_and_tiles_match(w, path, lens):
     say(f"[audit] {w.name}: counted {got[:5].tolist()} expected {want}")
     for slot, n in want.items():
         assert int(got[SLOTS[slot]]) == n, (slot, int(got[SLOTS[slot]]), n)
-    for slot in set(SLOTS) - set(want):
+    for slot in set(SLOTS) - set(want) - (VARIANT_SLOTS if path == "tiled" else set()):
         assert got[SLOTS[slot]] == 0, slot
 
 
@@ -152,13 +155,18 @@ def test_full_length_visits_triangle(dh, dtype):
 
 
 @pytest.mark.parametrize("dh", [16, 64])
-def test_first_layer_split_follows_magnitude(dh):
-    """With 16-bit I/O the first layer's scores take the hi/lo split only
-    where the bound on a single fp16 pass's score error, formed from the
-    largest |q_i| and |k_j| of a (sequence, head), exceeds 2^-8 in exp2
-    units.  Inputs of scale 1 (|q|, |k| ~ 1) stay on the single pass; at scale
-    1e3 every first-layer workgroup takes the split, and the output still
-    meets the gate against the oracle."""
+def test_score_variant_follows_magnitude(dh):
+    """Each layer-wise attention workgroup picks its score variant from the
+    largest |q_i| and |k_j| of its (sequence, head).  Split: with 16-bit I/O
+    the first layer's scores take the hi/lo split only where the bound on a
+    single fp16 pass's score error exceeds 2^-8 in exp2 units.  Bounded: when
+    every score is within +-14 in exp2 units the weights take no reference.
+    The statistics are formed for the first layer and, at head dim 16, for
+    every layer (a layer without them neither splits nor bounds).  Inputs of
+    scale 1 (|q|, |k| ~ 1): no split, every workgroup with statistics
+    bounded.  Scale 1e3: every first-layer workgroup splits and is not
+    bounded; the second layer (LayerNorm-bounded input) is bounded where it
+    has statistics.  The outputs meet the gate against the oracle."""
     import torch
 
     import masked_attention_causal_amd as tfl
@@ -167,11 +175,13 @@ def test_first_layer_split_follows_magnitude(dh):
     w = W(f"a_adapt_dh{dh}", 2, dh * H, H, 256, 2, 300, "f16", 1, 300, 1.0)
     bq = 128 if dh == 16 else 64
     layer0_wgs = w.B * w.H * cdiv(w.L, bq)
-    for scale, want in ((1.0, 0), (1e3, layer0_wgs)):
+    later = layer0_wgs if dh == 16 else 0      # second-layer workgroups with statistics
+    for scale, want_split, want_bounded in ((1.0, 0, layer0_wgs + later), (1e3, layer0_wgs, later)):
         inp = synth.make_inputs(w, 7, scale=scale)
         counters = torch.zeros(8, dtype=torch.int64, device="cuda")
-        say(f"[audit adapt] {w.name} scale={scale}")
+        say(f"[audit variant] {w.name} scale={scale}")
         y = run(inp, "tiled", tfl.AUDIT_LIB_PATH, counters)
-        got = int(counters.cpu().numpy()[SLOTS["split_wg"]])
-        assert got == want, (scale, got, want)
+        got = counters.cpu().numpy()
+        assert int(got[SLOTS["split_wg"]]) == want_split, (scale, got.tolist())
+        assert int(got[SLOTS["bounded_wg"]]) == want_bounded, (scale, got.tolist())
         assert_gate(y, oracle_forward(inp), f"{w.name} scale {scale}")
