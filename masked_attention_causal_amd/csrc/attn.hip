@@ -615,7 +615,7 @@ __global__ __launch_bounds__(64 * ATT16_WAVES) void attn_ring16_kernel(AttnArgs 
 // Maxima of the row norms |q_i| and |k_j| of one (sequence, head) over a
 // chunk of QKS_ROWS rows of the hi planes, one workgroup per (sequence
 // head, chunk): out[bh * nch + chunk] = (max |q_i|, max |k_j|).
-constexpr int QKS_ROWS = 2048;
+constexpr int QKS_ROWS = 256;  // one row per thread: enough workgroups to fill the chip at B*H = 4
 
 template <int DH>
 __global__ __launch_bounds__(256) void qk_stats_kernel(const f16* __restrict__ Q, const f16* __restrict__ K, int L,

@@ -126,7 +126,7 @@ def test_workspace_covers_the_tiled_buffers():
     assert plan.endswith("/rowfused"), plan
     T = w.B * w.L
     Lp = (w.L + 127) // 128 * 128          # V^T rows padded to whole 128-key tiles
-    stats = w.B * w.H * -(-w.L // 2048) * 8    # first-layer Q/K row-norm maxima per 2048 rows
+    stats = w.B * w.H * -(-w.L // 256) * 8     # per-layer Q/K row-norm maxima per 256 rows
     need = 3 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + stats
     assert need <= ws <= need + 7 * 256
     # d_model 1024, bf16 I/O: separate kernels, all buffers, plus every
@@ -137,7 +137,7 @@ def test_workspace_covers_the_tiled_buffers():
     T = w.B * w.L
     Lp = (w.L + 127) // 128 * 128
     wts = w.n_layers * (4 * w.d * w.d + 2 * w.d * w.f)
-    stats = w.B * w.H * -(-w.L // 2048) * 8
+    stats = w.B * w.H * -(-w.L // 256) * 8
     need = 5 * T * w.d * 4 + 2 * T * w.d * 2 + w.B * w.d * Lp * 2 + T * w.f * 2 + wts * 2 + stats
     assert need <= ws <= need + 11 * 256
     # fp32 I/O stays on the separate kernels, with two fp16 planes (hi, lo)
