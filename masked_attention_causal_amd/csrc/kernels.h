@@ -84,6 +84,9 @@ struct SeqArgs {
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
+// First-layer QKV tasks per 64-row tile on the PQ path.
+constexpr int PQ_QKV_PARTS = 3;
+
 // PQ path: the stack as a task list over 64-row tiles (layer-0 QKV
 // projection, split-K attention, fused row tasks), run as one launch per
 // stage of the list.

@@ -6,7 +6,10 @@
 // tasks sized so that every compute unit has work).
 //
 // Task list (64-row tiles of one sequence; t = tile, s = key split):
-//   QKV0(b,t)           layer-0 projection of x rows
+//   QKV0(b,t,part)      layer-0 projection of x rows, in PQ_QKV_PARTS tasks
+//                       per tile (each a third of every wave's output
+//                       features), so this stage has three times the tiles'
+//                       workgroups
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
 //   ROW(l,b,t)          merge of the partials, out-projection + residual +
@@ -269,7 +272,7 @@ struct PqTile {
 // One pass of QNB feature blocks starting at global QKV feature n0 (0..3D):
 // adds the bias, sends q and k rows to the head-major fp16 buffers (hi, and
 // lo when `lo_parts`), and v into the LDS V^T staging area.
-template <class WT, int D, int DH, int QNB>
+template <class WT, int D, int DH, int QNB, bool DIRECT_VT>
 __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqArgs& p, int layer, bool lo_parts,
                                           int b, int t, int n0, f16* vts, int c16, int g) {
     constexpr int H = D / DH;
@@ -289,8 +292,16 @@ __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqAr
 #pragma unroll
             for (int e = 0; e < 4; e++) v[e] = acc[nb][rb][e] + bv[e];
             if (which == 2) {
+                if constexpr (DIRECT_VT) {
+                    // straight to the layer's V^T rows (columns past L hold
+                    // the bias of zero rows: finite, and masked as keys)
+                    f16* vt = p.Vt + (size_t)layer * p.B * D * p.Lp + (((size_t)b * H + h) * DH + dd) * p.Lp + pos;
 #pragma unroll
-                for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
+                    for (int e = 0; e < 4; e++) vt[(size_t)e * p.Lp] = (f16)v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
+                }
             } else if (pos < p.L) {
                 const size_t off = (size_t)layer * TD + (((size_t)b * H + h) * p.L + pos) * DH + dd;
                 f16* hi = (which == 0 ? p.Qh : p.Kh) + off;
@@ -325,9 +336,13 @@ __device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int 
 }
 
 // QKV projection of the 64 rows held in LDS (act; act_lo with fp32 I/O on
-// layer 0), then V^T flush.  Caller has synchronised after filling act.
-template <class WT, int D, int DH>
-__device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int t, char* smem, int tid) {
+// layer 0): every wave's passes [ps0, ps1) of its output features.  V^T goes
+// through the LDS staging area and one coalesced flush, or (DIRECT_VT, for a
+// task that computes only some of the features) straight to global memory.
+// Caller has synchronised after filling act.
+template <class WT, int D, int DH, bool DIRECT_VT = false>
+__device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int t, char* smem, int tid, int ps0 = 0,
+                                         int ps1 = PqTile<WT, D, DH>::QPASS) {
     typedef PqTile<WT, D, DH> TL;
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     const f16* act = (const f16*)(smem + TL::OFF_ACT);
@@ -335,7 +350,7 @@ __device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int 
     const WT* W = (const WT*)p.lw[layer].w_qkv;
     const bool first = layer == 0;
 #pragma unroll 1
-    for (int ps = 0; ps < TL::QPASS; ps++) {
+    for (int ps = ps0; ps < ps1; ps++) {
         const int n0 = wave * (3 * D / 4) + ps * 16 * TL::QNB;
         f32x4 acc[TL::QNB][4];
 #pragma unroll
@@ -361,16 +376,18 @@ __device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int 
         } else {
             mm_rows<TL::QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
         }
-        qkv_store<WT, D, DH, TL::QNB>(acc, p, layer, first, b, t, n0, vts, c16, g);
+        qkv_store<WT, D, DH, TL::QNB, DIRECT_VT>(acc, p, layer, first, b, t, n0, vts, c16, g);
     }
-    __syncthreads();
-    vt_flush<WT, D, DH>(p, layer, b, t, vts, tid);
+    if constexpr (!DIRECT_VT) {
+        __syncthreads();
+        vt_flush<WT, D, DH>(p, layer, b, t, vts, tid);
+    }
 }
 
 // ------------------------------------------------------------------ tasks
 
 template <class WT, int D, int DH>
-__device__ void task_qkv0(const PqArgs& p, int b, int t, char* smem, int tid) {
+__device__ void task_qkv0(const PqArgs& p, int b, int t, int part, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
     f16* act = (f16*)(smem + TL::OFF_ACT);
     f16* act_lo = (f16*)(smem + TL::OFF_ACT2);
@@ -402,7 +419,9 @@ __device__ void task_qkv0(const PqArgs& p, int b, int t, char* smem, int tid) {
         }
     }
     __syncthreads();
-    qkv_rows<WT, D, DH>(p, 0, b, t, smem, tid);
+    constexpr int QP = TL::QPASS / PQ_QKV_PARTS;
+    static_assert(QP * PQ_QKV_PARTS == TL::QPASS, "QKV passes split evenly over the parts");
+    qkv_rows<WT, D, DH, true>(p, 0, b, t, smem, tid, part * QP, (part + 1) * QP);
 }
 
 template <class WT, int D, int DH, bool SPLIT>
@@ -826,13 +845,15 @@ template <int H>
 __device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
     PqTask k{};
     const int BNT = p.B * p.NT;
-    if (task < BNT) {                            // QKV0(b, t): tile-major order
+    if (task < PQ_QKV_PARTS * BNT) {             // QKV0(b, t, part): part-major, then tile-major
         k.kind = 0;
-        k.t = task / p.B;
-        k.b = task - k.t * p.B;
+        k.s = task / BNT;
+        const int r = task - k.s * BNT;
+        k.t = r / p.B;
+        k.b = r - k.t * p.B;
         return k;
     }
-    task -= BNT;
+    task -= PQ_QKV_PARTS * BNT;
     const int n_att = p.B * H * p.Ctot;
     const int seg = n_att + BNT;                 // tasks per layer after QKV0
     k.l = task / seg;
@@ -862,7 +883,7 @@ __device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
 template <class WT, int D, int DH>
 __device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* smem, int tid) {
     if (k.kind == 0)
-        task_qkv0<WT, D, DH>(p, k.b, k.t, smem, tid);
+        task_qkv0<WT, D, DH>(p, k.b, k.t, k.s, smem, tid);
     else if (k.kind == 1 && k.l == 0)
         task_att<WT, D, DH, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
     else if (k.kind == 1)
@@ -895,7 +916,7 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
         return hipGetLastError();
     };
     hipError_t e;
-    if ((e = stage(BNT)) != hipSuccess) return e;
+    if ((e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     for (int l = 0; l < a.n_layers; l++) {
         if ((e = stage(n_att)) != hipSuccess) return e;
         if ((e = stage(BNT)) != hipSuccess) return e;
