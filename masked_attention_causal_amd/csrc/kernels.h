@@ -84,7 +84,7 @@ struct SeqArgs {
     LayerPtrs lw[SEQ_MAX_LAYERS];
 };
 
-// First-layer QKV tasks per 64-row tile on the PQ path.
+// QKV tasks per 64-row tile and layer on the PQ path.
 constexpr int PQ_QKV_PARTS = 3;
 
 // PQ path: the stack as a task list over 64-row tiles (layer-0 QKV

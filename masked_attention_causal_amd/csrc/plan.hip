@@ -123,7 +123,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         q.pq_ks = 8;
         q.pq_ctot = NT + q.pq_ks * (NT / q.pq_ks) * (NT / q.pq_ks - 1) / 2 + (NT / q.pq_ks) * (NT % q.pq_ks);
         const long n_att = (long)q.B * q.H * q.pq_ctot;
-        const long n_tasks = (long)PQ_QKV_PARTS * BNT + (long)q.n_layers * (n_att + BNT);
+        const long n_tasks = (long)PQ_QKV_PARTS * BNT * q.n_layers + (long)q.n_layers * (n_att + BNT);
         if (n_tasks > INT_MAX / 2) {
             *why = "too many tasks for the PQ path";
             return TFL_E_UNSUPPORTED;

@@ -6,19 +6,20 @@
 // tasks sized so that every compute unit has work).
 //
 // Task list (64-row tiles of one sequence; t = tile, s = key split):
-//   QKV0(b,t,part)      layer-0 projection of x rows, in PQ_QKV_PARTS tasks
-//                       per tile (each a third of every wave's output
-//                       features), so this stage has three times the tiles'
+//   QKV(l,b,t,part)     layer-l projection of the tile's rows (x for l = 0,
+//                       the residual stream after that), in PQ_QKV_PARTS
+//                       tasks per tile (each a third of every wave's output
+//                       features), so the stage has three times the tiles'
 //                       workgroups
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
 //   ROW(l,b,t)          merge of the partials, out-projection + residual +
 //                       LayerNorm, FFN (exact-erf GELU) + residual +
-//                       LayerNorm, then the next layer's QKV projection of
-//                       the same rows (or y after the last layer)
-// The list runs as one launch per stage (QKV0, then ATT and ROW of every
-// layer), workgroup i of a stage running its task i; each stage depends only
-// on earlier launches on the stream.  The pages' single persistent launch
+//                       LayerNorm, written to the residual stream (or y after
+//                       the last layer)
+// The list runs as one launch per stage (QKV, ATT and ROW of every layer),
+// workgroup i of a stage running its task i; each stage depends only on
+// earlier launches on the stream.  The pages' single persistent launch
 // (workgroups popping task ids from a device queue and waiting on dependency
 // counters) is not offered: its one run on the GPU did not finish, and no
 // cause has been shown.
@@ -387,7 +388,7 @@ __device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int 
 // ------------------------------------------------------------------ tasks
 
 template <class WT, int D, int DH>
-__device__ void task_qkv0(const PqArgs& p, int b, int t, int part, char* smem, int tid) {
+__device__ void task_qkv(const PqArgs& p, int layer, int b, int t, int part, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
     f16* act = (f16*)(smem + TL::OFF_ACT);
     f16* act_lo = (f16*)(smem + TL::OFF_ACT2);
@@ -400,7 +401,11 @@ __device__ void task_qkv0(const PqArgs& p, int b, int t, int part, char* smem, i
         const int pos = t * PQ_RT + r;
         const bool ok = pos < p.L;
         const WT* src = x + ((size_t)b * p.L + pos) * D + k;
-        if constexpr (TL::F32) {
+        if (layer > 0) {
+            // the residual stream the previous layer's row task wrote (rows
+            // past L: zeros, they only feed masked keys and unstored rows)
+            *(f16x8*)(act + r * TL::ALD + k) = ok ? load8_as_f16(p.X + ((size_t)b * p.L + pos) * D + k) : f16x8{};
+        } else if constexpr (TL::F32) {
             f16x8 hi = {}, lo = {};
             if (ok) {
                 const float4 a = *(const float4*)src, c2 = *(const float4*)(src + 4);
@@ -421,7 +426,7 @@ __device__ void task_qkv0(const PqArgs& p, int b, int t, int part, char* smem, i
     __syncthreads();
     constexpr int QP = TL::QPASS / PQ_QKV_PARTS;
     static_assert(QP * PQ_QKV_PARTS == TL::QPASS, "QKV passes split evenly over the parts");
-    qkv_rows<WT, D, DH, true>(p, 0, b, t, smem, tid, part * QP, (part + 1) * QP);
+    qkv_rows<WT, D, DH, true>(p, layer, b, t, smem, tid, part * QP, (part + 1) * QP);
 }
 
 template <class WT, int D, int DH, bool SPLIT>
@@ -827,37 +832,38 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
                 else
                     store4(p.X + row * D + n, v);
             }
-            if (!last) store4(act + r * TL::ALD + n, v);
         }
     }
-    if (last) return;
-    __syncthreads();
-    qkv_rows<WT, D, DH>(p, l + 1, b, t, smem, tid);
 }
 
 // ------------------------------------------------------------------ task list
 
-// Task id -> (kind, layer, sequence, head, tile, split).  kind: 0 QKV0, 1 ATT, 2 ROW.
+// Task id -> (kind, layer, sequence, head, tile, split or part).  kind: 0
+// QKV, 1 ATT, 2 ROW.  Order: QKV(0); then per layer ATT, ROW and, before
+// every later layer, its QKV.
 struct PqTask {
     int kind, l, b, h, t, s;
 };
 template <int H>
 __device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
     PqTask k{};
-    const int BNT = p.B * p.NT;
-    if (task < PQ_QKV_PARTS * BNT) {             // QKV0(b, t, part): part-major, then tile-major
+    const int BNT = p.B * p.NT, NQ = PQ_QKV_PARTS * BNT;
+    auto qkv = [&](int layer, int r) {           // QKV(layer, b, t, part): part-major, then tile-major
         k.kind = 0;
-        k.s = task / BNT;
-        const int r = task - k.s * BNT;
+        k.l = layer;
+        k.s = r / BNT;
+        r -= k.s * BNT;
         k.t = r / p.B;
         k.b = r - k.t * p.B;
         return k;
-    }
-    task -= PQ_QKV_PARTS * BNT;
+    };
+    if (task < NQ) return qkv(0, task);
+    task -= NQ;
     const int n_att = p.B * H * p.Ctot;
-    const int seg = n_att + BNT;                 // tasks per layer after QKV0
+    const int seg = n_att + BNT + NQ;            // tasks per layer after QKV(0), the last has no QKV
     k.l = task / seg;
     int r = task - k.l * seg;
+    if (r >= n_att + BNT) return qkv(k.l + 1, r - n_att - BNT);
     if (r < n_att) {                             // ATT(l, b, h, t, s)
         const int BH = p.B * H;
         const int pair = r / BH, bh = r - pair * BH;
@@ -883,7 +889,7 @@ __device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
 template <class WT, int D, int DH>
 __device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* smem, int tid) {
     if (k.kind == 0)
-        task_qkv0<WT, D, DH>(p, k.b, k.t, k.s, smem, tid);
+        task_qkv<WT, D, DH>(p, k.l, k.b, k.t, k.s, smem, tid);
     else if (k.kind == 1 && k.l == 0)
         task_att<WT, D, DH, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
     else if (k.kind == 1)
@@ -920,6 +926,7 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     for (int l = 0; l < a.n_layers; l++) {
         if ((e = stage(n_att)) != hipSuccess) return e;
         if ((e = stage(BNT)) != hipSuccess) return e;
+        if (l + 1 < a.n_layers && (e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     }
     return hipSuccess;
 }
