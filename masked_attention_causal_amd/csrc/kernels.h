@@ -109,6 +109,10 @@ struct PqArgs {
     float2* ML;      // [B*H*Ctot][64] (running max in log2 units, sum)
     unsigned long long* audit;  // tile counters of the audit build (null otherwise)
     LayerPtrs lw[SEQ_MAX_LAYERS];
+    // fp16 weight matrices per layer (W_qkv, W_o, W_1, W_2): the given ones
+    // with fp16 I/O, else converted once per forward; with fp32 I/O each is
+    // followed by its lo plane (rounding remainder times 2^11)
+    const _Float16* wh[SEQ_MAX_LAYERS][4];
 };
 
 // Fused row kernel of the layer-wise path (16-bit I/O, d in {64, 128, 256}):

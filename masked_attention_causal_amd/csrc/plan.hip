@@ -139,6 +139,10 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         q.off_pVt = o; o += up256((size_t)q.B * q.d * q.Lp * 2 * q.n_layers);
         q.off_Op = o;  o += up256(slots * 64 * q.dh * 4);
         q.off_ML = o;  o += up256(slots * 64 * 8);
+        // fp16 weight planes (bf16 / fp32 I/O; fp32: hi and lo planes)
+        q.off_pW = o;
+        if (q.mode != MODE_F16)
+            o += up256(((size_t)4 * q.d * q.d + (size_t)2 * q.d * q.f) * q.n_layers * (q.mode == MODE_F32 ? 4 : 2));
         q.ws_bytes = o;
         std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d/staged/%s", q.pq_ks, q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
         *p = q;
@@ -422,8 +426,29 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
         a.lw[l] = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b,
                             w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
     }
+    // fp16 weights: the given ones with fp16 I/O, else converted here
+    const size_t dd = (size_t)P.d * P.d, df = (size_t)P.d * P.f, planes = P.mode == MODE_F32 ? 2 : 1;
+    const size_t n[4] = {3 * dd, dd, df, df};
+    WconvArgs wa{};
+    f16* cw = (f16*)(ws + P.off_pW);
+    for (int l = 0; l < P.n_layers; l++) {
+        const tfl_layer& w = layers[l];
+        const void* src[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
+        for (int k = 0; k < 4; k++) {
+            if (P.mode == MODE_F16) {
+                a.wh[l][k] = (const f16*)src[k];
+            } else {
+                a.wh[l][k] = cw;
+                wa.seg[wa.nseg++] = WconvSeg{src[k], cw, (long)n[k]};
+                cw += n[k] * planes;
+            }
+        }
+    }
     Timed tm(T, TFL_STAGE_FUSED, s);
-    return tm.done(launch_pq(P.mode, P.d, P.dh, a, s));
+    hipError_t e = hipSuccess;
+    if (wa.nseg > 0) e = launch_wconv(P.mode, wa, s);   // at most 4 * SEQ_MAX_LAYERS = WCONV_MAX_SEGS segments
+    if (e == hipSuccess) e = launch_pq(P.mode, P.d, P.dh, a, s);
+    return tm.done(e);
 }
 
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,

@@ -33,13 +33,16 @@
 // Products: activations of the 64 tile rows sit in LDS as fp16 (B operand);
 // each wave streams its own slice of output features' weight rows straight
 // from global memory into registers (A operand), so weights are never
-// staged through LDS and each weight fragment feeds four MFMAs.
+// staged through LDS and each weight fragment feeds four MFMAs.  The weights
+// are fp16 in memory: bf16 and fp32 weights are converted once per forward
+// (fp32: an fp16 plane and a plane of the remainders times 2^11), which
+// halves the bytes every row task streams and takes the conversion out of
+// its loads.
 //
-// Precision: fp32 residual stream and LayerNorm; fp16 operands (bf16 and
-// fp32 weights are rounded to fp16 as they are loaded) except where the
-// first layer sees raw inputs: its attention scores use hi + lo fp16 parts
-// of fp32 Q and K (three MFMAs), and with fp32 I/O its QKV projection uses
-// hi + 2^11-scaled lo parts of both x and the weights (three MFMAs, two
+// Precision: fp32 residual stream and LayerNorm; fp16 operands except where
+// the first layer sees raw inputs: its attention scores use hi + lo fp16
+// parts of fp32 Q and K (three MFMAs), and with fp32 I/O its QKV projection
+// uses hi + 2^11-scaled lo parts of both x and the weights (three MFMAs, two
 // accumulators), which keeps scores near 1e5 fp32-accurate.
 #pragma once
 #include "common.h"
@@ -82,19 +85,6 @@ __device__ __forceinline__ void store4(WT* p, const float (&v)[4]) {
 __device__ __forceinline__ void store4(float* p, const float (&v)[4]) { *(float4*)p = float4{v[0], v[1], v[2], v[3]}; }
 __device__ __forceinline__ void store4(f16* p, const float (&v)[4]) {
     *(f16x4*)p = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-}
-
-// Eight fp32 weights -> hi fp16 and lo fp16 scaled by 2^11 (w = hi + lo * 2^-11
-// to about 22 significant bits).
-__device__ __forceinline__ void load8_split(const float* p, f16x8& hi, f16x8& lo) {
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const f16 h = (f16)v[e];
-        hi[e] = h;
-        lo[e] = (f16)((v[e] - (float)h) * 2048.0f);
-    }
 }
 
 // acc[nb][rb] += W[n0 + 16 nb + i][k0 + k] * act[16 rb + j][k] for k < K:
@@ -157,11 +147,12 @@ __device__ __forceinline__ void frags_mma(f32x4 (&acc)[NBW][4], const f16x8 (&a)
     }
 }
 
-// Three-pass version for fp32 weights and a hi/lo activation pair:
+// Three-pass version for hi/lo weight planes and a hi/lo activation pair:
 // main += Wh*Ah, lo += Wl*Ah + Wh*Al (lo parts carry a 2^11 scale).
 template <int NBW, int K>
-__device__ __forceinline__ void mm_rows_split(f32x4 (&main)[NBW][4], f32x4 (&lo)[NBW][4], const float* W, int ldw,
-                                              int n0, const f16* act, const f16* act_lo, int ald, int c16, int g) {
+__device__ __forceinline__ void mm_rows_split(f32x4 (&main)[NBW][4], f32x4 (&lo)[NBW][4], const f16* W,
+                                              const f16* Wlo, int ldw, int n0, const f16* act, const f16* act_lo,
+                                              int ald, int c16, int g) {
     constexpr int KS = K / 32;
     static_assert(KS % 2 == 0, "K must be a multiple of 64");
 #pragma unroll 1
@@ -170,8 +161,11 @@ __device__ __forceinline__ void mm_rows_split(f32x4 (&main)[NBW][4], f32x4 (&lo)
     for (int ks = ks2; ks < ks2 + 2; ks++) {
         f16x8 wh[NBW], wl[NBW];
 #pragma unroll
-        for (int nb = 0; nb < NBW; nb++)
-            load8_split(W + (size_t)(n0 + 16 * nb + c16) * ldw + ks * 32 + 8 * g, wh[nb], wl[nb]);
+        for (int nb = 0; nb < NBW; nb++) {
+            const size_t o = (size_t)(n0 + 16 * nb + c16) * ldw + ks * 32 + 8 * g;
+            wh[nb] = *(const f16x8*)(W + o);
+            wl[nb] = *(const f16x8*)(Wlo + o);
+        }
         f16x8 bh[4], bl[4];
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) {
@@ -348,7 +342,7 @@ __device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int 
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     const f16* act = (const f16*)(smem + TL::OFF_ACT);
     f16* vts = (f16*)(smem + TL::OFF_GV);
-    const WT* W = (const WT*)p.lw[layer].w_qkv;
+    const f16* W = p.wh[layer][0];
     const bool first = layer == 0;
 #pragma unroll 1
     for (int ps = ps0; ps < ps1; ps++) {
@@ -365,7 +359,7 @@ __device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int 
                 for (int nb = 0; nb < TL::QNB; nb++)
 #pragma unroll
                     for (int rb = 0; rb < 4; rb++) lo[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mm_rows_split<TL::QNB, D>(acc, lo, (const float*)W, D, n0, act,
+                mm_rows_split<TL::QNB, D>(acc, lo, W, W + (size_t)3 * D * D, D, n0, act,
                                           (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
 #pragma unroll
                 for (int nb = 0; nb < TL::QNB; nb++)
@@ -681,7 +675,7 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     constexpr bool PRE = NB <= 2;
     constexpr int NBWO = NB == 1 ? 1 : 2;
     f16x8 ao[PRE ? D / 32 : 1][NBWO];
-    if constexpr (PRE) frags_load<NBWO, D / 32>(ao, (const WT*)w.w_o, D, n0, 0, c16, g);
+    if constexpr (PRE) frags_load<NBWO, D / 32>(ao, p.wh[l][1], D, n0, 0, c16, g);
     merge_att<WT, D, DH>(p, b, t, act, tid);
     __syncthreads();
 
@@ -695,12 +689,12 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
         f32x4 (&zz)[NBWO][4] = *reinterpret_cast<f32x4(*)[NBWO][4]>(&z[0]);
         frags_mma<NBWO, D / 32>(zz, ao, act, TL::ALD, c16, g);
     } else if constexpr (NB == 1) {
-        mm_rows<1, D>(z, (const WT*)w.w_o, D, n0, 0, act, TL::ALD, c16, g);
+        mm_rows<1, D>(z, p.wh[l][1], D, n0, 0, act, TL::ALD, c16, g);
     } else {
 #pragma unroll
         for (int half = 0; half < NB / 2; half++) {
             f32x4 (&zz)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&z[2 * half]);
-            mm_rows<2, D>(zz, (const WT*)w.w_o, D, n0 + 32 * half, 0, act, TL::ALD, c16, g);
+            mm_rows<2, D>(zz, p.wh[l][1], D, n0 + 32 * half, 0, act, TL::ALD, c16, g);
         }
     }
 #pragma unroll
@@ -758,14 +752,14 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
         if constexpr (PRE) {
 #pragma unroll
             for (int hh = 0; hh < NH; hh++)
-                frags_load<NBW2, PQ_FC / 32>(a2[hh], (const WT*)w.w_2, p.F, n0 + 32 * hh, c * PQ_FC, c16, g);
+                frags_load<NBW2, PQ_FC / 32>(a2[hh], p.wh[l][3], p.F, n0 + 32 * hh, c * PQ_FC, c16, g);
         }
         f32x4 ga[2][4];
 #pragma unroll
         for (int nb = 0; nb < 2; nb++)
 #pragma unroll
             for (int rb = 0; rb < 4; rb++) ga[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mm_rows<2, D>(ga, (const WT*)w.w_1, D, f0, 0, act, TL::ALD, c16, g);
+        mm_rows<2, D>(ga, p.wh[l][2], D, f0, 0, act, TL::ALD, c16, g);
         // bias, then GELU on all 32 values of the lane at once: the
         // short-range polynomial when the whole wave is in its range
 #pragma unroll
@@ -798,7 +792,7 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
 #pragma unroll
             for (int hh = 0; hh < NB / 2; hh++) {
                 f32x4 (&yy)[2][4] = *reinterpret_cast<f32x4(*)[2][4]>(&y2[2 * hh]);
-                mm_rows<2, PQ_FC>(yy, (const WT*)w.w_2, p.F, n0 + 32 * hh, c * PQ_FC, gb, TL::GLD, c16, g);
+                mm_rows<2, PQ_FC>(yy, p.wh[l][3], p.F, n0 + 32 * hh, c * PQ_FC, gb, TL::GLD, c16, g);
             }
         }
     }

@@ -113,9 +113,14 @@ def test_pq_workspace_layout():
     pairs = NT + ks * q * (q - 1) // 2 + q * r          # (tile, split) pairs per (sequence, head)
     assert pairs == sum(t // ks + 1 for t in range(NT))
     T, dh, Lp = B * L, d // H, NT * 64
+    weights = n_layers * (4 * d * d + 2 * d * f) * 2 * 2     # fp16 hi and lo planes of every GEMM weight
     need = (up(T * d * 4) + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
-            + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8))
+            + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8)
+            + up(weights))
     assert ws == need
+    # fp16 I/O reads the given weights: no planes
+    ws16 = tfl.plan_for(n_layers, d, H, f, B, L, "f16", force_path="pq")[2]
+    assert ws16 == need - up(weights) - (up(T * d * 4) - up(T * d * 4))
 
 
 def test_workspace_covers_the_tiled_buffers():
