@@ -259,7 +259,8 @@ struct PqTile {
     static constexpr int ROW_BYTES = OFF_RED + 2 * 256 * 4;
     // attention task
     static constexpr int KLD = DH + 8, VLD = 64 + 8;
-    static constexpr int ATT_BYTES = 2 * (2 * 64 * KLD * 2) + 2 * DH * VLD * 2;
+    static constexpr int ATT_BYTES = 2 * (2 * 64 * KLD * 2) + 2 * DH * VLD * 2;     // with lo K planes
+    static constexpr int ATT1_BYTES = 2 * 64 * KLD * 2 + 2 * DH * VLD * 2;         // without
     static constexpr int SMEM = ROW_BYTES > ATT_BYTES ? ROW_BYTES : ATT_BYTES;
 };
 
@@ -429,8 +430,8 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     constexpr int KT = 64, KLD = TL::KLD, VLD = TL::VLD, ND = DH / 16, QK = DH / 32;
     constexpr int H = D / DH;
     f16* Ks = (f16*)smem;                  // [2][KT * KLD]
-    f16* Kls = Ks + 2 * KT * KLD;          // [2][KT * KLD]
-    f16* Vs = Kls + 2 * KT * KLD;          // [2][DH * VLD]
+    f16* Kls = Ks + 2 * KT * KLD;          // [2][KT * KLD], lo planes (SPLIT only)
+    f16* Vs = Ks + (SPLIT ? 4 : 2) * KT * KLD;  // [2][DH * VLD]
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     const int L = p.L, Lp = p.Lp;
     int len = p.lens[b];
@@ -904,6 +905,17 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int b
     pq_run<WT, D, DH>(p, k, smem, threadIdx.x);
 }
 
+// Attention stages of the later layers (single fp16 scores) in a kernel of
+// their own: LDS for K and V only and registers for four workgroups per CU,
+// so the stage's (tile, split) tasks run in one round.
+template <class WT, int D, int DH>
+__global__ __launch_bounds__(PQ_THREADS, 4) void pq_att1_kernel(PqArgs p, int begin) {
+    typedef PqTile<WT, D, DH> TL;
+    __shared__ __attribute__((aligned(16))) char smem[TL::ATT1_BYTES];
+    const PqTask k = pq_decode<D / DH>(p, begin + (int)blockIdx.x);
+    task_att<WT, D, DH, false>(p, k.l, k.b, k.h, k.t, k.s, smem, threadIdx.x);
+}
+
 template <class WT, int D, int DH>
 hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     typedef PqTile<WT, D, DH> TL;
@@ -918,7 +930,13 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     hipError_t e;
     if ((e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     for (int l = 0; l < a.n_layers; l++) {
-        if ((e = stage(n_att)) != hipSuccess) return e;
+        if (l > 0) {
+            hipLaunchKernelGGL((pq_att1_kernel<WT, D, DH>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
+            begin += n_att;
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else if ((e = stage(n_att)) != hipSuccess) {
+            return e;
+        }
         if ((e = stage(BNT)) != hipSuccess) return e;
         if (l + 1 < a.n_layers && (e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     }
