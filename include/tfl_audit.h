@@ -27,8 +27,9 @@ extern "C" {
  * scored per 16-query wave by the layer-wise attention kernels (slots 0, 1),
  * 32-key chunks scored per 16-query wave by the fused SEQ kernel (slot 2),
  * key tiles staged per task and scored per wave by the PQ attention tasks
- * (slots 3, 4), and the layer-wise attention workgroups that took the hi/lo
- * split scores (slot 5) or reference-free bounded weights (slot 6).  The
+ * (slots 3, 4), and the layer-wise attention workgroups and PQ attention
+ * tasks that took the hi/lo split scores (slot 5) or reference-free bounded
+ * weights (slot 6).  The
  * small fused kernel scores key by key (no tiles) and adds nothing. */
 enum { TFL_AUDIT_SLOTS = 8 };
 

@@ -40,8 +40,8 @@ enum AuditSlot {
     AUD_SEQ_WAVE = 2,    // fused SEQ kernel: 32-key chunks scored per 16-query wave
     AUD_PQ_WG = 3,       // PQ attention tasks: key tiles staged per task
     AUD_PQ_WAVE = 4,     // PQ attention tasks: key tiles scored per 16-query wave
-    AUD_SPLIT_WG = 5,    // layer-wise attention: workgroups that took the split scores
-    AUD_BOUNDED_WG = 6,  // layer-wise attention: workgroups whose weights need no reference
+    AUD_SPLIT_WG = 5,    // layer-wise attention workgroups / PQ attention tasks that took the split scores
+    AUD_BOUNDED_WG = 6,  // the same whose weights need no reference
     AUD_SLOTS = 8
 };
 __device__ __forceinline__ void audit_add(unsigned long long* ctr, int slot, unsigned long long v) {

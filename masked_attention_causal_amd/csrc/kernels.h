@@ -113,6 +113,10 @@ struct PqArgs {
     // with fp16 I/O, else converted once per forward; with fp32 I/O each is
     // followed by its lo plane (rounding remainder times 2^11)
     const _Float16* wh[SEQ_MAX_LAYERS][4];
+    // [B H][NT] per (sequence, head) and 64-row tile bounds on the largest
+    // row norm of the current layer's Q and K (written by the QKV tasks):
+    // each attention task's score variant
+    float2* qk_stats;
 };
 
 // Fused row kernel of the layer-wise path (16-bit I/O, d in {64, 128, 256}):

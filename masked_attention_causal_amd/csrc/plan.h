@@ -26,7 +26,7 @@ struct Plan {
     // PQ path: key tiles per split, (tile, split) pairs per (sequence, head),
     // tasks, and workspace offsets
     int pq_ks, pq_ctot, pq_tasks;
-    size_t off_pX, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML, off_pW;
+    size_t off_pX, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML, off_pW, off_pS;
     size_t ws_bytes;
 };
 

@@ -247,7 +247,8 @@ struct PqTile {
     static constexpr int VLDT = PQ_RT + 8;              // V^T staging row pitch
     static constexpr int NB = D / 64;                   // 16-feature blocks per wave for D outputs
     static constexpr int QNB = (3 * D / 4) % 32 == 0 ? 2 : 1;   // blocks per QKV pass
-    static constexpr int QPASS = (3 * D / 4) / (16 * QNB);     // QKV passes per wave
+    static constexpr int QPASS = (3 * D / 4) / (16 * QNB);     // QKV passes per wave (all of Q, K, V)
+    static constexpr int PPW = (D / 4) / (16 * QNB);           // QKV passes per wave of one part (Q, K or V)
     static constexpr int ACT_BYTES = PQ_RT * ALD * 2;
     static constexpr int G_BYTES = 2 * PQ_RT * GLD * 2;
     static constexpr int VT_BYTES = D * VLDT * 2;
@@ -265,21 +266,23 @@ struct PqTile {
 };
 
 // ------------------------------------------------------------------ QKV epilogue
-// One pass of QNB feature blocks starting at global QKV feature n0 (0..3D):
-// adds the bias, sends q and k rows to the head-major fp16 buffers (hi, and
-// lo when `lo_parts`), and v into the LDS V^T staging area.
-template <class WT, int D, int DH, int QNB, bool DIRECT_VT>
+// One pass of QNB feature blocks of a QKV part's output (`which` 0: Q, 1: K,
+// 2: V), from feature nn0 of it: adds the bias; q and k rows go to the
+// head-major fp16 buffers (hi, and lo when `lo_parts`) and the sums of squares
+// of their hi values to ss (per row of the lane, rows past L add nothing); v
+// goes to the LDS V^T staging area.
+template <class WT, int D, int DH, int QNB>
 __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqArgs& p, int layer, bool lo_parts,
-                                          int b, int t, int n0, f16* vts, int c16, int g) {
+                                          int b, int t, int which, int nn0, f16* vts, float (&ss)[4], int c16,
+                                          int g) {
     constexpr int H = D / DH;
-    const WT* bias = (const WT*)p.lw[layer].b_qkv;
+    const WT* bias = (const WT*)p.lw[layer].b_qkv + which * D;
     const size_t TD = (size_t)p.B * p.L * D;
 #pragma unroll
     for (int nb = 0; nb < QNB; nb++) {
-        const int n = n0 + 16 * nb + 4 * g;             // first of four consecutive features
+        const int nn = nn0 + 16 * nb + 4 * g;           // first of four consecutive features
         float bv[4];
-        load4_f32(bias + n, bv);
-        const int which = n / D, nn = n - which * D;
+        load4_f32(bias + nn, bv);
         const int h = nn / DH, dd = nn - h * DH;
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) {
@@ -288,27 +291,20 @@ __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqAr
 #pragma unroll
             for (int e = 0; e < 4; e++) v[e] = acc[nb][rb][e] + bv[e];
             if (which == 2) {
-                if constexpr (DIRECT_VT) {
-                    // straight to the layer's V^T rows (columns past L hold
-                    // the bias of zero rows: finite, and masked as keys)
-                    f16* vt = p.Vt + (size_t)layer * p.B * D * p.Lp + (((size_t)b * H + h) * DH + dd) * p.Lp + pos;
+                // rows past L hold the bias of zero rows: finite, and masked as keys
 #pragma unroll
-                    for (int e = 0; e < 4; e++) vt[(size_t)e * p.Lp] = (f16)v[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
-                }
+                for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
             } else if (pos < p.L) {
-                const size_t off = (size_t)layer * TD + (((size_t)b * H + h) * p.L + pos) * DH + dd;
-                f16* hi = (which == 0 ? p.Qh : p.Kh) + off;
+                const size_t off = (((size_t)b * H + h) * p.L + pos) * DH + dd;
                 f16x4 hv, lv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     hv[e] = (f16)v[e];
                     lv[e] = (f16)(v[e] - (float)hv[e]);
+                    ss[rb] = fmaf((float)hv[e], (float)hv[e], ss[rb]);
                 }
-                *(f16x4*)hi = hv;
-                if (lo_parts) *(f16x4*)((which == 0 ? p.Ql : p.Kl) + (off - (size_t)layer * TD)) = lv;
+                *(f16x4*)((which == 0 ? p.Qh : p.Kh) + (size_t)layer * TD + off) = hv;
+                if (lo_parts) *(f16x4*)((which == 0 ? p.Ql : p.Kl) + off) = lv;
             }
         }
     }
@@ -332,51 +328,79 @@ __device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int 
 }
 
 // QKV projection of the 64 rows held in LDS (act; act_lo with fp32 I/O on
-// layer 0): every wave's passes [ps0, ps1) of its output features.  V^T goes
-// through the LDS staging area and one coalesced flush, or (DIRECT_VT, for a
-// task that computes only some of the features) straight to global memory.
-// Caller has synchronised after filling act.
-template <class WT, int D, int DH, bool DIRECT_VT = false>
-__device__ __forceinline__ void qkv_rows(const PqArgs& p, int layer, int b, int t, char* smem, int tid, int ps0 = 0,
-                                         int ps1 = PqTile<WT, D, DH>::QPASS) {
+// layer 0), part `which` of its output: Q, K or V (D features each), wave w
+// computing features [w D/4, (w+1) D/4) of it in PPW passes.  V^T goes through
+// the LDS staging area and one coalesced flush.  Q and K parts also write,
+// per head, an upper bound on the largest row norm of the tile's hi values
+// (sqrt of the largest sum of squares, one ulp up) to the .x (Q) or .y (K)
+// of the layer's qk_stats[(b H + h) NT + t].  Caller has synchronised after
+// filling act.
+template <class WT, int D, int DH>
+__device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int t, int which, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
+    constexpr int QNB = TL::QNB, PPW = TL::PPW, H = D / DH;
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     const f16* act = (const f16*)(smem + TL::OFF_ACT);
     f16* vts = (f16*)(smem + TL::OFF_GV);
+    float* red = (float*)(smem + TL::OFF_RED);   // [D / (16 QNB) chunks][64 rows] sums of squares
     const f16* W = p.wh[layer][0];
     const bool first = layer == 0;
 #pragma unroll 1
-    for (int ps = ps0; ps < ps1; ps++) {
-        const int n0 = wave * (3 * D / 4) + ps * 16 * TL::QNB;
-        f32x4 acc[TL::QNB][4];
+    for (int ps = 0; ps < PPW; ps++) {
+        const int nn0 = wave * (D / 4) + ps * 16 * QNB;   // feature within the part
+        const int n0 = which * D + nn0;                    // QKV output feature
+        f32x4 acc[QNB][4];
 #pragma unroll
-        for (int nb = 0; nb < TL::QNB; nb++)
+        for (int nb = 0; nb < QNB; nb++)
 #pragma unroll
             for (int rb = 0; rb < 4; rb++) acc[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (TL::F32) {
             if (first) {
-                f32x4 lo[TL::QNB][4];
+                f32x4 lo[QNB][4];
 #pragma unroll
-                for (int nb = 0; nb < TL::QNB; nb++)
+                for (int nb = 0; nb < QNB; nb++)
 #pragma unroll
                     for (int rb = 0; rb < 4; rb++) lo[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mm_rows_split<TL::QNB, D>(acc, lo, W, W + (size_t)3 * D * D, D, n0, act,
-                                          (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
+                mm_rows_split<QNB, D>(acc, lo, W, W + (size_t)3 * D * D, D, n0, act,
+                                      (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
 #pragma unroll
-                for (int nb = 0; nb < TL::QNB; nb++)
+                for (int nb = 0; nb < QNB; nb++)
 #pragma unroll
                     for (int rb = 0; rb < 4; rb++) acc[nb][rb] += lo[nb][rb] * (1.0f / 2048.0f);
             } else {
-                mm_rows<TL::QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
+                mm_rows<QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
             }
         } else {
-            mm_rows<TL::QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
+            mm_rows<QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
         }
-        qkv_store<WT, D, DH, TL::QNB, DIRECT_VT>(acc, p, layer, first, b, t, n0, vts, c16, g);
+        float ss[4] = {0.f, 0.f, 0.f, 0.f};
+        qkv_store<WT, D, DH, QNB>(acc, p, layer, first, b, t, which, nn0, vts, ss, c16, g);
+        if (which != 2) {
+            // the pass's 16 QNB features of each row: sum over the four lane groups
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) {
+                ss[rb] += __shfl_xor(ss[rb], 16, WAVE);
+                ss[rb] += __shfl_xor(ss[rb], 32, WAVE);
+                if (g == 0) red[(wave * PPW + ps) * PQ_RT + 16 * rb + c16] = ss[rb];
+            }
+        }
     }
-    if constexpr (!DIRECT_VT) {
-        __syncthreads();
+    __syncthreads();
+    if (which == 2) {
         vt_flush<WT, D, DH>(p, layer, b, t, vts, tid);
+        return;
+    }
+    // passes align with heads (16 QNB divides DH): head h is chunks [h CPH, (h+1) CPH)
+    constexpr int CPH = DH / (16 * QNB);
+    for (int h = wave; h < H; h += PQ_THREADS / 64) {
+        float sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPH; c++) sq += red[(h * CPH + c) * PQ_RT + lane];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sq = fmaxf(sq, __shfl_xor(sq, o, WAVE));
+        if (lane == 0)
+            ((float*)(p.qk_stats + ((size_t)b * H + h) * p.NT + t))[which] =
+                __uint_as_float(__float_as_uint(sqrtf(sq)) + 1u);
     }
 }
 
@@ -419,12 +443,13 @@ __device__ void task_qkv(const PqArgs& p, int layer, int b, int t, int part, cha
         }
     }
     __syncthreads();
-    constexpr int QP = TL::QPASS / PQ_QKV_PARTS;
-    static_assert(QP * PQ_QKV_PARTS == TL::QPASS, "QKV passes split evenly over the parts");
-    qkv_rows<WT, D, DH, true>(p, layer, b, t, smem, tid, part * QP, (part + 1) * QP);
+    qkv_part<WT, D, DH>(p, layer, b, t, part, smem, tid);
 }
 
-template <class WT, int D, int DH, bool SPLIT>
+// BOUNDED: every score of this (sequence, head) is within +-14 in exp2 units
+// (pq_variant), so the weights 2^s take no reference: no running max, no
+// rescaling; the partial state carries m = 0 (or -inf when no key was seen).
+template <class WT, int D, int DH, bool SPLIT, bool BOUNDED>
 __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
     constexpr int KT = 64, KLD = TL::KLD, VLD = TL::VLD, ND = DH / 16, QK = DH / 32;
@@ -553,16 +578,21 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                             if (key > myq || key >= len) v = -INFINITY;
                         }
                         sc[kb][e] = v;
-                        mx = fmaxf(mx, v);
+                        if constexpr (!BOUNDED) mx = fmaxf(mx, v);
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                const float m_new = fmaxf(m_run, mx);
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                // hardware exp2: its flushing below 2^-126 is far below the fp16
-                // rounding of the weights and next to a row sum >= 1
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-                m_run = m_new;
+                float m_use = 0.f, alpha = 1.f;
+                if constexpr (BOUNDED) {
+                    m_run = 0.f;
+                } else {
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                    const float m_new = fmaxf(m_run, mx);
+                    m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    // hardware exp2: its flushing below 2^-126 is far below the fp16
+                    // rounding of the weights and next to a row sum >= 1
+                    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                    m_run = m_new;
+                }
                 float ls = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; kb++)
@@ -572,9 +602,13 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                         sc[kb][e] = pv;
                         ls += pv;
                     }
-                l_run = l_run * alpha + ls;
+                if constexpr (BOUNDED) {
+                    l_run += ls;
+                } else {
+                    l_run = l_run * alpha + ls;
 #pragma unroll
-                for (int db = 0; db < ND; db++) o[db] *= alpha;
+                    for (int db = 0; db < ND; db++) o[db] *= alpha;
+                }
 #pragma unroll
                 for (int cc = 0; cc < 2; cc++) {
                     f16x8 pb;
@@ -883,18 +917,15 @@ __device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
 
 template <class WT, int D, int DH>
 __device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* smem, int tid) {
+    // attention stages run in pq_att_kernel
     if (k.kind == 0)
         task_qkv<WT, D, DH>(p, k.l, k.b, k.t, k.s, smem, tid);
-    else if (k.kind == 1 && k.l == 0)
-        task_att<WT, D, DH, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
-    else if (k.kind == 1)
-        task_att<WT, D, DH, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
-    else
+    else if (k.kind == 2)
         task_row<WT, D, DH>(p, k.l, k.b, k.t, smem, tid);
 }
 
-// One launch per stage of the task list (QKV0, then ATT and ROW of every
-// layer), workgroup i running task begin + i.  Every dependency of a stage
+// One launch per stage of the task list (QKV, ATT and ROW of every layer),
+// workgroup i running task begin + i.  Every dependency of a stage
 // was completed by an earlier launch on the stream, so no workgroup ever
 // waits on another.
 template <class WT, int D, int DH>
@@ -905,15 +936,53 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int b
     pq_run<WT, D, DH>(p, k, smem, threadIdx.x);
 }
 
-// Attention stages of the later layers (single fp16 scores) in a kernel of
-// their own: LDS for K and V only and registers for four workgroups per CU,
-// so the stage's (tile, split) tasks run in one round.
-template <class WT, int D, int DH>
-__global__ __launch_bounds__(PQ_THREADS, 4) void pq_att1_kernel(PqArgs p, int begin) {
+// Score variant of an attention task's (sequence, head) from the row-norm
+// maxima of its Q and K hi planes (qk_stats, formed after every QKV stage):
+// the first layer takes the hi/lo split only where the bound on a single fp16
+// pass's score error, (2u + u^2)|q||k|c with u = 2^-11, exceeds 2^-8 in exp2
+// units; bounded when every score is within +-14 in exp2 units (|q||k|c,
+// times 1 + 2^-9 for the lo parts), so the weights 2^s need no reference.
+__device__ __forceinline__ void pq_variant(const PqArgs& p, int bh, int layer, bool& split, bool& bounded) {
+    const float2* st = p.qk_stats + (size_t)bh * p.NT;
+    float mq = 0.f, mk = 0.f;
+    for (int i = (int)(threadIdx.x & 63); i < p.NT; i += 64) {
+        mq = fmaxf(mq, st[i].x);
+        mk = fmaxf(mk, st[i].y);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, o, WAVE));
+        mk = fmaxf(mk, __shfl_xor(mk, o, WAVE));
+    }
+    const float qk = mq * mk * p.scale_log2;
+    split = layer == 0 && !((0.0009765625f + 2.384185791015625e-07f) * qk <= 0.00390625f);  // NaN or inf: split
+    bounded = qk * 1.001953125f <= 14.f;
+}
+
+// Attention stages in kernels of their own: LDS for K (and, in the first
+// layer, its lo planes) and V only, and registers for four workgroups per CU
+// after the first layer, so a stage's (tile, split) tasks run in one round.
+template <class WT, int D, int DH, bool FIRST>
+__global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArgs p, int begin) {
     typedef PqTile<WT, D, DH> TL;
-    __shared__ __attribute__((aligned(16))) char smem[TL::ATT1_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[FIRST ? TL::ATT_BYTES : TL::ATT1_BYTES];
     const PqTask k = pq_decode<D / DH>(p, begin + (int)blockIdx.x);
-    task_att<WT, D, DH, false>(p, k.l, k.b, k.h, k.t, k.s, smem, threadIdx.x);
+    bool split, bounded;
+    pq_variant(p, k.b * (D / DH) + k.h, k.l, split, bounded);
+    const int tid = threadIdx.x;
+    if constexpr (MASK_ALL) {
+        if (tid == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
+        if (tid == 0 && bounded) audit_add(p.audit, AUD_BOUNDED_WG, 1);
+    }
+    if (FIRST && split) {
+        if constexpr (FIRST) {
+            if (bounded) task_att<WT, D, DH, true, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+            else task_att<WT, D, DH, true, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+        }
+    } else {
+        if (bounded) task_att<WT, D, DH, false, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+        else task_att<WT, D, DH, false, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+    }
 }
 
 template <class WT, int D, int DH>
@@ -930,13 +999,12 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     hipError_t e;
     if ((e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     for (int l = 0; l < a.n_layers; l++) {
-        if (l > 0) {
-            hipLaunchKernelGGL((pq_att1_kernel<WT, D, DH>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
-            begin += n_att;
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else if ((e = stage(n_att)) != hipSuccess) {
-            return e;
-        }
+        if (l == 0)
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
+        else
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
+        begin += n_att;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = stage(BNT)) != hipSuccess) return e;
         if (l + 1 < a.n_layers && (e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     }

@@ -116,6 +116,7 @@ def test_pq_workspace_layout():
     weights = n_layers * (4 * d * d + 2 * d * f) * 2 * 2     # fp16 hi and lo planes of every GEMM weight
     need = (up(T * d * 4) + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
             + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8)
+            + up(B * H * NT * 8)                                 # per (sequence, head, tile) Q/K norm bounds
             + up(weights))
     assert ws == need
     # fp16 I/O reads the given weights: no planes

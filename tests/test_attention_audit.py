@@ -30,8 +30,9 @@ pytestmark = pytest.mark.gpu
 
 W = synth.Workload
 SLOTS = {"tiled_wg": 0, "tiled_wave": 1, "seq_wave": 2, "pq_wg": 3, "pq_wave": 4, "split_wg": 5, "bounded_wg": 6}
-# per-workgroup score-variant counts of the layer-wise kernels (checked by
-# test_score_variant_follows_magnitude, not by the tile-count test)
+# per-workgroup score-variant counts of the layer-wise and PQ attention
+# (checked by test_score_variant_follows_magnitude and
+# test_pq_score_variant_follows_magnitude, not by the tile-count test)
 VARIANT_SLOTS = {"split_wg", "bounded_wg"}
 
 
@@ -128,7 +129,7 @@ def test_mask_every_tile_is_bit_identical_and_tiles_match(w, path, lens):
     say(f"[audit] {w.name}: counted {got[:5].tolist()} expected {want}")
     for slot, n in want.items():
         assert int(got[SLOTS[slot]]) == n, (slot, int(got[SLOTS[slot]]), n)
-    for slot in set(SLOTS) - set(want) - (VARIANT_SLOTS if path == "tiled" else set()):
+    for slot in set(SLOTS) - set(want) - (VARIANT_SLOTS if path in ("tiled", "pq") else set()):
         assert got[SLOTS[slot]] == 0, slot
 
 
@@ -184,4 +185,35 @@ def test_score_variant_follows_magnitude(dh):
         got = counters.cpu().numpy()
         assert int(got[SLOTS["split_wg"]]) == want_split, (scale, got.tolist())
         assert int(got[SLOTS["bounded_wg"]]) == want_bounded, (scale, got.tolist())
+        assert_gate(y, oracle_forward(inp), f"{w.name} scale {scale}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_pq_score_variant_follows_magnitude(dtype):
+    """The PQ attention tasks pick their score variant as the layer-wise
+    kernels do, from the row-norm maxima of their (sequence, head), formed
+    for every layer: split only in the first layer and only where a single
+    fp16 pass's score error bound exceeds 2^-8; bounded where every score is
+    within +-14 in exp2 units.  Every layer has the same N attention tasks.
+    Scale 1: no task splits, all 2N are bounded.  Scale 1e3: the N
+    first-layer tasks split and are not bounded, the N second-layer tasks
+    (LayerNorm-bounded input) are bounded.  The outputs meet the gate."""
+    import torch
+
+    import masked_attention_causal_amd as tfl
+    from tests.gate import assert_gate, oracle_forward
+    w = W(f"a_pq_adapt_{dtype}", 2, 128, 2, 512, 2, 900, dtype, 1, 900, 1.0)
+    n_att = None
+    for scale in (1.0, 1e3):
+        inp = synth.make_inputs(w, 11, scale=scale)
+        counters = torch.zeros(8, dtype=torch.int64, device="cuda")
+        say(f"[audit variant] {w.name} scale={scale}")
+        y = run(inp, "pq", tfl.AUDIT_LIB_PATH, counters)
+        got = counters.cpu().numpy()
+        split, bounded = int(got[SLOTS["split_wg"]]), int(got[SLOTS["bounded_wg"]])
+        if scale == 1.0:
+            assert split == 0 and bounded > 0 and bounded % 2 == 0, got.tolist()
+            n_att = bounded // 2
+        else:
+            assert split == n_att and bounded == n_att, (n_att, got.tolist())
         assert_gate(y, oracle_forward(inp), f"{w.name} scale {scale}")
