@@ -86,9 +86,11 @@ struct SeqArgs {
 
 // QKV tasks per 64-row tile and layer on the PQ path.
 constexpr int PQ_QKV_PARTS = 3;
+constexpr int PQ_FS_MAX = 4;   // PQ FFN tasks per 64-row tile, at most
 
-// PQ path: the stack as a task list over 64-row tiles (layer-0 QKV
-// projection, split-K attention, fused row tasks), run as one launch per
+// PQ path: the stack as a task list over 64-row tiles (QKV projection,
+// split-K attention, out-projection + LayerNorm, FFN parts; the LayerNorm
+// after the FFN runs where the rows are next loaded), run as one launch per
 // stage of the list.
 struct PqArgs {
     const void* x;   // [B, L, d] I/O dtype
@@ -100,6 +102,9 @@ struct PqArgs {
     float eps;
     float scale_log2;
     float* X;        // [B*L, d] fp32 residual stream between layers
+    float* X1;       // [B*L, d] fp32 rows after attention + LayerNorm
+    float* FP;       // [FS][B*L, d] fp32 FFN down-projection partials
+    int FS;          // FFN tasks per tile (each F / FS hidden features)
     _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 (hi part for layer 0)
     _Float16* Kh;
     _Float16* Ql;    // [B, H, L, dh] fp16 lo parts of layer 0

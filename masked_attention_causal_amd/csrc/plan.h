@@ -25,8 +25,8 @@ struct Plan {
     int n_wconv;
     // PQ path: key tiles per split, (tile, split) pairs per (sequence, head),
     // tasks, and workspace offsets
-    int pq_ks, pq_ctot, pq_tasks;
-    size_t off_pX, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML, off_pW, off_pS;
+    int pq_ks, pq_ctot, pq_tasks, pq_fs;
+    size_t off_pX, off_pX1, off_pFP, off_Qh, off_Kh, off_Ql, off_Kl, off_pVt, off_Op, off_ML, off_pW, off_pS;
     size_t ws_bytes;
 };
 

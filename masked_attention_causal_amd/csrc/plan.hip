@@ -123,7 +123,14 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         q.pq_ks = 8;
         q.pq_ctot = NT + q.pq_ks * (NT / q.pq_ks) * (NT / q.pq_ks - 1) / 2 + (NT / q.pq_ks) * (NT % q.pq_ks);
         const long n_att = (long)q.B * q.H * q.pq_ctot;
-        const long n_tasks = (long)PQ_QKV_PARTS * BNT * q.n_layers + (long)q.n_layers * (n_att + BNT);
+        // FFN tasks per tile: a divisor of the F/128 hidden chunks, up to 4,
+        // so the FFN stage has about one workgroup per CU
+        const int nch = q.f / 128;
+        int fs = 1;
+        for (int c = 1; c <= PQ_FS_MAX && c <= nch; c++)
+            if (nch % c == 0 && (long)BNT * c <= 256) fs = c;
+        q.pq_fs = fs;
+        const long n_tasks = (long)q.n_layers * ((PQ_QKV_PARTS + 1 + fs) * (long)BNT + n_att) + BNT;
         if (n_tasks > INT_MAX / 2) {
             *why = "too many tasks for the PQ path";
             return TFL_E_UNSUPPORTED;
@@ -132,6 +139,8 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         const size_t slots = (size_t)n_att;
         size_t o = 0;
         q.off_pX = o;  o += up256(Td * 4);
+        q.off_pX1 = o; o += up256(Td * 4);
+        q.off_pFP = o; o += up256(Td * 4 * fs);
         q.off_Qh = o;  o += up256(Td * 2 * q.n_layers);
         q.off_Kh = o;  o += up256(Td * 2 * q.n_layers);
         q.off_Ql = o;  o += up256(Td * 2);
@@ -145,7 +154,8 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         if (q.mode != MODE_F16)
             o += up256(((size_t)4 * q.d * q.d + (size_t)2 * q.d * q.f) * q.n_layers * (q.mode == MODE_F32 ? 4 : 2));
         q.ws_bytes = o;
-        std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d/staged/%s", q.pq_ks, q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
+        std::snprintf(q.name, sizeof(q.name), "PQ/t64.ks%d.fs%d/staged/%s", q.pq_ks, q.pq_fs,
+                      q.mode == MODE_F32 ? "f32io.f16op" : "f16op");
         *p = q;
         return TFL_OK;
     }
@@ -414,6 +424,9 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
     a.eps = P.eps;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
     a.X = (float*)(ws + P.off_pX);
+    a.X1 = (float*)(ws + P.off_pX1);
+    a.FP = (float*)(ws + P.off_pFP);
+    a.FS = P.pq_fs;
     a.Qh = (_Float16*)(ws + P.off_Qh);
     a.Kh = (_Float16*)(ws + P.off_Kh);
     a.Ql = (_Float16*)(ws + P.off_Ql);

@@ -6,23 +6,24 @@
 // tasks sized so that every compute unit has work).
 //
 // Task list (64-row tiles of one sequence; t = tile, s = key split):
-//   QKV(l,b,t,part)     layer-l projection of the tile's rows (x for l = 0,
-//                       the residual stream after that), in PQ_QKV_PARTS
-//                       tasks per tile (each a third of every wave's output
-//                       features), so the stage has three times the tiles'
-//                       workgroups
+//   QKV(l,b,t,part)     layer-l projection of the tile's rows (x for l = 0;
+//                       after that the previous layer's output rows, formed
+//                       here: LayerNorm of X1 + bias + FFN partials), in
+//                       PQ_QKV_PARTS tasks per tile (Q, K, V), so the stage has
+//                       three times the tiles' workgroups
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
-//   ROW(l,b,t)          merge of the partials, out-projection + residual +
-//                       LayerNorm, FFN (exact-erf GELU) + residual +
-//                       LayerNorm, written to the residual stream (or y after
-//                       the last layer)
-// The list runs as one launch per stage (QKV, ATT and ROW of every layer),
-// workgroup i of a stage running its task i; each stage depends only on
-// earlier launches on the stream.  The pages' single persistent launch
-// (workgroups popping task ids from a device queue and waiting on dependency
-// counters) is not offered: its one run on the GPU did not finish, and no
-// cause has been shown.
+//   ROWA(l,b,t)         merge of the partials, out-projection + residual +
+//                       LayerNorm -> X1
+//   FFN(l,b,t,cg)       FS tasks per tile, each F/FS hidden features:
+//                       up-projection + GELU, and its share of the
+//                       down-projection as an fp32 partial
+//   FIN(b,t)            the last layer's output rows (as in QKV) to y
+// The list runs as one launch per stage, workgroup i of a stage running its
+// task i; each stage depends only on earlier launches on the stream.  The
+// pages' single persistent launch (workgroups popping task ids from a device
+// queue and waiting on dependency counters) is not offered: its one run on
+// the GPU did not finish, and no cause has been shown.
 //
 // Splitting one query tile's keys over several tasks and combining the
 // partial softmax states (m, l, O) exactly is the split-K attention of
@@ -406,6 +407,68 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
 
 // ------------------------------------------------------------------ tasks
 
+// Rows of tile t at the end of layer lp: LayerNorm (ln2) of X1 + b_2 + the
+// FS down-projection partials.  Eight features per lane, a row over D/8
+// consecutive lanes of one wave; emit(r, pos, k, v) for every row r of the
+// tile (rows past L are formed from zeros; the caller drops them).
+template <class WT, int D, class Emit>
+__device__ __forceinline__ void ffn_out_rows(const PqArgs& p, int lp, int b, int t, int tid, Emit emit) {
+    constexpr int TPR = D / 8, RPI = PQ_THREADS / TPR;
+    static_assert(TPR <= WAVE && RPI * TPR == PQ_THREADS, "a row within one wave");
+    const LayerPtrs& w = p.lw[lp];
+    const size_t TD = (size_t)p.B * p.L * D;
+    const int k = (tid % TPR) * 8;
+    float bb[8], gm[8], bt[8];
+    load4_f32((const WT*)w.b_2 + k, *reinterpret_cast<float(*)[4]>(&bb[0]));
+    load4_f32((const WT*)w.b_2 + k + 4, *reinterpret_cast<float(*)[4]>(&bb[4]));
+    load4_f32((const WT*)w.ln2_g + k, *reinterpret_cast<float(*)[4]>(&gm[0]));
+    load4_f32((const WT*)w.ln2_g + k + 4, *reinterpret_cast<float(*)[4]>(&gm[4]));
+    load4_f32((const WT*)w.ln2_b + k, *reinterpret_cast<float(*)[4]>(&bt[0]));
+    load4_f32((const WT*)w.ln2_b + k + 4, *reinterpret_cast<float(*)[4]>(&bt[4]));
+#pragma unroll
+    for (int i = 0; i < PQ_RT / RPI; i++) {
+        const int r = tid / TPR + i * RPI, pos = t * PQ_RT + r;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (pos < p.L) {
+            const size_t off = ((size_t)b * p.L + pos) * D + k;
+            const float4 x0 = *(const float4*)(p.X1 + off), x1 = *(const float4*)(p.X1 + off + 4);
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+#pragma unroll
+            for (int e = 0; e < 8; e++) v[e] += bb[e];
+            // every partial's loads in flight together (FS <= PQ_FS_MAX)
+            float4 a[PQ_FS_MAX][2];
+#pragma unroll
+            for (int c = 0; c < PQ_FS_MAX; c++)
+                if (c < p.FS) {
+                    a[c][0] = *(const float4*)(p.FP + c * TD + off);
+                    a[c][1] = *(const float4*)(p.FP + c * TD + off + 4);
+                }
+#pragma unroll
+            for (int c = 0; c < PQ_FS_MAX; c++)
+                if (c < p.FS) {
+                    v[0] += a[c][0].x; v[1] += a[c][0].y; v[2] += a[c][0].z; v[3] += a[c][0].w;
+                    v[4] += a[c][1].x; v[5] += a[c][1].y; v[6] += a[c][1].z; v[7] += a[c][1].w;
+                }
+        }
+        float sm = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sm += __shfl_xor(sm, o, WAVE);
+        const float mean = sm * (1.0f / D);
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) sq = fmaf(v[e] - mean, v[e] - mean, sq);
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
+        const float rs = 1.0f / sqrtf(sq * (1.0f / D) + p.eps);
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) out[e] = (v[e] - mean) * rs * gm[e] + bt[e];
+        emit(r, pos, k, out);
+    }
+}
+
+
 template <class WT, int D, int DH>
 __device__ void task_qkv(const PqArgs& p, int layer, int b, int t, int part, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
@@ -413,34 +476,48 @@ __device__ void task_qkv(const PqArgs& p, int layer, int b, int t, int part, cha
     f16* act_lo = (f16*)(smem + TL::OFF_ACT2);
     const WT* x = (const WT*)p.x;
     constexpr int CH = PQ_RT * D / 8;
+    if (layer == 0) {
 #pragma unroll
-    for (int i = 0; i < CH / PQ_THREADS; i++) {
-        const int c = tid + i * PQ_THREADS;
-        const int r = c / (D / 8), k = (c % (D / 8)) * 8;
-        const int pos = t * PQ_RT + r;
-        const bool ok = pos < p.L;
-        const WT* src = x + ((size_t)b * p.L + pos) * D + k;
-        if (layer > 0) {
-            // the residual stream the previous layer's row task wrote (rows
-            // past L: zeros, they only feed masked keys and unstored rows)
-            *(f16x8*)(act + r * TL::ALD + k) = ok ? load8_as_f16(p.X + ((size_t)b * p.L + pos) * D + k) : f16x8{};
-        } else if constexpr (TL::F32) {
-            f16x8 hi = {}, lo = {};
-            if (ok) {
-                const float4 a = *(const float4*)src, c2 = *(const float4*)(src + 4);
-                const float v[8] = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
+        for (int i = 0; i < CH / PQ_THREADS; i++) {
+            const int c = tid + i * PQ_THREADS;
+            const int r = c / (D / 8), k = (c % (D / 8)) * 8;
+            const int pos = t * PQ_RT + r;
+            const bool ok = pos < p.L;
+            const WT* src = x + ((size_t)b * p.L + pos) * D + k;
+            if constexpr (TL::F32) {
+                f16x8 hi = {}, lo = {};
+                if (ok) {
+                    const float4 a = *(const float4*)src, c2 = *(const float4*)(src + 4);
+                    const float v[8] = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const f16 h = (f16)v[e];
-                    hi[e] = h;
-                    lo[e] = (f16)((v[e] - (float)h) * 2048.0f);
+                    for (int e = 0; e < 8; e++) {
+                        const f16 h = (f16)v[e];
+                        hi[e] = h;
+                        lo[e] = (f16)((v[e] - (float)h) * 2048.0f);
+                    }
                 }
+                *(f16x8*)(act + r * TL::ALD + k) = hi;
+                *(f16x8*)(act_lo + r * TL::ALD + k) = lo;
+            } else {
+                *(f16x8*)(act + r * TL::ALD + k) = ok ? load8_as_f16(src) : f16x8{};
             }
-            *(f16x8*)(act + r * TL::ALD + k) = hi;
-            *(f16x8*)(act_lo + r * TL::ALD + k) = lo;
-        } else {
-            *(f16x8*)(act + r * TL::ALD + k) = ok ? load8_as_f16(src) : f16x8{};
         }
+    } else {
+        // the previous layer's output rows (its LayerNorm after the FFN);
+        // the Q part also keeps them as the residual stream X.  Rows past L:
+        // zeros, they only feed masked keys and unstored rows.
+        ffn_out_rows<WT, D>(p, layer - 1, b, t, tid, [&](int r, int pos, int k, const float (&v)[8]) {
+            const bool ok = pos < p.L;
+            f16x8 h;
+#pragma unroll
+            for (int e = 0; e < 8; e++) h[e] = ok ? (f16)v[e] : (f16)0.f;
+            *(f16x8*)(act + r * TL::ALD + k) = h;
+            if (part == 0 && ok) {
+                float* xr = p.X + ((size_t)b * p.L + pos) * D + k;
+                *(float4*)xr = float4{v[0], v[1], v[2], v[3]};
+                *(float4*)(xr + 4) = float4{v[4], v[5], v[6], v[7]};
+            }
+        });
     }
     __syncthreads();
     qkv_part<WT, D, DH>(p, layer, b, t, part, smem, tid);
@@ -658,24 +735,46 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
         for (int i = 0; i < QD; i++) acc[i] = 0.f;
         if (pos < p.L) {
             const size_t slot0 = ((size_t)b * H + h) * p.Ctot + pb;
-            float M = -INFINITY;
+            // splits in batches of MB whose loads are all in flight together,
+            // combined with a running maximum (rescaling what came before)
+            constexpr int MB = 4;
+            float M = -INFINITY, lsum = 0.f;
 #pragma unroll 1
-            for (int s = 0; s < ns; s++) M = fmaxf(M, p.ML[(slot0 + s) * PQ_RT + r].x);
-            float lsum = 0.f;
-#pragma unroll 1
-            for (int s = 0; s < ns; s++) {
-                const float2 ml = p.ML[(slot0 + s) * PQ_RT + r];
-                if (ml.x == -INFINITY) continue;
-                const float w = __builtin_amdgcn_exp2f(ml.x - M);
-                lsum += w * ml.y;
-                const float* op = p.Op + ((slot0 + s) * PQ_RT + r) * DH + qd;
+            for (int s0 = 0; s0 < ns; s0 += MB) {
+                float2 ml[MB];
+                float4 ov[MB][QD / 4];
 #pragma unroll
-                for (int i = 0; i < QD; i += 4) {
-                    const float4 v = *(const float4*)(op + i);
-                    acc[i] += w * v.x;
-                    acc[i + 1] += w * v.y;
-                    acc[i + 2] += w * v.z;
-                    acc[i + 3] += w * v.w;
+                for (int j = 0; j < MB; j++) {
+                    if (s0 + j < ns) {
+                        ml[j] = p.ML[(slot0 + s0 + j) * PQ_RT + r];
+                        const float* op = p.Op + ((slot0 + s0 + j) * PQ_RT + r) * DH + qd;
+#pragma unroll
+                        for (int i = 0; i < QD / 4; i++) ov[j][i] = *(const float4*)(op + 4 * i);
+                    } else {
+                        ml[j] = float2{-INFINITY, 0.f};
+                    }
+                }
+                float mb = M;
+#pragma unroll
+                for (int j = 0; j < MB; j++) mb = fmaxf(mb, ml[j].x);
+                if (mb == -INFINITY) continue;           // no key seen yet
+                const float sc = __builtin_amdgcn_exp2f(M - mb);   // 0 while M = -inf
+                lsum *= sc;
+#pragma unroll
+                for (int i = 0; i < QD; i++) acc[i] *= sc;
+                M = mb;
+#pragma unroll
+                for (int j = 0; j < MB; j++) {
+                    if (ml[j].x == -INFINITY) continue;
+                    const float w = __builtin_amdgcn_exp2f(ml[j].x - M);
+                    lsum += w * ml[j].y;
+#pragma unroll
+                    for (int i = 0; i < QD / 4; i++) {
+                        acc[4 * i] += w * ov[j][i].x;
+                        acc[4 * i + 1] += w * ov[j][i].y;
+                        acc[4 * i + 2] += w * ov[j][i].z;
+                        acc[4 * i + 3] += w * ov[j][i].w;
+                    }
                 }
             }
             const float inv = 1.0f / lsum;
@@ -693,17 +792,15 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
 }
 
 template <class WT, int D, int DH>
-__device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int tid) {
+__device__ void task_rowa(const PqArgs& p, int l, int b, int t, char* smem, int tid) {
     typedef PqTile<WT, D, DH> TL;
     constexpr int NB = TL::NB;
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     f16* act = (f16*)(smem + TL::OFF_ACT);
-    f16* gs = (f16*)(smem + TL::OFF_GV);
     float* red0 = (float*)(smem + TL::OFF_RED);
     float* red1 = red0 + 256;
     const LayerPtrs& w = p.lw[l];
     const int n0 = wave * (D / 4);          // this wave's output features
-    const bool last = l == p.n_layers - 1;
 
     // Up to d = 128 the out-projection's weight fragments are fetched before
     // the merge of the attention partials, so the two memory waits overlap.
@@ -753,19 +850,40 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
         }
     }
     row_layernorm<D, NB>(z, (const WT*)w.ln1_g, (const WT*)w.ln1_b, p.eps, red0, red1, n0, wave, c16, g);
-    // X1: fp16 operand copy in LDS (every wave is past its out-projection
-    // reads: row_sum synchronised) and the fp32 value in this tile's rows of
-    // the residual buffer, read back by the same lanes after the FFN (the
-    // layer input there is no longer needed).
+    // X1 (fp32) to this tile's rows of its buffer, for the FFN tasks and the
+    // residual after the FFN
 #pragma unroll
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) {
-            const int r = 16 * rb + c16, pos = t * PQ_RT + r;
+            const int pos = t * PQ_RT + 16 * rb + c16;
             const float v[4] = {z[nb][rb][0], z[nb][rb][1], z[nb][rb][2], z[nb][rb][3]};
-            store4(act + r * TL::ALD + n0 + 16 * nb + 4 * g, v);
-            if (pos < p.L) store4(p.X + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
+            if (pos < p.L) store4(p.X1 + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
         }
+}
+
+// Part cg of layer l's FFN for the rows of tile t: chunks [cg, cg + 1) F / FS
+// of the hidden features, up-projection + bias + GELU, then that chunk's
+// share of the down-projection, written as an fp32 partial (no bias).
+template <class WT, int D, int DH>
+__device__ void task_ffn(const PqArgs& p, int l, int b, int t, int cg, char* smem, int tid) {
+    typedef PqTile<WT, D, DH> TL;
+    constexpr int NB = TL::NB;
+    constexpr bool PRE = NB <= 2;
+    const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
+    f16* act = (f16*)(smem + TL::OFF_ACT);
+    f16* gs = (f16*)(smem + TL::OFF_GV);
+    const LayerPtrs& w = p.lw[l];
+    const int n0 = wave * (D / 4);          // this wave's output features
+    constexpr int CH = PQ_RT * D / 8;
+#pragma unroll
+    for (int i = 0; i < CH / PQ_THREADS; i++) {
+        const int c = tid + i * PQ_THREADS;
+        const int r = c / (D / 8), k = (c % (D / 8)) * 8;
+        const int pos = t * PQ_RT + r;
+        *(f16x8*)(act + r * TL::ALD + k) =
+            pos < p.L ? load8_as_f16(p.X1 + ((size_t)b * p.L + pos) * D + k) : f16x8{};
+    }
     __syncthreads();
 
     // ---- FFN in chunks of PQ_FC features: G chunk to LDS, then accumulate W2 G^T
@@ -774,14 +892,14 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) y2[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = p.F / PQ_FC;
+    const int nch = p.F / PQ_FC / p.FS;     // chunks of this task: [cg nch, (cg + 1) nch)
     // Up to d = 128 the W2 fragments of a chunk are fetched before its W1
     // products and GELU, so that round trip overlaps them instead of
     // following the barrier (at d = 256 the registers they need would spill).
     constexpr int NBW2 = NB == 1 ? 1 : 2, NH = NB == 1 ? 1 : NB / 2;
     f16x8 a2[PRE ? NH : 1][PQ_FC / 32][NBW2];
 #pragma unroll 1
-    for (int c = 0; c < nch; c++) {
+    for (int c = cg * nch; c < (cg + 1) * nch; c++) {
         f16* gb = gs + (c & 1) * PQ_RT * TL::GLD;
         const int f0 = c * PQ_FC + wave * (PQ_FC / 4);
         if constexpr (PRE) {
@@ -831,109 +949,75 @@ __device__ void task_row(const PqArgs& p, int l, int b, int t, char* smem, int t
             }
         }
     }
-    // ---- + bias + residual (X1), LayerNorm
+    float* fp = p.FP + (size_t)cg * p.B * p.L * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-        float bv[4];
-        load4_f32((const WT*)w.b_2 + n0 + 16 * nb + 4 * g, bv);
+    for (int nb = 0; nb < NB; nb++)
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) {
             const int pos = t * PQ_RT + 16 * rb + c16;
-            float xr[4] = {0.f, 0.f, 0.f, 0.f};
-            if (pos < p.L) load4_f32(p.X + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, xr);
-#pragma unroll
-            for (int e = 0; e < 4; e++) y2[nb][rb][e] += bv[e] + xr[e];
-        }
-    }
-    row_layernorm<D, NB>(y2, (const WT*)w.ln2_g, (const WT*)w.ln2_b, p.eps, red0, red1, n0, wave, c16, g);
-
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-        const int n = n0 + 16 * nb + 4 * g;
-#pragma unroll
-        for (int rb = 0; rb < 4; rb++) {
-            const int r = 16 * rb + c16, pos = t * PQ_RT + r;
             const float v[4] = {y2[nb][rb][0], y2[nb][rb][1], y2[nb][rb][2], y2[nb][rb][3]};
-            if (pos < p.L) {
-                const size_t row = (size_t)b * p.L + pos;
-                if (last)
-                    store4((WT*)p.y + row * D + n, v);
-                else
-                    store4(p.X + row * D + n, v);
-            }
+            if (pos < p.L) store4(fp + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
         }
-    }
+}
+
+// The last layer's output rows of tile t to y.
+template <class WT, int D>
+__device__ void task_fin(const PqArgs& p, int b, int t, int tid) {
+    ffn_out_rows<WT, D>(p, p.n_layers - 1, b, t, tid, [&](int, int pos, int k, const float (&v)[8]) {
+        if (pos < p.L) {
+            WT* yr = (WT*)p.y + ((size_t)b * p.L + pos) * D + k;
+            store4(yr, *reinterpret_cast<const float(*)[4]>(&v[0]));
+            store4(yr + 4, *reinterpret_cast<const float(*)[4]>(&v[4]));
+        }
+    });
 }
 
 // ------------------------------------------------------------------ task list
 
-// Task id -> (kind, layer, sequence, head, tile, split or part).  kind: 0
-// QKV, 1 ATT, 2 ROW.  Order: QKV(0); then per layer ATT, ROW and, before
-// every later layer, its QKV.
-struct PqTask {
-    int kind, l, b, h, t, s;
-};
-template <int H>
-__device__ __forceinline__ PqTask pq_decode(const PqArgs& p, int task) {
-    PqTask k{};
-    const int BNT = p.B * p.NT, NQ = PQ_QKV_PARTS * BNT;
-    auto qkv = [&](int layer, int r) {           // QKV(layer, b, t, part): part-major, then tile-major
-        k.kind = 0;
-        k.l = layer;
-        k.s = r / BNT;
-        r -= k.s * BNT;
-        k.t = r / p.B;
-        k.b = r - k.t * p.B;
-        return k;
-    };
-    if (task < NQ) return qkv(0, task);
-    task -= NQ;
-    const int n_att = p.B * H * p.Ctot;
-    const int seg = n_att + BNT + NQ;            // tasks per layer after QKV(0), the last has no QKV
-    k.l = task / seg;
-    int r = task - k.l * seg;
-    if (r >= n_att + BNT) return qkv(k.l + 1, r - n_att - BNT);
-    if (r < n_att) {                             // ATT(l, b, h, t, s)
-        const int BH = p.B * H;
-        const int pair = r / BH, bh = r - pair * BH;
-        int lo = 0, hi = p.NT - 1;               // tile t with pairs_before(t) <= pair < pairs_before(t+1)
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pq_pairs_before(mid, p.KS) <= pair) lo = mid; else hi = mid - 1;
-        }
-        k.kind = 1;
-        k.t = lo;
-        k.s = pair - pq_pairs_before(lo, p.KS);
-        k.b = bh / H;
-        k.h = bh - k.b * H;
-    } else {                                     // ROW(l, b, t)
-        r -= n_att;
-        k.kind = 2;
-        k.t = r / p.B;
-        k.b = r - k.t * p.B;
-    }
-    return k;
-}
+// Stage kinds (one launch each; a stage's workgroup i runs its task i).
+enum PqStage { PQ_STAGE_QKV = 0, PQ_STAGE_ROWA = 1, PQ_STAGE_FFN = 2, PQ_STAGE_FIN = 3 };
 
+// Every dependency of a stage was completed by an earlier launch on the
+// stream, so no workgroup ever waits on another.
 template <class WT, int D, int DH>
-__device__ __forceinline__ void pq_run(const PqArgs& p, const PqTask& k, char* smem, int tid) {
-    // attention stages run in pq_att_kernel
-    if (k.kind == 0)
-        task_qkv<WT, D, DH>(p, k.l, k.b, k.t, k.s, smem, tid);
-    else if (k.kind == 2)
-        task_row<WT, D, DH>(p, k.l, k.b, k.t, smem, tid);
-}
-
-// One launch per stage of the task list (QKV, ATT and ROW of every layer),
-// workgroup i running task begin + i.  Every dependency of a stage
-// was completed by an earlier launch on the stream, so no workgroup ever
-// waits on another.
-template <class WT, int D, int DH>
-__global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int begin) {
+__global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int kind, int l) {
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
-    const PqTask k = pq_decode<D / DH>(p, begin + (int)blockIdx.x);
-    pq_run<WT, D, DH>(p, k, smem, threadIdx.x);
+    const int i = blockIdx.x, tid = threadIdx.x, BNT = p.B * p.NT;
+    if (kind == PQ_STAGE_QKV) {                  // QKV(l, b, t, part): part-major, then tile-major
+        const int part = i / BNT, r = i - part * BNT, t = r / p.B;
+        task_qkv<WT, D, DH>(p, l, r - t * p.B, t, part, smem, tid);
+    } else if (kind == PQ_STAGE_FFN) {           // FFN(l, b, t, cg): cg fastest, so one XCD sees few chunks
+        const int r = i / p.FS, cg = i - r * p.FS, t = r / p.B;
+        task_ffn<WT, D, DH>(p, l, r - t * p.B, t, cg, smem, tid);
+    } else {
+        const int t = i / p.B, b = i - t * p.B;
+        if (kind == PQ_STAGE_ROWA)
+            task_rowa<WT, D, DH>(p, l, b, t, smem, tid);
+        else
+            task_fin<WT, D>(p, b, t, tid);
+    }
+}
+
+// ATT(l, b, h, t, s) of stage index i: (tile, split) pair-major, then (b, h).
+struct PqAtt {
+    int b, h, t, s;
+};
+template <int H>
+__device__ __forceinline__ PqAtt pq_att_decode(const PqArgs& p, int i) {
+    const int BH = p.B * H;
+    const int pair = i / BH, bh = i - pair * BH;
+    int lo = 0, hi = p.NT - 1;                   // tile t with pairs_before(t) <= pair < pairs_before(t+1)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pq_pairs_before(mid, p.KS) <= pair) lo = mid; else hi = mid - 1;
+    }
+    PqAtt k;
+    k.t = lo;
+    k.s = pair - pq_pairs_before(lo, p.KS);
+    k.b = bh / H;
+    k.h = bh - k.b * H;
+    return k;
 }
 
 // Score variant of an attention task's (sequence, head) from the row-norm
@@ -963,12 +1047,12 @@ __device__ __forceinline__ void pq_variant(const PqArgs& p, int bh, int layer, b
 // layer, its lo planes) and V only, and registers for four workgroups per CU
 // after the first layer, so a stage's (tile, split) tasks run in one round.
 template <class WT, int D, int DH, bool FIRST>
-__global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArgs p, int begin) {
+__global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArgs p, int l) {
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[FIRST ? TL::ATT_BYTES : TL::ATT1_BYTES];
-    const PqTask k = pq_decode<D / DH>(p, begin + (int)blockIdx.x);
+    const PqAtt k = pq_att_decode<D / DH>(p, (int)blockIdx.x);
     bool split, bounded;
-    pq_variant(p, k.b * (D / DH) + k.h, k.l, split, bounded);
+    pq_variant(p, k.b * (D / DH) + k.h, l, split, bounded);
     const int tid = threadIdx.x;
     if constexpr (MASK_ALL) {
         if (tid == 0 && split) audit_add(p.audit, AUD_SPLIT_WG, 1);
@@ -976,12 +1060,12 @@ __global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArg
     }
     if (FIRST && split) {
         if constexpr (FIRST) {
-            if (bounded) task_att<WT, D, DH, true, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
-            else task_att<WT, D, DH, true, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+            if (bounded) task_att<WT, D, DH, true, true>(p, l, k.b, k.h, k.t, k.s, smem, tid);
+            else task_att<WT, D, DH, true, false>(p, l, k.b, k.h, k.t, k.s, smem, tid);
         }
     } else {
-        if (bounded) task_att<WT, D, DH, false, true>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
-        else task_att<WT, D, DH, false, false>(p, k.l, k.b, k.h, k.t, k.s, smem, tid);
+        if (bounded) task_att<WT, D, DH, false, true>(p, l, k.b, k.h, k.t, k.s, smem, tid);
+        else task_att<WT, D, DH, false, false>(p, l, k.b, k.h, k.t, k.s, smem, tid);
     }
 }
 
@@ -990,25 +1074,22 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     typedef PqTile<WT, D, DH> TL;
     static_assert(TL::SMEM <= 160 * 1024, "LDS budget");
     const int BNT = a.B * a.NT, n_att = a.B * (D / DH) * a.Ctot;
-    int begin = 0;
-    auto stage = [&](int n) {
-        hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, begin);
-        begin += n;
+    auto stage = [&](int kind, int l, int n) {
+        hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, kind, l);
         return hipGetLastError();
     };
     hipError_t e;
-    if ((e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
     for (int l = 0; l < a.n_layers; l++) {
+        if ((e = stage(PQ_STAGE_QKV, l, PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
         if (l == 0)
-            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, l);
         else
-            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, begin);
-        begin += n_att;
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, l);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = stage(BNT)) != hipSuccess) return e;
-        if (l + 1 < a.n_layers && (e = stage(PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
+        if ((e = stage(PQ_STAGE_ROWA, l, BNT)) != hipSuccess) return e;
+        if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT)) != hipSuccess) return e;
     }
-    return hipSuccess;
+    return stage(PQ_STAGE_FIN, a.n_layers - 1, BNT);
 }
 
 template <class WT>
