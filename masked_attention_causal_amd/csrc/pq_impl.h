@@ -565,40 +565,39 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     constexpr int VCH = DH * KT / 8;
     constexpr int VPT = VCH / PQ_THREADS;
     static_assert(KPT >= 1 && VPT >= 1, "tile too small");
-    uint4 rk[KPT], rkl[SPLIT ? KPT : 1], rv[VPT];
-    auto gload = [&](int k0) {
+    // K/V tiles are staged through registers: a tile's global loads are
+    // issued two tiles ahead of its use (two register sets, the loop
+    // unrolled by two), so their latency spans two tiles' compute.  V^T rows
+    // are padded to whole 64-key tiles (the columns past L are finite and
+    // masked as keys), so V needs no bounds test.
+    constexpr int NKL = SPLIT ? KPT : 1;
+    f16x8 ka[KPT], kla[NKL], va[VPT], kb_[KPT], klb[NKL], vb[VPT];   // native vectors: plain loads, kept in registers
+    auto gload = [&](int k0, f16x8 (&rk)[KPT], f16x8 (&rkl)[NKL], f16x8 (&rv)[VPT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
             const int c = tid + i * PQ_THREADS, key = c / (DH / 8), col = (c % (DH / 8)) * 8;
             const bool ok = k0 + key < L;
-            rk[i] = ok ? *(const uint4*)(Kg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
-            if constexpr (SPLIT) rkl[i] = ok ? *(const uint4*)(Klg + (size_t)(k0 + key) * DH + col) : uint4{0, 0, 0, 0};
+            rk[i] = ok ? *(const f16x8*)(Kg + (size_t)(k0 + key) * DH + col) : f16x8{};
+            if constexpr (SPLIT) rkl[i] = ok ? *(const f16x8*)(Klg + (size_t)(k0 + key) * DH + col) : f16x8{};
         }
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
             const int c = tid + i * PQ_THREADS, row = c / (KT / 8), kc = (c % (KT / 8)) * 8;
-            const f16* src = Vg + (size_t)row * Lp + k0 + kc;
-            if (k0 + kc + 8 <= L) {
-                rv[i] = *(const uint4*)src;
-            } else {
-                union { uint4 u; f16 e[8]; } tmp;
-#pragma unroll
-                for (int e = 0; e < 8; e++) tmp.e[e] = (k0 + kc + e < L) ? src[e] : (f16)0.f;
-                rv[i] = tmp.u;
-            }
+            rv[i] = *(const f16x8*)(Vg + (size_t)row * Lp + k0 + kc);
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const f16x8 (&rk)[KPT], const f16x8 (&rkl)[NKL], const f16x8 (&rv)[VPT])
+                      __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
             const int c = tid + i * PQ_THREADS, key = c / (DH / 8), col = (c % (DH / 8)) * 8;
-            *(uint4*)&Ks[buf * KT * KLD + key * KLD + col] = rk[i];
-            if constexpr (SPLIT) *(uint4*)&Kls[buf * KT * KLD + key * KLD + col] = rkl[i];
+            *(f16x8*)&Ks[buf * KT * KLD + key * KLD + col] = rk[i];
+            if constexpr (SPLIT) *(f16x8*)&Kls[buf * KT * KLD + key * KLD + col] = rkl[i];
         }
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
             const int c = tid + i * PQ_THREADS, row = c / (KT / 8), kc = (c % (KT / 8)) * 8;
-            *(uint4*)&Vs[buf * DH * VLD + row * VLD + kc] = rv[i];
+            *(f16x8*)&Vs[buf * DH * VLD + row * VLD + kc] = rv[i];
         }
     };
 
@@ -612,96 +611,107 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
         if (tid == 0 && ntl > 0) audit_add(p.audit, AUD_PQ_WG, ntl);
     }
     int n_vis = 0;  // tiles scored by this wave (audit build)
-    if (ntl > 0) {
-        gload(kt0 * KT);
-        sstore(0);
-        __syncthreads();
-#pragma unroll 1
-        for (int it = 0; it < ntl; it++) {
-            const int buf = it & 1;
-            const int k0 = (kt0 + it) * KT;
-            if (it + 1 < ntl) gload(k0 + KT);
-            if (k0 <= qw0 + 15) {
-                if constexpr (MASK_ALL) n_vis++;
-                const f16* ks = Ks + buf * KT * KLD;
-                const f16* kls = Kls + buf * KT * KLD;
-                const f16* vs = Vs + buf * DH * VLD;
-                // S^T = K Q^T; key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
-                f32x4 sc[4];
+    // scores and accumulation of key tile `it` of the split from LDS buffer buf
+    auto tile = [&](int it, int buf) __attribute__((always_inline)) {
+        const int k0 = (kt0 + it) * KT;
+        if (k0 <= qw0 + 15) {
+            if constexpr (MASK_ALL) n_vis++;
+            const f16* ks = Ks + buf * KT * KLD;
+            const f16* kls = Kls + buf * KT * KLD;
+            const f16* vs = Vs + buf * DH * VLD;
+            // S^T = K Q^T; key of (block kb, group g, element e) = (kb/2)*32 + 8g + 4(kb%2) + e
+            f32x4 sc[4];
 #pragma unroll
-                for (int kb = 0; kb < 4; kb++) {
-                    sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int krow = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
+            for (int kb = 0; kb < 4; kb++) {
+                sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int krow = (kb >> 1) * 32 + (c16 >> 2) * 8 + (kb & 1) * 4 + (c16 & 3);
 #pragma unroll
-                    for (int kk = 0; kk < QK; kk++) {
-                        const f16x8 a = *(const f16x8*)&ks[krow * KLD + kk * 32 + g * 8];
-                        sc[kb] = mfma_16x16x32(a, qh[kk], sc[kb]);
-                        if constexpr (SPLIT) {
-                            const f16x8 al = *(const f16x8*)&kls[krow * KLD + kk * 32 + g * 8];
-                            sc[kb] = mfma_16x16x32(al, qh[kk], sc[kb]);
-                            sc[kb] = mfma_16x16x32(a, ql[kk], sc[kb]);
-                        }
-                    }
-                }
-                const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        float v = sc[kb][e] * sl2;
-                        if (need_mask) {
-                            const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
-                            if (key > myq || key >= len) v = -INFINITY;
-                        }
-                        sc[kb][e] = v;
-                        if constexpr (!BOUNDED) mx = fmaxf(mx, v);
-                    }
-                float m_use = 0.f, alpha = 1.f;
-                if constexpr (BOUNDED) {
-                    m_run = 0.f;
-                } else {
-                    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                    const float m_new = fmaxf(m_run, mx);
-                    m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                    // hardware exp2: its flushing below 2^-126 is far below the fp16
-                    // rounding of the weights and next to a row sum >= 1
-                    alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-                    m_run = m_new;
-                }
-                float ls = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const float pv = __builtin_amdgcn_exp2f(sc[kb][e] - m_use);
-                        sc[kb][e] = pv;
-                        ls += pv;
-                    }
-                if constexpr (BOUNDED) {
-                    l_run += ls;
-                } else {
-                    l_run = l_run * alpha + ls;
-#pragma unroll
-                    for (int db = 0; db < ND; db++) o[db] *= alpha;
-                }
-#pragma unroll
-                for (int cc = 0; cc < 2; cc++) {
-                    f16x8 pb;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        pb[e] = (f16)sc[2 * cc][e];
-                        pb[4 + e] = (f16)sc[2 * cc + 1][e];
-                    }
-#pragma unroll
-                    for (int db = 0; db < ND; db++) {
-                        const f16x8 va = *(const f16x8*)&vs[(db * 16 + c16) * VLD + cc * 32 + g * 8];
-                        o[db] = mfma_16x16x32(va, pb, o[db]);
+                for (int kk = 0; kk < QK; kk++) {
+                    const f16x8 a = *(const f16x8*)&ks[krow * KLD + kk * 32 + g * 8];
+                    sc[kb] = mfma_16x16x32(a, qh[kk], sc[kb]);
+                    if constexpr (SPLIT) {
+                        const f16x8 al = *(const f16x8*)&kls[krow * KLD + kk * 32 + g * 8];
+                        sc[kb] = mfma_16x16x32(al, qh[kk], sc[kb]);
+                        sc[kb] = mfma_16x16x32(a, ql[kk], sc[kb]);
                     }
                 }
             }
-            if (it + 1 < ntl) sstore(buf ^ 1);
+            const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    float v = sc[kb][e] * sl2;
+                    if (need_mask) {
+                        const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
+                        if (key > myq || key >= len) v = -INFINITY;
+                    }
+                    sc[kb][e] = v;
+                    if constexpr (!BOUNDED) mx = fmaxf(mx, v);
+                }
+            float m_use = 0.f, alpha = 1.f;
+            if constexpr (BOUNDED) {
+                m_run = 0.f;
+            } else {
+                mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+                const float m_new = fmaxf(m_run, mx);
+                m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                // hardware exp2: its flushing below 2^-126 is far below the fp16
+                // rounding of the weights and next to a row sum >= 1
+                alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                m_run = m_new;
+            }
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float pv = __builtin_amdgcn_exp2f(sc[kb][e] - m_use);
+                    sc[kb][e] = pv;
+                    ls += pv;
+                }
+            if constexpr (BOUNDED) {
+                l_run += ls;
+            } else {
+                l_run = l_run * alpha + ls;
+#pragma unroll
+                for (int db = 0; db < ND; db++) o[db] *= alpha;
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; cc++) {
+                f16x8 pb;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    pb[e] = (f16)sc[2 * cc][e];
+                    pb[4 + e] = (f16)sc[2 * cc + 1][e];
+                }
+#pragma unroll
+                for (int db = 0; db < ND; db++) {
+                    const f16x8 va = *(const f16x8*)&vs[(db * 16 + c16) * VLD + cc * 32 + g * 8];
+                    o[db] = mfma_16x16x32(va, pb, o[db]);
+                }
+            }
+        }
+    };
+    if (ntl > 0) {
+        gload(kt0 * KT, ka, kla, va);
+        sstore(0, ka, kla, va);
+        if (ntl > 1) gload((kt0 + 1) * KT, ka, kla, va);
+        __syncthreads();
+#pragma unroll 1
+        for (int it = 0; it < ntl; it += 2) {
+            // buffer 0 holds tile it; set a is in flight with tile it + 1
+            if (it + 2 < ntl) gload((kt0 + it + 2) * KT, kb_, klb, vb);
+            tile(it, 0);
+            if (it + 1 < ntl) sstore(1, ka, kla, va);
+            __syncthreads();
+            if (it + 1 >= ntl) break;
+            // buffer 1 holds tile it + 1; set b is in flight with tile it + 2
+            if (it + 3 < ntl) gload((kt0 + it + 3) * KT, ka, kla, va);
+            tile(it + 1, 1);
+            if (it + 2 < ntl) sstore(0, kb_, klb, vb);
             __syncthreads();
         }
     }
