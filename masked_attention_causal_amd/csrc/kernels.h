@@ -110,7 +110,7 @@ struct PqArgs {
     _Float16* Ql;    // [B, H, L, dh] fp16 lo parts of layer 0
     _Float16* Kl;
     _Float16* Vt;    // [n_layers][B, H, dh, Lp] fp16
-    float* Op;       // [B*H*Ctot][64][dh] fp32 partial attention outputs
+    _Float16* Op;    // [B*H*Ctot][64][dh] fp16 partial attention outputs, normalised by their sums
     float2* ML;      // [B*H*Ctot][64] (running max in log2 units, sum)
     unsigned long long* audit;  // tile counters of the audit build (null otherwise)
     LayerPtrs lw[SEQ_MAX_LAYERS];

@@ -146,7 +146,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         q.off_Ql = o;  o += up256(Td * 2);
         q.off_Kl = o;  o += up256(Td * 2);
         q.off_pVt = o; o += up256((size_t)q.B * q.d * q.Lp * 2 * q.n_layers);
-        q.off_Op = o;  o += up256(slots * 64 * q.dh * 4);
+        q.off_Op = o;  o += up256(slots * 64 * q.dh * 2);
         q.off_ML = o;  o += up256(slots * 64 * 8);
         q.off_pS = o;  o += up256((size_t)BNT * q.H * sizeof(float2));
         // fp16 weight planes (bf16 / fp32 I/O; fp32: hi and lo planes)
@@ -432,7 +432,7 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
     a.Ql = (_Float16*)(ws + P.off_Ql);
     a.Kl = (_Float16*)(ws + P.off_Kl);
     a.Vt = (_Float16*)(ws + P.off_pVt);
-    a.Op = (float*)(ws + P.off_Op);
+    a.Op = (_Float16*)(ws + P.off_Op);
     a.ML = (float2*)(ws + P.off_ML);
     a.qk_stats = (float2*)(ws + P.off_pS);
     a.audit = audit_counters;

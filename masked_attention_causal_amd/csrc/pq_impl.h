@@ -425,46 +425,58 @@ __device__ __forceinline__ void ffn_out_rows(const PqArgs& p, int lp, int b, int
     load4_f32((const WT*)w.ln2_g + k + 4, *reinterpret_cast<float(*)[4]>(&gm[4]));
     load4_f32((const WT*)w.ln2_b + k, *reinterpret_cast<float(*)[4]>(&bt[0]));
     load4_f32((const WT*)w.ln2_b + k + 4, *reinterpret_cast<float(*)[4]>(&bt[4]));
+    // rows in groups of G iterations: every load of a group is issued before
+    // its sums and reductions
+    constexpr int NI = PQ_RT / RPI, G = NI < 2 ? NI : 2;
 #pragma unroll
-    for (int i = 0; i < PQ_RT / RPI; i++) {
-        const int r = tid / TPR + i * RPI, pos = t * PQ_RT + r;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (pos < p.L) {
-            const size_t off = ((size_t)b * p.L + pos) * D + k;
-            const float4 x0 = *(const float4*)(p.X1 + off), x1 = *(const float4*)(p.X1 + off + 4);
-            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    for (int i0 = 0; i0 < NI; i0 += G) {
+        float4 xa[G][2], pa[G][PQ_FS_MAX][2];
 #pragma unroll
-            for (int e = 0; e < 8; e++) v[e] += bb[e];
-            // every partial's loads in flight together (FS <= PQ_FS_MAX)
-            float4 a[PQ_FS_MAX][2];
+        for (int gi = 0; gi < G; gi++) {
+            const int pos = t * PQ_RT + tid / TPR + (i0 + gi) * RPI;
+            if (pos < p.L) {
+                const size_t off = ((size_t)b * p.L + pos) * D + k;
+                xa[gi][0] = *(const float4*)(p.X1 + off);
+                xa[gi][1] = *(const float4*)(p.X1 + off + 4);
 #pragma unroll
-            for (int c = 0; c < PQ_FS_MAX; c++)
-                if (c < p.FS) {
-                    a[c][0] = *(const float4*)(p.FP + c * TD + off);
-                    a[c][1] = *(const float4*)(p.FP + c * TD + off + 4);
-                }
-#pragma unroll
-            for (int c = 0; c < PQ_FS_MAX; c++)
-                if (c < p.FS) {
-                    v[0] += a[c][0].x; v[1] += a[c][0].y; v[2] += a[c][0].z; v[3] += a[c][0].w;
-                    v[4] += a[c][1].x; v[5] += a[c][1].y; v[6] += a[c][1].z; v[7] += a[c][1].w;
-                }
+                for (int c = 0; c < PQ_FS_MAX; c++)
+                    if (c < p.FS) {
+                        pa[gi][c][0] = *(const float4*)(p.FP + c * TD + off);
+                        pa[gi][c][1] = *(const float4*)(p.FP + c * TD + off + 4);
+                    }
+            }
         }
-        float sm = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 #pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) sm += __shfl_xor(sm, o, WAVE);
-        const float mean = sm * (1.0f / D);
-        float sq = 0.f;
+        for (int gi = 0; gi < G; gi++) {
+            const int r = tid / TPR + (i0 + gi) * RPI, pos = t * PQ_RT + r;
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (pos < p.L) {
+                v[0] = xa[gi][0].x; v[1] = xa[gi][0].y; v[2] = xa[gi][0].z; v[3] = xa[gi][0].w;
+                v[4] = xa[gi][1].x; v[5] = xa[gi][1].y; v[6] = xa[gi][1].z; v[7] = xa[gi][1].w;
 #pragma unroll
-        for (int e = 0; e < 8; e++) sq = fmaf(v[e] - mean, v[e] - mean, sq);
+                for (int e = 0; e < 8; e++) v[e] += bb[e];
 #pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
-        const float rs = 1.0f / sqrtf(sq * (1.0f / D) + p.eps);
-        float out[8];
+                for (int c = 0; c < PQ_FS_MAX; c++)
+                    if (c < p.FS) {
+                        v[0] += pa[gi][c][0].x; v[1] += pa[gi][c][0].y; v[2] += pa[gi][c][0].z; v[3] += pa[gi][c][0].w;
+                        v[4] += pa[gi][c][1].x; v[5] += pa[gi][c][1].y; v[6] += pa[gi][c][1].z; v[7] += pa[gi][c][1].w;
+                    }
+            }
+            float sm = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 #pragma unroll
-        for (int e = 0; e < 8; e++) out[e] = (v[e] - mean) * rs * gm[e] + bt[e];
-        emit(r, pos, k, out);
+            for (int o = 1; o < TPR; o <<= 1) sm += __shfl_xor(sm, o, WAVE);
+            const float mean = sm * (1.0f / D);
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) sq = fmaf(v[e] - mean, v[e] - mean, sq);
+#pragma unroll
+            for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
+            const float rs = 1.0f / sqrtf(sq * (1.0f / D) + p.eps);
+            float out[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) out[e] = (v[e] - mean) * rs * gm[e] + bt[e];
+            emit(r, pos, k, out);
+        }
     }
 }
 
@@ -720,12 +732,19 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     if constexpr (MASK_ALL) {
         if (lane == 0) audit_add(p.audit, AUD_PQ_WAVE, n_vis);
     }
-    // partial state of (b, h, t, s): unnormalised O, running max (log2 units), sum
+    // partial state of (b, h, t, s): O / l in fp16 (a convex combination of
+    // V rows, so within V's range), the reference (log2 units) and the sum l
     const size_t slot = ((size_t)b * H + h) * p.Ctot + pq_pairs_before(t, p.KS) + s;
     const int qr = 16 * wave + c16;
-    float* op = p.Op + (slot * PQ_RT + qr) * DH;
+    f16* op = p.Op + (slot * PQ_RT + qr) * DH;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
-    for (int db = 0; db < ND; db++) *(float4*)(op + db * 16 + 4 * g) = float4{o[db][0], o[db][1], o[db][2], o[db][3]};
+    for (int db = 0; db < ND; db++) {
+        f16x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; e++) hv[e] = (f16)(o[db][e] * inv);
+        *(f16x4*)(op + db * 16 + 4 * g) = hv;
+    }
     if (g == 0) p.ML[slot * PQ_RT + qr] = float2{m_run, l_run};
 }
 
@@ -746,20 +765,21 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
         if (pos < p.L) {
             const size_t slot0 = ((size_t)b * H + h) * p.Ctot + pb;
             // splits in batches of MB whose loads are all in flight together,
-            // combined with a running maximum (rescaling what came before)
-            constexpr int MB = 4;
+            // combined with a running maximum (rescaling what came before);
+            // a split adds w l (O / l)
+            constexpr int MB = 8;
             float M = -INFINITY, lsum = 0.f;
 #pragma unroll 1
             for (int s0 = 0; s0 < ns; s0 += MB) {
                 float2 ml[MB];
-                float4 ov[MB][QD / 4];
+                f16x8 ov[MB][QD / 8];
 #pragma unroll
                 for (int j = 0; j < MB; j++) {
                     if (s0 + j < ns) {
                         ml[j] = p.ML[(slot0 + s0 + j) * PQ_RT + r];
-                        const float* op = p.Op + ((slot0 + s0 + j) * PQ_RT + r) * DH + qd;
+                        const f16* op = p.Op + ((slot0 + s0 + j) * PQ_RT + r) * DH + qd;
 #pragma unroll
-                        for (int i = 0; i < QD / 4; i++) ov[j][i] = *(const float4*)(op + 4 * i);
+                        for (int i = 0; i < QD / 8; i++) ov[j][i] = *(const f16x8*)(op + 8 * i);
                     } else {
                         ml[j] = float2{-INFINITY, 0.f};
                     }
@@ -776,15 +796,10 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
 #pragma unroll
                 for (int j = 0; j < MB; j++) {
                     if (ml[j].x == -INFINITY) continue;
-                    const float w = __builtin_amdgcn_exp2f(ml[j].x - M);
-                    lsum += w * ml[j].y;
+                    const float wl = __builtin_amdgcn_exp2f(ml[j].x - M) * ml[j].y;
+                    lsum += wl;
 #pragma unroll
-                    for (int i = 0; i < QD / 4; i++) {
-                        acc[4 * i] += w * ov[j][i].x;
-                        acc[4 * i + 1] += w * ov[j][i].y;
-                        acc[4 * i + 2] += w * ov[j][i].z;
-                        acc[4 * i + 3] += w * ov[j][i].w;
-                    }
+                    for (int i = 0; i < QD; i++) acc[i] += wl * (float)ov[j][i / 8][i % 8];
                 }
             }
             const float inv = 1.0f / lsum;

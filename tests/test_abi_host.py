@@ -117,7 +117,7 @@ def test_pq_workspace_layout():
     fs = 4                                                  # FFN tasks per tile: 4 x 64 tiles fill 256 CUs
     need = (up(T * d * 4) + up(T * d * 4) + up(T * d * 4 * fs)   # residual, X1, FFN partials
             + 2 * up(T * d * 2 * n_layers) + 2 * up(T * d * 2)
-            + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 4) + up(B * H * pairs * 64 * 8)
+            + up(B * d * Lp * 2 * n_layers) + up(B * H * pairs * 64 * dh * 2) + up(B * H * pairs * 64 * 8)
             + up(B * H * NT * 8)                                 # per (sequence, head, tile) Q/K norm bounds
             + up(weights))
     assert ws == need
