@@ -648,27 +648,31 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                     }
                 }
             }
+            // mask only the tiles that straddle the diagonal or the padding
+            // boundary (a wave-uniform branch), then one FMA per score into
+            // the hardware exp2 (scale > 0, so the max of raw scores is taken)
             const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
-            float mx = -INFINITY;
+            if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++)
+                for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    float v = sc[kb][e] * sl2;
-                    if (need_mask) {
+                    for (int e = 0; e < 4; e++) {
                         const int key = k0 + (kb >> 1) * 32 + 8 * g + 4 * (kb & 1) + e;
-                        if (key > myq || key >= len) v = -INFINITY;
+                        if (key > myq || key >= len) sc[kb][e] = -INFINITY;
                     }
-                    sc[kb][e] = v;
-                    if constexpr (!BOUNDED) mx = fmaxf(mx, v);
-                }
+            }
             float m_use = 0.f, alpha = 1.f;
             if constexpr (BOUNDED) {
                 m_run = 0.f;
             } else {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) mx = fmaxf(mx, sc[kb][e]);
                 mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                const float m_new = fmaxf(m_run, mx);
+                const float m_new = fmaxf(m_run, mx * sl2);
                 m_use = (m_new == -INFINITY) ? 0.f : m_new;
                 // hardware exp2: its flushing below 2^-126 is far below the fp16
                 // rounding of the weights and next to a row sum >= 1
@@ -680,7 +684,7 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
             for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const float pv = __builtin_amdgcn_exp2f(sc[kb][e] - m_use);
+                    const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] * sl2 : fmaf(sc[kb][e], sl2, -m_use));
                     sc[kb][e] = pv;
                     ls += pv;
                 }
