@@ -105,7 +105,7 @@ struct PqArgs {
     float* X1;       // [B*L, d] fp32 rows after attention + LayerNorm
     float* FP;       // [FS][B*L, d] fp32 FFN down-projection partials
     int FS;          // FFN tasks per tile (each F / FS hidden features)
-    _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 (hi part for layer 0)
+    _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 q * log2(e)/sqrt(dh) (hi part for layer 0)
     _Float16* Kh;
     _Float16* Ql;    // [B, H, L, dh] fp16 lo parts of layer 0
     _Float16* Kl;

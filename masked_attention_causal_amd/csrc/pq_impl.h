@@ -297,6 +297,12 @@ __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqAr
                 for (int e = 0; e < 4; e++) vts[(nn + e) * PqTile<WT, D, DH>::VLDT + r] = (f16)v[e];
             } else if (pos < p.L) {
                 const size_t off = (((size_t)b * H + h) * p.L + pos) * DH + dd;
+                // q leaves multiplied by log2(e)/sqrt(dh), so scores come out of
+                // the score MFMA in exp2 units (the same single rounding to fp16)
+                if (which == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v[e] *= p.scale_log2;
+                }
                 f16x4 hv, lv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
@@ -617,7 +623,6 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
 #pragma unroll
     for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = p.scale_log2;
 
     if constexpr (MASK_ALL) {
         if (tid == 0 && ntl > 0) audit_add(p.audit, AUD_PQ_WG, ntl);
@@ -649,8 +654,8 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                 }
             }
             // mask only the tiles that straddle the diagonal or the padding
-            // boundary (a wave-uniform branch), then one FMA per score into
-            // the hardware exp2 (scale > 0, so the max of raw scores is taken)
+            // boundary (a wave-uniform branch); the scores are in exp2 units
+            // already (q is stored scaled)
             const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
             if (need_mask) {
 #pragma unroll
@@ -672,7 +677,7 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
                     for (int e = 0; e < 4; e++) mx = fmaxf(mx, sc[kb][e]);
                 mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-                const float m_new = fmaxf(m_run, mx * sl2);
+                const float m_new = fmaxf(m_run, mx);
                 m_use = (m_new == -INFINITY) ? 0.f : m_new;
                 // hardware exp2: its flushing below 2^-126 is far below the fp16
                 // rounding of the weights and next to a row sum >= 1
@@ -684,7 +689,7 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
             for (int kb = 0; kb < 4; kb++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] * sl2 : fmaf(sc[kb][e], sl2, -m_use));
+                    const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] : sc[kb][e] - m_use);
                     sc[kb][e] = pv;
                     ls += pv;
                 }
@@ -1050,11 +1055,13 @@ __device__ __forceinline__ PqAtt pq_att_decode(const PqArgs& p, int i) {
 }
 
 // Score variant of an attention task's (sequence, head) from the row-norm
-// maxima of its Q and K hi planes (qk_stats, formed after every QKV stage):
-// the first layer takes the hi/lo split only where the bound on a single fp16
-// pass's score error, (2u + u^2)|q||k|c with u = 2^-11, exceeds 2^-8 in exp2
-// units; bounded when every score is within +-14 in exp2 units (|q||k|c,
-// times 1 + 2^-9 for the lo parts), so the weights 2^s need no reference.
+// maxima of its Q and K hi planes (qk_stats, written by the QKV tasks; q is
+// stored times c = log2(e)/sqrt(dh), so |q||k| below is |q||k|c of the
+// unscaled rows): the first layer takes the hi/lo split only where the bound
+// on a single fp16 pass's score error, (2u + u^2)|q||k|c with u = 2^-11,
+// exceeds 2^-8 in exp2 units; bounded when every score is within +-14 in
+// exp2 units (|q||k|c, times 1 + 2^-9 for the lo parts), so the weights 2^s
+// need no reference.
 __device__ __forceinline__ void pq_variant(const PqArgs& p, int bh, int layer, bool& split, bool& bounded) {
     const float2* st = p.qk_stats + (size_t)bh * p.NT;
     float mq = 0.f, mk = 0.f;
@@ -1067,7 +1074,7 @@ __device__ __forceinline__ void pq_variant(const PqArgs& p, int bh, int layer, b
         mq = fmaxf(mq, __shfl_xor(mq, o, WAVE));
         mk = fmaxf(mk, __shfl_xor(mk, o, WAVE));
     }
-    const float qk = mq * mk * p.scale_log2;
+    const float qk = mq * mk;   // q is stored scaled by log2(e)/sqrt(dh)
     split = layer == 0 && !((0.0009765625f + 2.384185791015625e-07f) * qk <= 0.00390625f);  // NaN or inf: split
     bounded = qk * 1.001953125f <= 14.f;
 }
