@@ -102,7 +102,7 @@ struct PqArgs {
     float eps;
     float scale_log2;
     float* X;        // [B*L, d] fp32 residual stream between layers
-    float* X1;       // [B*L, d] fp32 rows after attention + LayerNorm
+    float* X1;       // [B*L, d] fp32 rows after attention + LayerNorm (from the FFN tasks of part 0)
     float* FP;       // [FS][B*L, d] fp32 FFN down-projection partials
     int FS;          // FFN tasks per tile (each F / FS hidden features)
     _Float16* Qh;    // [n_layers][B, H, L, dh] fp16 q * log2(e)/sqrt(dh) (hi part for layer 0)

@@ -13,11 +13,11 @@
 //                       three times the tiles' workgroups
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
-//   ROWA(l,b,t)         merge of the partials, out-projection + residual +
-//                       LayerNorm -> X1
-//   FFN(l,b,t,cg)       FS tasks per tile, each F/FS hidden features:
-//                       up-projection + GELU, and its share of the
-//                       down-projection as an fp32 partial
+//   FFN(l,b,t,cg)       FS tasks per tile: each forms the tile's X1 (merge
+//                       of the attention partials, out-projection + residual
+//                       + LayerNorm; part 0 also writes it out), then for
+//                       F/FS hidden features the up-projection + GELU and
+//                       their share of the down-projection as an fp32 partial
 //   FIN(b,t)            the last layer's output rows (as in QKV) to y
 // The list runs as one launch per stage, workgroup i of a stage running its
 // task i; each stage depends only on earlier launches on the stream.  The
@@ -825,8 +825,14 @@ __device__ __forceinline__ void merge_att(const PqArgs& p, int b, int t, f16* ac
     }
 }
 
+// Rows of tile t after layer l's attention: merge of the partials,
+// out-projection + bias + residual, LayerNorm -> z (X1 of the rows this wave
+// holds: features n0 + 16 nb + 4 g .. + 3 of rows 16 rb + c16).  Uses act
+// and the reduction buffers; every wave is past its reads of act when it
+// returns (the LayerNorm's sums synchronise).
 template <class WT, int D, int DH>
-__device__ void task_rowa(const PqArgs& p, int l, int b, int t, char* smem, int tid) {
+__device__ __forceinline__ void post_attn_rows(const PqArgs& p, int l, int b, int t, char* smem, int tid,
+                                          f32x4 (&z)[PqTile<WT, D, DH>::NB][4]) {
     typedef PqTile<WT, D, DH> TL;
     constexpr int NB = TL::NB;
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
@@ -846,7 +852,6 @@ __device__ void task_rowa(const PqArgs& p, int l, int b, int t, char* smem, int 
     __syncthreads();
 
     // ---- out-projection + bias + residual
-    f32x4 z[NB][4];
 #pragma unroll
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
@@ -884,16 +889,6 @@ __device__ void task_rowa(const PqArgs& p, int l, int b, int t, char* smem, int 
         }
     }
     row_layernorm<D, NB>(z, (const WT*)w.ln1_g, (const WT*)w.ln1_b, p.eps, red0, red1, n0, wave, c16, g);
-    // X1 (fp32) to this tile's rows of its buffer, for the FFN tasks and the
-    // residual after the FFN
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-        for (int rb = 0; rb < 4; rb++) {
-            const int pos = t * PQ_RT + 16 * rb + c16;
-            const float v[4] = {z[nb][rb][0], z[nb][rb][1], z[nb][rb][2], z[nb][rb][3]};
-            if (pos < p.L) store4(p.X1 + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
-        }
 }
 
 // Part cg of layer l's FFN for the rows of tile t: chunks [cg, cg + 1) F / FS
@@ -909,14 +904,21 @@ __device__ void task_ffn(const PqArgs& p, int l, int b, int t, int cg, char* sme
     f16* gs = (f16*)(smem + TL::OFF_GV);
     const LayerPtrs& w = p.lw[l];
     const int n0 = wave * (D / 4);          // this wave's output features
-    constexpr int CH = PQ_RT * D / 8;
+    {
+        // every FFN task of a tile forms the tile's X1 itself (merge,
+        // out-projection, LayerNorm): fp16 copy into act, and from part 0 the
+        // fp32 rows to X1, the residual of the LayerNorm after the FFN
+        f32x4 z[NB][4];
+        post_attn_rows<WT, D, DH>(p, l, b, t, smem, tid, z);
 #pragma unroll
-    for (int i = 0; i < CH / PQ_THREADS; i++) {
-        const int c = tid + i * PQ_THREADS;
-        const int r = c / (D / 8), k = (c % (D / 8)) * 8;
-        const int pos = t * PQ_RT + r;
-        *(f16x8*)(act + r * TL::ALD + k) =
-            pos < p.L ? load8_as_f16(p.X1 + ((size_t)b * p.L + pos) * D + k) : f16x8{};
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) {
+                const int r = 16 * rb + c16, pos = t * PQ_RT + r;
+                const float v[4] = {z[nb][rb][0], z[nb][rb][1], z[nb][rb][2], z[nb][rb][3]};
+                store4(act + r * TL::ALD + n0 + 16 * nb + 4 * g, v);
+                if (cg == 0 && pos < p.L) store4(p.X1 + ((size_t)b * p.L + pos) * D + n0 + 16 * nb + 4 * g, v);
+            }
     }
     __syncthreads();
 
@@ -1009,7 +1011,7 @@ __device__ void task_fin(const PqArgs& p, int b, int t, int tid) {
 // ------------------------------------------------------------------ task list
 
 // Stage kinds (one launch each; a stage's workgroup i runs its task i).
-enum PqStage { PQ_STAGE_QKV = 0, PQ_STAGE_ROWA = 1, PQ_STAGE_FFN = 2, PQ_STAGE_FIN = 3 };
+enum PqStage { PQ_STAGE_QKV = 0, PQ_STAGE_FFN = 1, PQ_STAGE_FIN = 2 };
 
 // Every dependency of a stage was completed by an earlier launch on the
 // stream, so no workgroup ever waits on another.
@@ -1024,12 +1026,9 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int k
     } else if (kind == PQ_STAGE_FFN) {           // FFN(l, b, t, cg): cg fastest, so one XCD sees few chunks
         const int r = i / p.FS, cg = i - r * p.FS, t = r / p.B;
         task_ffn<WT, D, DH>(p, l, r - t * p.B, t, cg, smem, tid);
-    } else {
+    } else {                                     // FIN(b, t)
         const int t = i / p.B, b = i - t * p.B;
-        if (kind == PQ_STAGE_ROWA)
-            task_rowa<WT, D, DH>(p, l, b, t, smem, tid);
-        else
-            task_fin<WT, D>(p, b, t, tid);
+        task_fin<WT, D>(p, b, t, tid);
     }
 }
 
@@ -1122,7 +1121,6 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
         else
             hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, l);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = stage(PQ_STAGE_ROWA, l, BNT)) != hipSuccess) return e;
         if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT)) != hipSuccess) return e;
     }
     return stage(PQ_STAGE_FIN, a.n_layers - 1, BNT);
