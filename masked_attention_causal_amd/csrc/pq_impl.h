@@ -593,10 +593,11 @@ __device__ void task_att(const PqArgs& p, int l, int b, int h, int t, int s, cha
     auto gload = [&](int k0, f16x8 (&rk)[KPT], f16x8 (&rkl)[NKL], f16x8 (&rv)[VPT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KPT; i++) {
-            const int c = tid + i * PQ_THREADS, key = c / (DH / 8), col = (c % (DH / 8)) * 8;
-            const bool ok = k0 + key < L;
-            rk[i] = ok ? *(const f16x8*)(Kg + (size_t)(k0 + key) * DH + col) : f16x8{};
-            if constexpr (SPLIT) rkl[i] = ok ? *(const f16x8*)(Klg + (size_t)(k0 + key) * DH + col) : f16x8{};
+            // keys past L read row L-1 instead (finite, and masked): no
+            // branch around the load
+            const int c = tid + i * PQ_THREADS, key = min(k0 + c / (DH / 8), L - 1), col = (c % (DH / 8)) * 8;
+            rk[i] = *(const f16x8*)(Kg + (size_t)key * DH + col);
+            if constexpr (SPLIT) rkl[i] = *(const f16x8*)(Klg + (size_t)key * DH + col);
         }
 #pragma unroll
         for (int i = 0; i < VPT; i++) {
