@@ -356,8 +356,8 @@ def interleaved(tfl, torch, w, inp, paths, rounds=6, iters=5):
 
 # Steps and warm-up for the workloads reported beside the headline (the
 # 100k-token forward takes ~7 ms, the others well under 1 ms).
-EXTRA_STEPS = {"tiny_d32_b4_l32": (50, 10), "gemm_d1024_b8_l512": (20, 5),
-               "latency_d128_b1_l4096": (30, 5), "stream_d64_b1_l100000": (4, 1)}
+EXTRA_STEPS = {"tiny_d32_b4_l32": (300, 30), "gemm_d1024_b8_l512": (40, 5),
+               "latency_d128_b1_l4096": (200, 20), "stream_d64_b1_l100000": (10, 2)}
 # Workloads whose plan choice is timed against its alternative.
 DISPATCH = {"batch4096_d256_l64": ["seq", "tiled"], "latency_d128_b1_l4096": ["pq", "tiled"]}
 
