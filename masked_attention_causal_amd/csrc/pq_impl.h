@@ -1033,25 +1033,35 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int k
     }
 }
 
-// ATT(l, b, h, t, s) of stage index i: (tile, split) pair-major, then (b, h).
+// ATT(l, b, h, t, s) of workgroup i, or false for a workgroup past the last
+// task (the grid is rounded up to a multiple of 8).  Workgroups go to the
+// eight XCDs round-robin (XCD = i mod 8), so task q = (i mod 8) per + i / 8
+// gives each XCD a contiguous run of tasks; tasks are ordered by (sequence,
+// head), then key split s, then query tile t (split s exists for the tiles
+// t >= s KS), so one run reads few bands of K and V and its XCD's L2 holds
+// what the run re-reads.  The partial-state slot of a task stays
+// (b H + h) Ctot + pairs_before(t) + s.
 struct PqAtt {
     int b, h, t, s;
 };
 template <int H>
-__device__ __forceinline__ PqAtt pq_att_decode(const PqArgs& p, int i) {
-    const int BH = p.B * H;
-    const int pair = i / BH, bh = i - pair * BH;
-    int lo = 0, hi = p.NT - 1;                   // tile t with pairs_before(t) <= pair < pairs_before(t+1)
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pq_pairs_before(mid, p.KS) <= pair) lo = mid; else hi = mid - 1;
+__device__ __forceinline__ bool pq_att_decode(const PqArgs& p, int i, PqAtt& k) {
+    const int n = p.B * H * p.Ctot, per = (n + 7) / 8;
+    const int q = (i & 7) * per + (i >> 3);
+    if (q >= n) return false;
+    const int bh = q / p.Ctot;
+    int r = q - bh * p.Ctot, s = 0;
+    for (;;) {
+        const int cnt = p.NT - s * p.KS;         // tiles with a split s
+        if (r < cnt) break;
+        r -= cnt;
+        s++;
     }
-    PqAtt k;
-    k.t = lo;
-    k.s = pair - pq_pairs_before(lo, p.KS);
+    k.s = s;
+    k.t = s * p.KS + r;
     k.b = bh / H;
     k.h = bh - k.b * H;
-    return k;
+    return true;
 }
 
 // Score variant of an attention task's (sequence, head) from the row-norm
@@ -1086,7 +1096,8 @@ template <class WT, int D, int DH, bool FIRST>
 __global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArgs p, int l) {
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[FIRST ? TL::ATT_BYTES : TL::ATT1_BYTES];
-    const PqAtt k = pq_att_decode<D / DH>(p, (int)blockIdx.x);
+    PqAtt k;
+    if (!pq_att_decode<D / DH>(p, (int)blockIdx.x, k)) return;
     bool split, bounded;
     pq_variant(p, k.b * (D / DH) + k.h, l, split, bounded);
     const int tid = threadIdx.x;
@@ -1117,10 +1128,11 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     hipError_t e;
     for (int l = 0; l < a.n_layers; l++) {
         if ((e = stage(PQ_STAGE_QKV, l, PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
+        const int att_grid = (n_att + 7) / 8 * 8;
         if (l == 0)
-            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, l);
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(att_grid), dim3(PQ_THREADS), 0, s, a, l);
         else
-            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(n_att), dim3(PQ_THREADS), 0, s, a, l);
+            hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(att_grid), dim3(PQ_THREADS), 0, s, a, l);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT)) != hipSuccess) return e;
     }
