@@ -1021,12 +1021,21 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int k
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
     const int i = blockIdx.x, tid = threadIdx.x, BNT = p.B * p.NT;
-    if (kind == PQ_STAGE_QKV) {                  // QKV(l, b, t, part): part-major, then tile-major
-        const int part = i / BNT, r = i - part * BNT, t = r / p.B;
-        task_qkv<WT, D, DH>(p, l, r - t * p.B, t, part, smem, tid);
-    } else if (kind == PQ_STAGE_FFN) {           // FFN(l, b, t, cg): cg fastest, so one XCD sees few chunks
-        const int r = i / p.FS, cg = i - r * p.FS, t = r / p.B;
-        task_ffn<WT, D, DH>(p, l, r - t * p.B, t, cg, smem, tid);
+    if (kind == PQ_STAGE_QKV || kind == PQ_STAGE_FFN) {
+        // Every task of tile r = t B + b (its QKV parts, its FFN parts and
+        // FIN) runs on XCD r mod 8 (workgroups go to the XCDs round-robin):
+        // workgroup i takes the (i / 8 mod n)-th task of tile
+        // (i mod 8) + 8 (i / 8 / n), n tasks per tile; the grid is rounded
+        // up to whole groups of eight tiles.  What one stage writes for a
+        // tile the next reads from the same XCD's L2.
+        const int n = kind == PQ_STAGE_QKV ? PQ_QKV_PARTS : p.FS;
+        const int j = i >> 3, r = (i & 7) + 8 * (j / n), part = j % n;
+        if (r >= BNT) return;
+        const int t = r / p.B, b = r - t * p.B;
+        if (kind == PQ_STAGE_QKV)
+            task_qkv<WT, D, DH>(p, l, b, t, part, smem, tid);
+        else
+            task_ffn<WT, D, DH>(p, l, b, t, part, smem, tid);
     } else {                                     // FIN(b, t)
         const int t = i / p.B, b = i - t * p.B;
         task_fin<WT, D>(p, b, t, tid);
@@ -1121,20 +1130,21 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     typedef PqTile<WT, D, DH> TL;
     static_assert(TL::SMEM <= 160 * 1024, "LDS budget");
     const int BNT = a.B * a.NT, n_att = a.B * (D / DH) * a.Ctot;
+    const int BNT8 = (BNT + 7) / 8 * 8;         // tiles rounded up to whole groups of eight
     auto stage = [&](int kind, int l, int n) {
         hipLaunchKernelGGL((pq_stage_kernel<WT, D, DH>), dim3(n), dim3(PQ_THREADS), 0, s, a, kind, l);
         return hipGetLastError();
     };
     hipError_t e;
     for (int l = 0; l < a.n_layers; l++) {
-        if ((e = stage(PQ_STAGE_QKV, l, PQ_QKV_PARTS * BNT)) != hipSuccess) return e;
+        if ((e = stage(PQ_STAGE_QKV, l, PQ_QKV_PARTS * BNT8)) != hipSuccess) return e;
         const int att_grid = (n_att + 7) / 8 * 8;
         if (l == 0)
             hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(att_grid), dim3(PQ_THREADS), 0, s, a, l);
         else
             hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, false>), dim3(att_grid), dim3(PQ_THREADS), 0, s, a, l);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT)) != hipSuccess) return e;
+        if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT8)) != hipSuccess) return e;
     }
     return stage(PQ_STAGE_FIN, a.n_layers - 1, BNT);
 }
