@@ -217,7 +217,6 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
 #pragma unroll
     for (int db = 0; db < ND; db++) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = p.scale_log2;
     const int ix16 = (lane ^ 16) << 2, ix32 = (lane ^ 32) << 2;  // ds_bpermute byte indices
 
     int n_vis = 0;  // tiles scored by this wave (audit build)
@@ -255,9 +254,10 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
                 }
             }
         }
-        // running max on raw scores (scale > 0), then one FMA per score into
-        // the hardware exp2 (its flushing of results below 2^-126 is far
-        // below the fp16 rounding of the weights and next to a row sum >= 1)
+        // scores are in exp2 units (K is stored pre-scaled): running max, then
+        // one subtraction per score into the hardware exp2 (its flushing of
+        // results below 2^-126 is far below the fp16 rounding of the weights
+        // and next to a row sum >= 1)
         const bool need_mask = MASK_ALL || (k0 + KT - 1 > qw0) || (k0 + KT > len);
         if (need_mask) {
 #pragma unroll
@@ -281,7 +281,7 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
             }
             mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix16, __float_as_int(mx))));
             mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(ix32, __float_as_int(mx))));
-            const float m_new = fmaxf(m_run, mx * sl2);
+            const float m_new = fmaxf(m_run, mx);
             m_use = (m_new == -INFINITY) ? 0.f : m_new;
             alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
             m_run = m_new;
@@ -291,7 +291,7 @@ __device__ __forceinline__ void ring_body(const AttnArgs& p, char* lds) {
         for (int kb = 0; kb < 4; kb++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] * sl2 : fmaf(sc[kb][e], sl2, -m_use));
+                const float pv = __builtin_amdgcn_exp2f(BOUNDED ? sc[kb][e] : sc[kb][e] - m_use);
                 sc[kb][e] = pv;
                 ls += pv;
             }
@@ -344,7 +344,7 @@ template <int DH, bool CAN_SPLIT>
 __global__ __launch_bounds__(256) void attn_ring_kernel(AttnArgs p) {
     __shared__ __attribute__((aligned(16))) char lds[ring_lds_bytes<DH, CAN_SPLIT>()];
     bool split, bounded;
-    score_variant(p, p.scale_log2, split, bounded);
+    score_variant(p, 1.0f, split, bounded);   // K is stored pre-scaled
     if (CAN_SPLIT && split) {
         if constexpr (CAN_SPLIT) {
             if (bounded) ring_body<DH, true, true>(p, lds);

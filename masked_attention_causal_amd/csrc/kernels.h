@@ -34,9 +34,9 @@ struct GemmArgs {
     void* Vt;
     int L, Lp, H, dh, d;
     int split;
-    // EPI_QKV: K is written multiplied by kscale (0 means 1).  The head-dim-16
-    // attention kernel takes keys pre-multiplied by log2(e)/sqrt(dh), so its
-    // score products come out in the exp2 domain.
+    // EPI_QKV: K is written multiplied by kscale (0 means 1).  The attention
+    // kernels take keys pre-multiplied by log2(e)/sqrt(dh), so their score
+    // products come out in the exp2 domain.
     float kscale;
     // EPI_GELU: out [M, N] fp16 (F32 mode: hi plane, lo plane M*N elements further)
     void* out;

@@ -291,8 +291,8 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
         g.Q = Q; g.Kd = K; g.Vt = Vt;
         g.L = P.L; g.Lp = P.Lp; g.H = P.H; g.dh = P.dh; g.d = P.d;
         g.split = split;
-        // the head-dim-16 attention kernel reads K pre-scaled
-        if (P.dh == 16) g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
+        // the attention kernels read K pre-scaled into exp2 units
+        g.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
         // with the fused row kernel, layers after the first get their Q, K
         // and V^T from the previous layer's row kernel
         if (!P.row_fused || l == 0) {
@@ -335,7 +335,7 @@ static hipError_t run_tiled(const Plan& P, const tfl_layer* layers, const void* 
             r.Q = (f16*)Q; r.K = (f16*)K; r.Vt = (f16*)Vt;
             r.B = P.B; r.L = P.L; r.Lp = P.Lp; r.F = P.f;
             r.eps = P.eps;
-            r.kscale = P.dh == 16 ? (float)(1.4426950408889634 / std::sqrt((double)P.dh)) : 0.f;
+            r.kscale = (float)(1.4426950408889634 / std::sqrt((double)P.dh));
             r.last = last ? 1 : 0;
             r.w = LayerPtrs{w.w_qkv, w.b_qkv, w.w_o, w.b_o, w.ln1_g, w.ln1_b, w.w_1, w.b_1, w.w_2, w.b_2, w.ln2_g, w.ln2_b};
             if (!last) {
