@@ -303,8 +303,9 @@ def measure(tfl, torch, w, name, inp, steps, warmup, path="auto"):
         tot_flops += stage_work(w, st, inp.lens)[0] * (1 if st == "fused" else w.n_layers)
     launches = sum(launches_per_forward(st, w.n_layers, plan) for st in stages)
     if enc.plan_path == "pq":
-        # QKV, ATT, FFN per layer, the final rows; weight conversion
-        launches = 3 * w.n_layers + 1 + (0 if w.dtype == "f16" else 1)
+        # QKV, ATT, FFN per layer, the final rows (the first QKV stage also
+        # converts the weights)
+        launches = 3 * w.n_layers + 1
     res = {
         "plan": plan,
         "ms_per_step": ms_step,

@@ -88,6 +88,14 @@ struct SeqArgs {
 constexpr int PQ_QKV_PARTS = 3;
 constexpr int PQ_FS_MAX = 4;   // PQ FFN tasks per 64-row tile, at most
 
+// A weight matrix converted to fp16 planes: n elements of src (I/O dtype)
+// to dst (fp32: hi plane, then the lo plane times 2^11 n elements further).
+struct WconvSeg {
+    const void* src;
+    _Float16* dst;
+    long n;
+};
+
 // PQ path: the stack as a task list over 64-row tiles (QKV projection,
 // split-K attention, out-projection + LayerNorm, FFN parts; the LayerNorm
 // after the FFN runs where the rows are next loaded), run as one launch per
@@ -118,6 +126,11 @@ struct PqArgs {
     // with fp16 I/O, else converted once per forward; with fp32 I/O each is
     // followed by its lo plane (rounding remainder times 2^11)
     const _Float16* wh[SEQ_MAX_LAYERS][4];
+    // bf16 / fp32 I/O: the weights the first attention stage converts into
+    // the planes of wh (every weight but the first layer's W_qkv, which the
+    // first QKV stage reads as given); nconv = 0 with fp16 I/O
+    WconvSeg conv[4 * SEQ_MAX_LAYERS];
+    int nconv;
     // [B H][NT] per (sequence, head) and 64-row tile bounds on the largest
     // row norm of the current layer's Q and K (written by the QKV tasks):
     // each attention task's score variant
@@ -159,11 +172,6 @@ hipError_t launch_gemm(Mode m, Epi e, const GemmArgs& a, hipStream_t s);
 // Weight staging of the layer-wise path (BF16 and F32 modes): each segment's
 // n source weights (I/O dtype) become n fp16 values at dst (F32 mode: hi at
 // dst, lo times 2^11 at dst + n).  n % 8 == 0.
-struct WconvSeg {
-    const void* src;
-    _Float16* dst;
-    long n;
-};
 constexpr int WCONV_MAX_SEGS = 32;
 struct WconvArgs {
     WconvSeg seg[WCONV_MAX_SEGS];

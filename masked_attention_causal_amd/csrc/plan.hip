@@ -444,26 +444,27 @@ static hipError_t run_pq(const Plan& P, const tfl_layer* layers, const void* x, 
     // fp16 weights: the given ones with fp16 I/O, else converted here
     const size_t dd = (size_t)P.d * P.d, df = (size_t)P.d * P.f, planes = P.mode == MODE_F32 ? 2 : 1;
     const size_t n[4] = {3 * dd, dd, df, df};
-    WconvArgs wa{};
+    // (converted by the first attention stage; the first QKV stage reads the
+    // first layer's W_qkv as given)
     f16* cw = (f16*)(ws + P.off_pW);
+    a.nconv = 0;
     for (int l = 0; l < P.n_layers; l++) {
         const tfl_layer& w = layers[l];
         const void* src[4] = {w.w_qkv, w.w_o, w.w_1, w.w_2};
         for (int k = 0; k < 4; k++) {
             if (P.mode == MODE_F16) {
                 a.wh[l][k] = (const f16*)src[k];
+            } else if (l == 0 && k == 0) {
+                a.wh[l][k] = nullptr;
             } else {
                 a.wh[l][k] = cw;
-                wa.seg[wa.nseg++] = WconvSeg{src[k], cw, (long)n[k]};
+                a.conv[a.nconv++] = WconvSeg{src[k], cw, (long)n[k]};
                 cw += n[k] * planes;
             }
         }
     }
     Timed tm(T, TFL_STAGE_FUSED, s);
-    hipError_t e = hipSuccess;
-    if (wa.nseg > 0) e = launch_wconv(P.mode, wa, s);   // at most 4 * SEQ_MAX_LAYERS = WCONV_MAX_SEGS segments
-    if (e == hipSuccess) e = launch_pq(P.mode, P.d, P.dh, a, s);
-    return tm.done(e);
+    return tm.done(launch_pq(P.mode, P.d, P.dh, a, s));
 }
 
 hipError_t run_plan(const Plan& p, const tfl_layer* layers, const void* x, const int32_t* lens, void* y, char* ws,

@@ -184,6 +184,49 @@ __device__ __forceinline__ void mm_rows_split(f32x4 (&main)[NBW][4], f32x4 (&lo)
     }
 }
 
+// mm_rows_split with the weights read as given in fp32 and split into the hi
+// and 2^11-scaled lo fp16 parts in registers (the same rounding as the
+// converted planes).
+template <int NBW, int K>
+__device__ __forceinline__ void mm_rows_split_f32(f32x4 (&main)[NBW][4], f32x4 (&lo)[NBW][4], const float* W,
+                                                  int ldw, int n0, const f16* act, const f16* act_lo, int ald,
+                                                  int c16, int g) {
+    constexpr int KS = K / 32;
+    static_assert(KS % 2 == 0, "K must be a multiple of 64");
+#pragma unroll 1
+    for (int ks2 = 0; ks2 < KS; ks2 += 2)
+#pragma unroll
+    for (int ks = ks2; ks < ks2 + 2; ks++) {
+        f16x8 wh[NBW], wl[NBW];
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++) {
+            const float* src = W + (size_t)(n0 + 16 * nb + c16) * ldw + ks * 32 + 8 * g;
+            const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const f16 h = (f16)v[e];
+                wh[nb][e] = h;
+                wl[nb][e] = (f16)((v[e] - (float)h) * 2048.0f);
+            }
+        }
+        f16x8 bh[4], bl[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+            bh[rb] = *(const f16x8*)(act + (16 * rb + c16) * ald + ks * 32 + 8 * g);
+            bl[rb] = *(const f16x8*)(act_lo + (16 * rb + c16) * ald + ks * 32 + 8 * g);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NBW; nb++)
+#pragma unroll
+            for (int rb = 0; rb < 4; rb++) {
+                main[nb][rb] = mfma_16x16x32(wh[nb], bh[rb], main[nb][rb]);
+                lo[nb][rb] = mfma_16x16x32(wl[nb], bh[rb], lo[nb][rb]);
+                lo[nb][rb] = mfma_16x16x32(wh[nb], bl[rb], lo[nb][rb]);
+            }
+    }
+}
+
 // Sum over the D features of each tile row, features spread over the four
 // waves as in mm_rows.  red: 256 floats of LDS.  out[rb] = row 16rb+c16.
 template <int NB>
@@ -352,6 +395,10 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
     float* red = (float*)(smem + TL::OFF_RED);   // [D / (16 QNB) chunks][64 rows] sums of squares
     const f16* W = p.wh[layer][0];
     const bool first = layer == 0;
+    // the first layer's W_qkv as given (converted by this stage for nothing
+    // else): fp32 split in registers, bf16 widened by the loads
+    const WT* Wg = (const WT*)p.lw[layer].w_qkv;
+    const bool given = first && !std::is_same<WT, f16>::value;
 #pragma unroll 1
     for (int ps = 0; ps < PPW; ps++) {
         const int nn0 = wave * (D / 4) + ps * 16 * QNB;   // feature within the part
@@ -368,8 +415,8 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
                 for (int nb = 0; nb < QNB; nb++)
 #pragma unroll
                     for (int rb = 0; rb < 4; rb++) lo[nb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                mm_rows_split<QNB, D>(acc, lo, W, W + (size_t)3 * D * D, D, n0, act,
-                                      (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
+                mm_rows_split_f32<QNB, D>(acc, lo, (const float*)Wg, D, n0, act,
+                                          (const f16*)(smem + TL::OFF_ACT2), TL::ALD, c16, g);
 #pragma unroll
                 for (int nb = 0; nb < QNB; nb++)
 #pragma unroll
@@ -377,6 +424,8 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
             } else {
                 mm_rows<QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
             }
+        } else if (given) {
+            mm_rows<QNB, D>(acc, Wg, D, n0, 0, act, TL::ALD, c16, g);
         } else {
             mm_rows<QNB, D>(acc, W, D, n0, 0, act, TL::ALD, c16, g);
         }
@@ -1009,6 +1058,31 @@ __device__ void task_fin(const PqArgs& p, int b, int t, int tid) {
     });
 }
 
+// Share of workgroup i of n of the weight conversion into fp16 planes (the
+// first attention stage runs it after its task: the FFN stage after it is
+// the first reader, and workgroups with short tasks take it off the stage's
+// critical path).  Eight elements per thread and step.
+template <class WT>
+__device__ __forceinline__ void pq_convert_share(const PqArgs& p, int i, int n, int tid) {
+    const long stride = (long)n * PQ_THREADS * 8;
+    for (int k = 0; k < p.nconv; k++) {
+        const WconvSeg sg = p.conv[k];
+        for (long e = ((long)i * PQ_THREADS + tid) * 8; e < sg.n; e += stride) {
+            float v[8];
+            load4_f32((const WT*)sg.src + e, *reinterpret_cast<float(*)[4]>(&v[0]));
+            load4_f32((const WT*)sg.src + e + 4, *reinterpret_cast<float(*)[4]>(&v[4]));
+            f16x8 h, lo;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                h[j] = (f16)v[j];
+                lo[j] = (f16)((v[j] - (float)h[j]) * 2048.0f);
+            }
+            *(f16x8*)(sg.dst + e) = h;
+            if constexpr (sizeof(WT) == 4) *(f16x8*)(sg.dst + sg.n + e) = lo;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ task list
 
 // Stage kinds (one launch each; a stage's workgroup i runs its task i).
@@ -1106,7 +1180,10 @@ __global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArg
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[FIRST ? TL::ATT_BYTES : TL::ATT1_BYTES];
     PqAtt k;
-    if (!pq_att_decode<D / DH>(p, (int)blockIdx.x, k)) return;
+    if (!pq_att_decode<D / DH>(p, (int)blockIdx.x, k)) {
+        if (FIRST) pq_convert_share<WT>(p, (int)blockIdx.x, (int)gridDim.x, (int)threadIdx.x);
+        return;
+    }
     bool split, bounded;
     pq_variant(p, k.b * (D / DH) + k.h, l, split, bounded);
     const int tid = threadIdx.x;
@@ -1123,6 +1200,7 @@ __global__ __launch_bounds__(PQ_THREADS, FIRST ? 2 : 4) void pq_att_kernel(PqArg
         if (bounded) task_att<WT, D, DH, false, true>(p, l, k.b, k.h, k.t, k.s, smem, tid);
         else task_att<WT, D, DH, false, false>(p, l, k.b, k.h, k.t, k.s, smem, tid);
     }
+    if (FIRST) pq_convert_share<WT>(p, (int)blockIdx.x, (int)gridDim.x, tid);
 }
 
 template <class WT, int D, int DH>
