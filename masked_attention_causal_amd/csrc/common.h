@@ -194,18 +194,32 @@ __device__ __forceinline__ float gelu_poly(float h) {
     r = fmaf(u, r, 0.39894226f);
     return fmaf(u, r, 0.5f * h);
 }
+// The same form with P of degree 3 (csrc/fit_erf_poly.py), for products
+// whose GELU output is rounded to fp16 next (the fused kernels' FFN
+// activations): within 1.7e-5 of the exact GELU and under 0.7 fp16 ulp of
+// its value on |h| < GELU_SMALL_MAX, i.e. one more rounding of at most that
+// size before the fp16 one.  Six instructions.
+__device__ __forceinline__ float gelu_poly16(float h) {
+    const float u = h * h;
+    float r = fmaf(u, -0.0008117355173453689f, 0.009531241841614246f);
+    r = fmaf(u, r, -0.06631539762020111f);
+    r = fmaf(u, r, 0.3989310562610626f);
+    return fmaf(u, r, 0.5f * h);
+}
 // GELU of N values in place: the short-range form when every value of the
 // wave is in its range (one wave-uniform test), the whole-range form
 // otherwise.  Normalised activations keep to the short range almost always,
 // so the common case is straight-line code with no divergent branches.
-template <int N>
+// FP16_OUT: the values are rounded to fp16 next, so the short range takes
+// gelu_poly16.
+template <int N, bool FP16_OUT = false>
 __device__ __forceinline__ void gelu_inplace(float* v) {
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < N; i++) m = fmaxf(m, fabsf(v[i]));
     if (__ballot(!(m < GELU_SMALL_MAX)) == 0) {
 #pragma unroll
-        for (int i = 0; i < N; i++) v[i] = gelu_poly(v[i]);
+        for (int i = 0; i < N; i++) v[i] = FP16_OUT ? gelu_poly16(v[i]) : gelu_poly(v[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < N; i++) v[i] = gelu_full(v[i]);

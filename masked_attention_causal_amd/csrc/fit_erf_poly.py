@@ -10,6 +10,11 @@ Chebyshev nodes that drives down the largest relative error (about 4e-8 in
 exact arithmetic); evaluated by Horner's rule in fp32 the result stays within
 2.2 ulp of erf.
 
+gelu_poly16 (the same form with P of degree 3, for products whose GELU
+output is rounded to fp16): the same fit with deg=3; relative error of
+erf(x)/x about 2.8e-5, GELU within 1.7e-5 absolute and under 0.7 fp16 ulp
+of its value on |h| < sqrt(2).
+
 gelu_full (whole range, no branch): erfc(a)/2 = u 2^(R(u) - a^2 log2 e) with
 a = |h|/sqrt(2) and u = 1/(2 + a), so GELU(h) = h - h e for h >= 0 and h e
 for h < 0, e = erfc(a)/2.  R (degree 9 in u) is the same kind of
@@ -80,6 +85,10 @@ if __name__ == "__main__":
     r = [v / (2 * math.sqrt(2) * 2 ** k) for k, v in enumerate(c)]
     print("GELU coefficients R (degree 0..5):", ", ".join(f"{np.float32(v)}f" for v in r))
     print(f"max relative error (exact arithmetic) {rel:.3g}; fp32 Horner {fp32_ulp_error(c):.2f} ulp")
+    c3, rel3 = fit(3)
+    r3 = [v / (2 * math.sqrt(2) * 2 ** k) for k, v in enumerate(c3)]
+    print("gelu_poly16 coefficients R (degree 0..3):", ", ".join(f"{float(np.float32(v))!r}f" for v in r3))
+    print(f"max relative error of erf(x)/x (exact arithmetic) {rel3:.3g}")
     t, terr = fit_tail()
     print("gelu_full coefficients R (degree 0..9):", ", ".join(f"{float(np.float32(v))!r}f" for v in t))
     print(f"max exponent error (exact arithmetic) {terr:.3g}")

@@ -1011,7 +1011,7 @@ __device__ void task_ffn(const PqArgs& p, int l, int b, int t, int cg, char* sme
                 for (int e = 0; e < 4; e++) ga[nb][rb][e] += bv[e];
         }
         static_assert(sizeof(ga) == 32 * sizeof(float), "ga is 32 packed floats");
-        gelu_inplace<32>((float*)&ga[0][0]);
+        gelu_inplace<32, true>((float*)&ga[0][0]);
 #pragma unroll
         for (int nb = 0; nb < 2; nb++)
 #pragma unroll

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void row_kernel(RowArgs p) {
                 for (int e = 0; e < 4; e++) ga[nb][rb][e] += bv[e];
         }
         static_assert(sizeof(ga) == 32 * sizeof(float), "ga is 32 packed floats");
-        gelu_inplace<32>((float*)&ga[0][0]);
+        gelu_inplace<32, true>((float*)&ga[0][0]);
 #pragma unroll
         for (int nb = 0; nb < 2; nb++)
 #pragma unroll

@@ -610,7 +610,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void seq_kernel(SeqArgs p) {
                 }
             pipeline_order<FCH / 16 + NKC * FCH / 16, NKC * FCH / 16 * TPW, TPW, SEQ_AHEAD>();
             static_assert(sizeof(carry) == FCH / 16 * TPW * 4 * sizeof(float), "carry is packed floats");
-            gelu_inplace<FCH / 16 * TPW * 4>((float*)&carry[0][0]);
+            gelu_inplace<FCH / 16 * TPW * 4, true>((float*)&carry[0][0]);
         } else {
             // ---- FFN down-projection chunk accumulated into the residual
             if (d.fc == 0) {

@@ -1,4 +1,4 @@
-"""The short-range GELU polynomial of the fused kernels (common.h, gelu_poly).
+"""The GELU forms of the kernels (common.h: gelu_poly, gelu_poly16, gelu_full).
 
 Host-side check of the coefficients the device code uses.  The kernel
 computes GELU(h) = h/2 + u R(u), u = h^2, for |h| < GELU_SMALL_MAX, where
@@ -86,6 +86,54 @@ def test_gelu_poly_identities():
 
 def test_gelu_small_threshold_inside_fit_range():
     assert _threshold() * 0.7071067811865475 <= 1.0
+
+
+# ---------------------------------------------------------------- short range, fp16 outputs (gelu_poly16)
+
+def _coefficients16():
+    """gelu_poly16's R, degree 0..3, read from the header."""
+    src = open(HDR).read()
+    body = src[src.index("float gelu_poly16(float h)"):]
+    body = body[:body.index("return fmaf(u, r, 0.5f * h);")]
+    nums = [float(v) for v in re.findall(r"(-?\d+\.\d+(?:e-?\d+)?)f", body)]
+    assert len(nums) == 4, nums
+    return nums[::-1]
+
+
+def _gelu_poly16(h):
+    r = _coefficients16()
+    h = np.asarray(h, dtype=np.float32)
+    u = (h * h).astype(np.float32)
+    q = _fma32(u, np.float32(r[3]), np.float32(r[2]))
+    for c in r[1::-1]:
+        q = _fma32(u, q, np.float32(c))
+    return _fma32(u, q, (np.float32(0.5) * h).astype(np.float32))
+
+
+def test_gelu_poly16_within_a_fraction_of_an_fp16_ulp():
+    """Evaluated in fp32 as the kernels do: within 2e-5 of the exact GELU and
+    under 0.75 fp16 ulp of its value (the output is rounded to fp16 next),
+    over the short range; the implied erf(x)/x is within 3e-5 relative."""
+    thr = _threshold()
+    h = np.linspace(-thr, thr, 200001, dtype=np.float32)
+    got = _gelu_poly16(h).astype(np.float64)
+    ref = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in h.astype(np.float64)])
+    err = np.abs(got - ref)
+    assert err.max() <= 2e-5
+    ulp16 = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert np.max(err / ulp16) <= 0.75
+    r = _coefficients16()
+    p = [rk * 2.0 * math.sqrt(2.0) * 2.0 ** k for k, rk in enumerate(r)]
+    x = np.linspace(1e-3, 1.0, 20001)
+    rel = np.abs(np.polyval(p[::-1], x * x) - np.array([math.erf(v) / v for v in x])) / np.array([math.erf(v) / v for v in x])
+    assert rel.max() <= 3e-5
+
+
+def test_gelu_poly16_identities():
+    h = np.float32([0.125, 0.5, 1.0, 1.375])
+    assert _gelu_poly16(np.float32([0.0]))[0] == 0.0
+    d = _gelu_poly16(h).astype(np.float64) - _gelu_poly16(-h).astype(np.float64)
+    assert np.allclose(d, h.astype(np.float64), rtol=0, atol=2e-7)
 
 
 # ---------------------------------------------------------------- whole-range form (gelu_full)
