@@ -36,15 +36,17 @@
 // from global memory into registers (A operand), so weights are never
 // staged through LDS and each weight fragment feeds four MFMAs.  The weights
 // are fp16 in memory: bf16 and fp32 weights are converted once per forward
-// (fp32: an fp16 plane and a plane of the remainders times 2^11), which
-// halves the bytes every row task streams and takes the conversion out of
-// its loads.
+// by the first attention stage (fp32: an fp16 plane and a plane of the
+// remainders times 2^11), which halves the bytes every FFN task streams and
+// takes the conversion out of its loads; the first QKV stage reads its W_qkv
+// as given.
 //
 // Precision: fp32 residual stream and LayerNorm; fp16 operands except where
-// the first layer sees raw inputs: its attention scores use hi + lo fp16
-// parts of fp32 Q and K (three MFMAs), and with fp32 I/O its QKV projection
-// uses hi + 2^11-scaled lo parts of both x and the weights (three MFMAs, two
-// accumulators), which keeps scores near 1e5 fp32-accurate.
+// the first layer sees raw inputs: its attention scores may use hi + lo
+// fp16 parts of Q and K (three MFMAs, chosen per (sequence, head) from their
+// row norms), and with fp32 I/O its QKV projection uses hi + 2^11-scaled lo
+// parts of both x and the weights (three MFMAs, two accumulators), which
+// keeps scores near 1e5 fp32-accurate.
 #pragma once
 #include "common.h"
 #include "kernels.h"
