@@ -76,7 +76,9 @@ typedef enum {
 
 typedef struct {
     int32_t n_layers;   /* >= 1 */
-    int32_t d_model;    /* multiple of 32, <= 1024 */
+    int32_t d_model;    /* multiple of 32, <= 1024, odd part <= 7: 32 x {1..8, 10, 12, 14, 16,
+                           20, 24, 28, 32} (a LayerNorm row is split over up to 64 lanes of
+                           at most 8 four-value chunks each) */
     int32_t n_heads;    /* d_model / n_heads in {16, 32, 64} */
     int32_t d_ffn;      /* multiple of 32 */
     int32_t batch;      /* >= 1 */

@@ -104,8 +104,9 @@ __device__ __forceinline__ void store_o4(f16* out, const float (&v)[4], size_t l
     f16x4 hv, lv;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        hv[e] = (f16)v[e];
-        lv[e] = (f16)((v[e] - (float)hv[e]) * 2048.0f);
+        const F16Split s = split_f16(v[e], 2048.0f);
+        hv[e] = s.hi;
+        lv[e] = s.lo;
     }
     *(f16x4*)out = hv;
     if (lo_plane) *(f16x4*)(out + lo_plane) = lv;

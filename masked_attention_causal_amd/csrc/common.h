@@ -69,6 +69,22 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
     return r;
 }
 
+// v as an fp16 hi part and the rounding remainder v - hi (exact in fp32)
+// times lo_scale, both taken from the same fp32 value.  v passes through an
+// empty asm first: where v is the result of a product or an FMA, the compiler
+// may otherwise fuse that operation into the fp16 conversion of hi (one
+// rounding from the exact result, v_fma_mix) while the remainder is formed
+// from the fp32-rounded v; at an fp16 rounding midpoint the two then disagree
+// and hi + lo is off by one fp16 ulp instead of ~2^-22 of v.
+struct F16Split {
+    f16 hi, lo;
+};
+__device__ __forceinline__ F16Split split_f16(float v, float lo_scale) {
+    asm("" : "+v"(v));
+    const f16 hi = (f16)v;
+    return F16Split{hi, (f16)((v - (float)hi) * lo_scale)};
+}
+
 // Eight consecutive stored values -> eight fp16 MFMA operands.
 __device__ __forceinline__ f16x8 load8_as_f16(const f16* p) { return *(const f16x8*)p; }
 __device__ __forceinline__ f16x8 load8_as_f16(const bf16* p) {

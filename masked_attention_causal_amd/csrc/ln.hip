@@ -71,8 +71,9 @@ __device__ __forceinline__ void st4_split(f16* p, size_t lo_plane, const float (
     float h[4], l[4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        h[e] = (float)(f16)v[e];
-        l[e] = (v[e] - h[e]) * 2048.0f;
+        const F16Split s = split_f16(v[e], 2048.0f);
+        h[e] = (float)s.hi;
+        l[e] = (float)s.lo;
     }
     st4(p, h);
     st4(p + lo_plane, l);

@@ -72,7 +72,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
     }
     int lpr, nc;
     if (c.d_model % 32 != 0 || c.d_model > 1024 || !ln_shape(c.d_model, &lpr, &nc)) {
-        *why = "d_model must be a multiple of 32 and at most 1024";
+        *why = "d_model must be a multiple of 32, at most 1024, with an odd part of at most 7 (LayerNorm row split)";
         return TFL_E_UNSUPPORTED;
     }
     if (c.d_ffn % 32 != 0) {

@@ -351,8 +351,9 @@ __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqAr
                 f16x4 hv, lv;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    hv[e] = (f16)v[e];
-                    lv[e] = (f16)(v[e] - (float)hv[e]);
+                    const F16Split sp = split_f16(v[e], 1.0f);
+                    hv[e] = sp.hi;
+                    lv[e] = sp.lo;
                     ss[rb] = fmaf((float)hv[e], (float)hv[e], ss[rb]);
                 }
                 *(f16x4*)((which == 0 ? p.Qh : p.Kh) + (size_t)layer * TD + off) = hv;

@@ -162,6 +162,7 @@ def test_workspace_covers_the_tiled_buffers():
     (dict(n_heads=3), 1), (dict(dtype=7), 1), (dict(force_path=9), 1),
     (dict(d_model=48, n_heads=1), 2), (dict(d_model=256, n_heads=2), 2), (dict(d_ffn=100), 2),
     (dict(d_model=2048, n_heads=32), 2), (dict(batch=70000), 2),
+    (dict(d_model=288, n_heads=9), 2), (dict(d_model=352, n_heads=11), 2), (dict(d_model=960, n_heads=15), 2),
 ])
 def test_create_rejects(cfg, status):
     base = dict(n_layers=2, d_model=64, n_heads=4, d_ffn=128, batch=2, seq_len=16, dtype="f16")
@@ -170,6 +171,14 @@ def test_create_rejects(cfg, status):
         tfl.plan_for(**base)
     assert e.value.status == status
     assert "tfl_create" in str(e.value)
+
+
+def test_create_accepts_d_model_with_small_odd_part():
+    # multiples of 32 up to 1024 whose odd part is at most 7 (the LayerNorm
+    # row split); the others are rejected above
+    for k in (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20, 24, 28, 32):
+        d = 32 * k
+        tfl.plan_for(1, d, d // 32, 2 * d, 2, 16, "f16", force_path="tiled")
 
 
 def test_create_rejects_bad_layer_pointers(lib):

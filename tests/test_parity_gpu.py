@@ -201,23 +201,31 @@ def test_small_sequence_resident(w, scale):
 # ---------------------------------------------------------------- pipelined GEMM tiles
 
 PIPE = [
-    # 256-token tiles (wide QKV / FFN1) with a ragged last token tile; 128 x 128 tiles elsewhere
+    # 64-token tiles (fewer than 512 tiles of 128 x 128) with a ragged last token tile
     W("g_bf16_d512", 2, 512, 8, 1024, 3, 700, "bf16", 1, 700, 1.0),
     # N = 3 * 320 = 960 and 320: feature blocks past N are clamped copies
     W("g_f16_d320", 1, 320, 5, 640, 7, 500, "f16", 1, 500, 1.0),
 ]
 
+# Shapes whose wide products take 128 x 192 tiles (two workgroups per CU
+# either way; fewer idle workgroup slots than 128 x 128 tiles):
+#  * d = 448, 6,600 tokens (ragged last token tile): QKV (N = 1344, 52 x 7
+#    tiles) and FFN up (N = 1216, ragged last feature tile); out-projection
+#    and FFN down take 64-token tiles;
+#  * d = 224 bf16, 10,900 tokens: QKV (N = 672, ragged last feature tile);
+#    the other products take 64-token tiles.
+WIDE = [
+    W("g_f16_d448", 1, 448, 7, 1216, 11, 600, "f16", 1, 600, 1.0),
+    W("g_bf16_d224", 1, 224, 7, 448, 10, 1090, "bf16", 1, 1090, 1.0),
+]
 
-@pytest.mark.parametrize("w", PIPE, ids=lambda w: w.name)
-def test_pipelined_gemm_shapes(w):
-    # Input scale stops at 1e2 here: at 1e3 with d = 512 and random affine
-    # parameters the first-layer scores reach ~5e5, and a few rows whose two
-    # largest scores lie within ~1 of each other sit inside the fp32 score
-    # rounding (|s| * 2^-22 ~ 0.15), for either GEMM kernel.
-    for seed, scale, affine in ((0, 1.0, False), (1, 1.0, True), (2, 1e2, True), (3, 1e-3, False)):
+
+@pytest.mark.parametrize("w", WIDE, ids=lambda w: w.name)
+def test_wide_feature_tiles(w):
+    for seed, scale, affine in ((0, 1.0, False), (1, 1e2, True)):
         inp = _case(w, seed, scale, affine=affine)
         inp.lens[0] = w.L
-        say(f"[pipe] {w.name} seed={seed} scale={scale} affine={affine} lens={inp.lens.tolist()}")
+        say(f"[wide] {w.name} seed={seed} scale={scale} affine={affine}")
         assert_gate(gpu_forward(inp, force_path="tiled"), oracle_forward(inp), f"{w.name} seed {seed}")
 
 
