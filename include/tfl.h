@@ -66,8 +66,8 @@ typedef enum {
 typedef enum {
     TFL_PATH_AUTO = 0,
     TFL_PATH_SEQ = 1,   /* one workgroup owns whole sequences, whole stack in one launch */
-    TFL_PATH_PQ = 2,    /* task list over 64-row tiles (split-K attention tasks, fused row
-                           tasks), one launch per stage of the list */
+    TFL_PATH_PQ = 2,    /* task list over 64-row tiles (QKV tasks, split-K attention tasks,
+                           FFN tasks), one launch per stage of the list */
     TFL_PATH_TILED = 3, /* per-stage kernels: QKV GEMM, attention, GEMM+residual, LayerNorm, FFN */
     TFL_PATH_PQ_SINGLE = 4 /* the PQ tasks in one persistent launch fed by a device queue:
                               disabled, tfl_create returns TFL_E_UNSUPPORTED (its one GPU
