@@ -469,8 +469,14 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
 // FS down-projection partials.  Eight features per lane, a row over D/8
 // consecutive lanes of one wave; emit(r, pos, k, v) for every row r of the
 // tile (rows past L are formed from zeros; the caller drops them).
+// Row groups of RPI rows in a tile: the final stage takes one per task.
+template <int D>
+constexpr int pq_row_groups() { return PQ_RT / (PQ_THREADS / (D / 8)); }
+
+// Rows of tile t at the end of layer lp (row group `only` alone when it is
+// >= 0): see ffn_out_rows below.
 template <class WT, int D, class Emit>
-__device__ __forceinline__ void ffn_out_rows(const PqArgs& p, int lp, int b, int t, int tid, Emit emit) {
+__device__ __forceinline__ void ffn_out_rows(const PqArgs& p, int lp, int b, int t, int tid, Emit emit, int only = -1) {
     constexpr int TPR = D / 8, RPI = PQ_THREADS / TPR;
     static_assert(TPR <= WAVE && RPI * TPR == PQ_THREADS, "a row within one wave");
     const LayerPtrs& w = p.lw[lp];
@@ -486,6 +492,47 @@ __device__ __forceinline__ void ffn_out_rows(const PqArgs& p, int lp, int b, int
     // rows in groups of G iterations: every load of a group is issued before
     // its sums and reductions
     constexpr int NI = PQ_RT / RPI, G = NI < 2 ? NI : 2;
+    if (only >= 0) {
+        // one row group: the same sums as below, G = 1
+        const int pos = t * PQ_RT + tid / TPR + only * RPI;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (pos < p.L) {
+            const size_t off = ((size_t)b * p.L + pos) * D + k;
+            const float4 x0 = *(const float4*)(p.X1 + off), x1 = *(const float4*)(p.X1 + off + 4);
+            float4 pa[PQ_FS_MAX][2];
+#pragma unroll
+            for (int c = 0; c < PQ_FS_MAX; c++)
+                if (c < p.FS) {
+                    pa[c][0] = *(const float4*)(p.FP + c * TD + off);
+                    pa[c][1] = *(const float4*)(p.FP + c * TD + off + 4);
+                }
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+#pragma unroll
+            for (int e = 0; e < 8; e++) v[e] += bb[e];
+#pragma unroll
+            for (int c = 0; c < PQ_FS_MAX; c++)
+                if (c < p.FS) {
+                    v[0] += pa[c][0].x; v[1] += pa[c][0].y; v[2] += pa[c][0].z; v[3] += pa[c][0].w;
+                    v[4] += pa[c][1].x; v[5] += pa[c][1].y; v[6] += pa[c][1].z; v[7] += pa[c][1].w;
+                }
+        }
+        float sm = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sm += __shfl_xor(sm, o, WAVE);
+        const float mean = sm * (1.0f / D);
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) sq = fmaf(v[e] - mean, v[e] - mean, sq);
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
+        const float rs = 1.0f / sqrtf(sq * (1.0f / D) + p.eps);
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) out[e] = (v[e] - mean) * rs * gm[e] + bt[e];
+        emit(tid / TPR + only * RPI, pos, k, out);
+        return;
+    }
 #pragma unroll
     for (int i0 = 0; i0 < NI; i0 += G) {
         float4 xa[G][2], pa[G][PQ_FS_MAX][2];
@@ -1051,14 +1098,14 @@ __device__ void task_ffn(const PqArgs& p, int l, int b, int t, int cg, char* sme
 
 // The last layer's output rows of tile t to y.
 template <class WT, int D>
-__device__ void task_fin(const PqArgs& p, int b, int t, int tid) {
+__device__ void task_fin(const PqArgs& p, int b, int t, int part, int tid) {
     ffn_out_rows<WT, D>(p, p.n_layers - 1, b, t, tid, [&](int, int pos, int k, const float (&v)[8]) {
         if (pos < p.L) {
             WT* yr = (WT*)p.y + ((size_t)b * p.L + pos) * D + k;
             store4(yr, *reinterpret_cast<const float(*)[4]>(&v[0]));
             store4(yr + 4, *reinterpret_cast<const float(*)[4]>(&v[4]));
         }
-    });
+    }, part);
 }
 
 // Share of workgroup i of n of the weight conversion into fp16 planes (the
@@ -1098,25 +1145,22 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int k
     typedef PqTile<WT, D, DH> TL;
     __shared__ __attribute__((aligned(16))) char smem[TL::SMEM];
     const int i = blockIdx.x, tid = threadIdx.x, BNT = p.B * p.NT;
-    if (kind == PQ_STAGE_QKV || kind == PQ_STAGE_FFN) {
-        // Every task of tile r = t B + b (its QKV parts, its FFN parts and
-        // FIN) runs on XCD r mod 8 (workgroups go to the XCDs round-robin):
-        // workgroup i takes the (i / 8 mod n)-th task of tile
-        // (i mod 8) + 8 (i / 8 / n), n tasks per tile; the grid is rounded
-        // up to whole groups of eight tiles.  What one stage writes for a
-        // tile the next reads from the same XCD's L2.
-        const int n = kind == PQ_STAGE_QKV ? PQ_QKV_PARTS : p.FS;
-        const int j = i >> 3, r = (i & 7) + 8 * (j / n), part = j % n;
-        if (r >= BNT) return;
-        const int t = r / p.B, b = r - t * p.B;
-        if (kind == PQ_STAGE_QKV)
-            task_qkv<WT, D, DH>(p, l, b, t, part, smem, tid);
-        else
-            task_ffn<WT, D, DH>(p, l, b, t, part, smem, tid);
-    } else {                                     // FIN(b, t)
-        const int t = i / p.B, b = i - t * p.B;
-        task_fin<WT, D>(p, b, t, tid);
-    }
+    // Every task of tile r = t B + b (its QKV parts, its FFN parts and its
+    // FIN parts) runs on XCD r mod 8 (workgroups go to the XCDs round-robin):
+    // workgroup i takes the (i / 8 mod n)-th task of tile (i mod 8) +
+    // 8 (i / 8 / n), n tasks per tile; the grid is rounded up to whole groups
+    // of eight tiles.  What one stage writes for a tile the next reads from
+    // the same XCD's L2.  FIN takes one row group per task.
+    const int n = kind == PQ_STAGE_QKV ? PQ_QKV_PARTS : kind == PQ_STAGE_FFN ? p.FS : pq_row_groups<D>();
+    const int j = i >> 3, r = (i & 7) + 8 * (j / n), part = j % n;
+    if (r >= BNT) return;
+    const int t = r / p.B, b = r - t * p.B;
+    if (kind == PQ_STAGE_QKV)
+        task_qkv<WT, D, DH>(p, l, b, t, part, smem, tid);
+    else if (kind == PQ_STAGE_FFN)
+        task_ffn<WT, D, DH>(p, l, b, t, part, smem, tid);
+    else
+        task_fin<WT, D>(p, b, t, part, tid);
 }
 
 // ATT(l, b, h, t, s) of workgroup i, or false for a workgroup past the last
@@ -1227,7 +1271,7 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = stage(PQ_STAGE_FFN, l, a.FS * BNT8)) != hipSuccess) return e;
     }
-    return stage(PQ_STAGE_FIN, a.n_layers - 1, BNT);
+    return stage(PQ_STAGE_FIN, a.n_layers - 1, pq_row_groups<D>() * BNT8);
 }
 
 template <class WT>
