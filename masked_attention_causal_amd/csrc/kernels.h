@@ -85,7 +85,7 @@ struct SeqArgs {
 };
 
 // QKV tasks per 64-row tile and layer on the PQ path.
-constexpr int PQ_QKV_PARTS = 3;
+constexpr int PQ_QKV_PARTS = 3;  // Q, K, V (each split over two head ranges at d >= 128)
 constexpr int PQ_FS_MAX = 4;   // PQ FFN tasks per 64-row tile, at most
 
 // A weight matrix converted to fp16 planes: n elements of src (I/O dtype)

@@ -130,7 +130,7 @@ tfl_status make_plan(const tfl_config& c, Plan* p, std::string* why) {
         for (int c = 1; c <= PQ_FS_MAX && c <= nch; c++)
             if (nch % c == 0 && (long)BNT * c <= 256) fs = c;
         q.pq_fs = fs;
-        const long n_tasks = (long)q.n_layers * ((PQ_QKV_PARTS + fs) * (long)BNT + n_att) + BNT;
+        const long n_tasks = (long)q.n_layers * ((2 * PQ_QKV_PARTS + fs) * (long)BNT + n_att) + 8L * BNT;
         if (n_tasks > INT_MAX / 2) {
             *why = "too many tasks for the PQ path";
             return TFL_E_UNSUPPORTED;

@@ -9,8 +9,9 @@
 //   QKV(l,b,t,part)     layer-l projection of the tile's rows (x for l = 0;
 //                       after that the previous layer's output rows, formed
 //                       here: LayerNorm of X1 + bias + FFN partials), in
-//                       PQ_QKV_PARTS tasks per tile (Q, K, V), so the stage has
-//                       three times the tiles' workgroups
+//                       3 QSPLIT tasks per tile (Q, K, V, each over QSPLIT
+//                       ranges of whole heads; QSPLIT = 2 at d >= 128), so
+//                       the stage has three or six times the tiles' workgroups
 //   ATT(l,b,h,t,s)      masked attention of query tile t over key tiles
 //                       [s*KS, min(s*KS+KS, t+1)), partial (m, l, O)
 //   FFN(l,b,t,cg)       FS tasks per tile: each forms the tile's X1 (merge
@@ -294,7 +295,14 @@ struct PqTile {
     static constexpr int NB = D / 64;                   // 16-feature blocks per wave for D outputs
     static constexpr int QNB = (3 * D / 4) % 32 == 0 ? 2 : 1;   // blocks per QKV pass
     static constexpr int QPASS = (3 * D / 4) / (16 * QNB);     // QKV passes per wave (all of Q, K, V)
-    static constexpr int PPW = (D / 4) / (16 * QNB);           // QKV passes per wave of one part (Q, K or V)
+    static constexpr int PPW = (D / 4) / (16 * QNB);           // QKV passes per wave of all of one Q, K or V
+    // QKV tasks split each of Q, K and V into QSPLIT feature ranges (whole
+    // heads); a task's wave computes D / (4 QSPLIT) features in PPWS passes
+    // of 16 QNBS
+    static constexpr int QSPLIT = D >= 128 ? 2 : 1;
+    static constexpr int QNBS = (D / (4 * QSPLIT)) % 32 == 0 ? 2 : 1;
+    static constexpr int PPWS = (D / (4 * QSPLIT)) / (16 * QNBS);
+    static constexpr int QTASKS = 3 * QSPLIT;
     static constexpr int ACT_BYTES = PQ_RT * ALD * 2;
     static constexpr int G_BYTES = 2 * PQ_RT * GLD * 2;
     static constexpr int VT_BYTES = D * VLDT * 2;
@@ -363,17 +371,20 @@ __device__ __forceinline__ void qkv_store(const f32x4 (&acc)[QNB][4], const PqAr
     }
 }
 
-// Copies the staged V^T block [D][64] of tile t to the layer's V^T buffer.
+// Copies features [f0, f0 + nf) of the staged V^T block [D][64] of tile t to
+// the layer's V^T buffer.
 template <class WT, int D, int DH>
-__device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int t, const f16* vts, int tid) {
+__device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int t, const f16* vts, int tid, int f0 = 0,
+                                         int nf = D) {
     constexpr int H = D / DH;
-    constexpr int CH = D * (PQ_RT / 8);
+    constexpr int CHM = D * (PQ_RT / 8);
+    const int CH = nf * (PQ_RT / 8);
     f16* Vt = p.Vt + (size_t)layer * p.B * D * p.Lp;
 #pragma unroll
-    for (int i = 0; i < (CH + PQ_THREADS - 1) / PQ_THREADS; i++) {
+    for (int i = 0; i < (CHM + PQ_THREADS - 1) / PQ_THREADS; i++) {
         const int c = tid + i * PQ_THREADS;
-        if (CH % PQ_THREADS != 0 && c >= CH) break;
-        const int nn = c / (PQ_RT / 8), c8 = (c % (PQ_RT / 8)) * 8;
+        if (c >= CH) break;
+        const int nn = f0 + c / (PQ_RT / 8), c8 = (c % (PQ_RT / 8)) * 8;
         const int h = nn / DH, dd = nn - h * DH;
         *(uint4*)(Vt + (((size_t)b * H + h) * DH + dd) * p.Lp + t * PQ_RT + c8) =
             *(const uint4*)(vts + nn * PqTile<WT, D, DH>::VLDT + c8);
@@ -389,9 +400,10 @@ __device__ __forceinline__ void vt_flush(const PqArgs& p, int layer, int b, int 
 // of the layer's qk_stats[(b H + h) NT + t].  Caller has synchronised after
 // filling act.
 template <class WT, int D, int DH>
-__device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int t, int which, char* smem, int tid) {
+__device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int t, int which, int sub, char* smem,
+                                         int tid) {
     typedef PqTile<WT, D, DH> TL;
-    constexpr int QNB = TL::QNB, PPW = TL::PPW, H = D / DH;
+    constexpr int QNB = TL::QNBS, PPW = TL::PPWS, H = D / DH, FS_ = D / TL::QSPLIT;
     const int lane = tid & 63, wave = tid >> 6, c16 = lane & 15, g = lane >> 4;
     const f16* act = (const f16*)(smem + TL::OFF_ACT);
     f16* vts = (f16*)(smem + TL::OFF_GV);
@@ -404,7 +416,7 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
     const bool given = first && !std::is_same<WT, f16>::value;
 #pragma unroll 1
     for (int ps = 0; ps < PPW; ps++) {
-        const int nn0 = wave * (D / 4) + ps * 16 * QNB;   // feature within the part
+        const int nn0 = sub * FS_ + wave * (FS_ / 4) + ps * 16 * QNB;   // feature within Q, K or V
         const int n0 = which * D + nn0;                    // QKV output feature
         f32x4 acc[QNB][4];
 #pragma unroll
@@ -446,15 +458,17 @@ __device__ __forceinline__ void qkv_part(const PqArgs& p, int layer, int b, int 
     }
     __syncthreads();
     if (which == 2) {
-        vt_flush<WT, D, DH>(p, layer, b, t, vts, tid);
+        vt_flush<WT, D, DH>(p, layer, b, t, vts, tid, sub * FS_, FS_);
         return;
     }
-    // passes align with heads (16 QNB divides DH): head h is chunks [h CPH, (h+1) CPH)
+    // passes align with heads (16 QNB divides DH): local head hl of this
+    // task's H / QSPLIT is chunks [hl CPH, (hl+1) CPH)
     constexpr int CPH = DH / (16 * QNB);
-    for (int h = wave; h < H; h += PQ_THREADS / 64) {
+    for (int hl = wave; hl < H / TL::QSPLIT; hl += PQ_THREADS / 64) {
+        const int h = sub * (H / TL::QSPLIT) + hl;
         float sq = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPH; c++) sq += red[(h * CPH + c) * PQ_RT + lane];
+        for (int c = 0; c < CPH; c++) sq += red[(hl * CPH + c) * PQ_RT + lane];
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) sq = fmaxf(sq, __shfl_xor(sq, o, WAVE));
         if (lane == 0)
@@ -637,7 +651,7 @@ __device__ void task_qkv(const PqArgs& p, int layer, int b, int t, int part, cha
         });
     }
     __syncthreads();
-    qkv_part<WT, D, DH>(p, layer, b, t, part, smem, tid);
+    qkv_part<WT, D, DH>(p, layer, b, t, part / TL::QSPLIT, part % TL::QSPLIT, smem, tid);
 }
 
 // BOUNDED: every score of this (sequence, head) is within +-14 in exp2 units
@@ -1151,7 +1165,7 @@ __global__ __launch_bounds__(PQ_THREADS, 2) void pq_stage_kernel(PqArgs p, int k
     // 8 (i / 8 / n), n tasks per tile; the grid is rounded up to whole groups
     // of eight tiles.  What one stage writes for a tile the next reads from
     // the same XCD's L2.  FIN takes one row group per task.
-    const int n = kind == PQ_STAGE_QKV ? PQ_QKV_PARTS : kind == PQ_STAGE_FFN ? p.FS : pq_row_groups<D>();
+    const int n = kind == PQ_STAGE_QKV ? TL::QTASKS : kind == PQ_STAGE_FFN ? p.FS : pq_row_groups<D>();
     const int j = i >> 3, r = (i & 7) + 8 * (j / n), part = j % n;
     if (r >= BNT) return;
     const int t = r / p.B, b = r - t * p.B;
@@ -1262,7 +1276,7 @@ hipError_t pq_launch_t(const PqArgs& a, hipStream_t s) {
     };
     hipError_t e;
     for (int l = 0; l < a.n_layers; l++) {
-        if ((e = stage(PQ_STAGE_QKV, l, PQ_QKV_PARTS * BNT8)) != hipSuccess) return e;
+        if ((e = stage(PQ_STAGE_QKV, l, TL::QTASKS * BNT8)) != hipSuccess) return e;
         const int att_grid = (n_att + 7) / 8 * 8;
         if (l == 0)
             hipLaunchKernelGGL((pq_att_kernel<WT, D, DH, true>), dim3(att_grid), dim3(PQ_THREADS), 0, s, a, l);
