@@ -123,9 +123,10 @@ def stage_kernel(stage, plan, w):
 
 
 def measured_traffic(stage, workload, plan, w):
-    """HBM bytes per launch recorded in profiles/*.md for this kernel and
-    workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
-    kernel's sources changed since the counters were taken."""
+    """HBM bytes per launch recorded in profiles/*.md for this kernel, stage
+    and workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    kernel's sources changed since the counters were taken or the counters
+    are for another stage of the same kernel."""
     import glob
     import hashlib
     kern, files = stage_kernel(stage, plan, w)
@@ -143,6 +144,7 @@ def measured_traffic(stage, workload, plan, w):
                     continue
                 kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
                 if (kv.get("kernel") == kern and kv.get("workload") == workload
+                        and kv.get("stage", stage) == stage
                         and kv.get("source_sha256") == digest and "traffic_bytes_per_launch" in kv):
                     return int(kv["traffic_bytes_per_launch"])
     return None
